@@ -1,0 +1,311 @@
+"""Plain, slow, float64 CPU oracle of the Qwen3 decoder forward.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): the library never
+imports this module.
+
+Every function computes the plain definition of one step, in the order and
+notation of the pages it cites:
+
+* "手写Qwen3-0.6B推理" (sections Qwen3Model, Qwen3DecoderLayer,
+  Qwen3RMSNorm, Attention, Rope, MLP, 推理),
+* "第 3 章 前向与生成（代码走读）" (sections 3.1-3.4, 4.1-4.3, 5),
+* "从零开始写Qwen3（二）" (sections norm, rope/原理, rope/简单计算),
+* "古法手撕简易LLM推理器" (sections 处理参数和超参数, 工具函数,
+  核心计算函数与Transformer层, prefill与predict, RoPE的细节),
+* "Pytorch手写大模型推理" (section 模型: the configuration values).
+
+Inputs are bfloat16 bit patterns (uint16) that are widened exactly to
+float64; nothing is rounded afterwards.  Only library primitives used as
+steps: NumPy matrix products, exp, sqrt, sin, cos, max, sum.
+
+Pinned by ``tests/test_oracle_pins.py`` against closed forms, invariants,
+brute force and independent library routines.  The full 28-layer forward
+on random weights has no printed numeric example on the pages: its values
+are "parity unpinned" beyond the per-step pins and the model-level
+invariants (causality, KV-cache equivalence, GQA reduction).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = [
+    "Cfg", "QWEN3", "widen_bf16", "rmsnorm", "silu", "rope_inv_freq", "rope",
+    "attention", "LayerW", "Model", "KVCache", "embed", "layer_forward",
+    "final_logits", "prefill", "decode_step", "argmax_lowest",
+    "generate_nocache", "generate_cached",
+]
+
+
+@dataclass(frozen=True)
+class Cfg:
+    """Hyper-parameters.  Defaults are the Qwen3-0.6B values printed in the
+    configuration on "Pytorch手写大模型推理" (section 模型) and read from
+    config.json on "古法手撕简易LLM推理器" (section 处理参数和超参数)."""
+
+    hidden: int = 1024
+    n_heads: int = 16
+    n_kv_heads: int = 8
+    head_dim: int = 128
+    inter: int = 3072
+    vocab: int = 151936
+    n_layers: int = 28
+    eps: float = 1e-6
+    theta: float = 1e6
+    max_pos: int = 40960
+
+
+QWEN3 = Cfg()
+
+
+def widen_bf16(bits) -> np.ndarray:
+    """bfloat16 bit patterns -> float64, exactly (a bf16 value is the top
+    half of a float32)."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------- elementwise
+
+def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float = QWEN3.eps) -> np.ndarray:
+    """RMSNorm over the last axis: gamma * x / sqrt(mean(x^2) + eps).
+
+    "手写Qwen3-0.6B推理" §Qwen3RMSNorm (eps inside the square root);
+    "古法手撕简易LLM推理器" §工具函数 (RMSNorm).  Used for the input and
+    post-attention norms, the final norm and the per-head q/k norms."""
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * gamma
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z / (1 + exp(-z)) ("古法手撕简易LLM推理器" §工具函数)."""
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def rope_inv_freq(head_dim: int, theta: float) -> np.ndarray:
+    """theta^(-2i/d) for i = 0 .. d/2-1 ("手写Qwen3-0.6B推理" §Rope;
+    "从零开始写Qwen3（二）" §rope/原理 gives the base angle beta^(-2i/d))."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return theta ** (-(2.0 * i) / head_dim)
+
+
+def rope(x: np.ndarray, positions, theta: float) -> np.ndarray:
+    """NeoX ("rotate_half") rotary embedding.
+
+    x has shape [..., T, H, D]; positions is broadcastable to [..., T].
+    Dimension i < D/2 is paired with i + D/2 and the pair is rotated by the
+    angle p * theta^(-2i/D):  x' = x*cos + rotate_half(x)*sin with
+    rotate_half(x) = [-x2, x1] ("手写Qwen3-0.6B推理" §Rope;
+    "古法手撕简易LLM推理器" §工具函数 and §RoPE的细节: Qwen3 uses the
+    half-swap pairing, base theta from the config)."""
+    d = x.shape[-1]
+    half = d // 2
+    p = np.asarray(positions, dtype=np.float64)
+    ang = p[..., None] * rope_inv_freq(d, theta)          # [..., T, D/2]
+    c = np.cos(ang)[..., None, :]                          # [..., T, 1, D/2]
+    s = np.sin(ang)[..., None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos, block: int = 1024) -> np.ndarray:
+    """Causal grouped-query scaled-dot-product attention for one sequence.
+
+    q: [Hq, Tq, D]; k, v: [Hkv, S, D] (cache rows 0..S-1); q_pos: [Tq]
+    absolute positions.  Query head h reads KV head h // (Hq/Hkv) (the
+    expand-then-flatten of "手写Qwen3-0.6B推理" §Attention, the
+    repeat_interleave of "第 3 章" §3.3).  A query at position p sees keys
+    0..p exactly (bottom-right aligned; "从零开始写Qwen3（二）" §Attn warns a
+    one-token decode query must see every cached key).  Scores are scaled by
+    1/sqrt(D) and normalised with a max-shifted softmax
+    ("古法手撕简易LLM推理器" §工具函数).  Query rows are processed in blocks
+    only to bound memory."""
+    hq, tq, d = q.shape
+    hkv, s_len, _ = k.shape
+    assert hq % hkv == 0, "Hq must be a multiple of Hkv"
+    groups = hq // hkv
+    q_pos = np.asarray(q_pos, dtype=np.int64).reshape(tq)
+    key_idx = np.arange(s_len)
+    out = np.empty((hq, tq, d), dtype=np.float64)
+    scale = 1.0 / np.sqrt(d)
+    for h in range(hq):
+        g = h // groups
+        for r0 in range(0, tq, block):
+            r1 = min(tq, r0 + block)
+            sc = (q[h, r0:r1] @ k[g].T) * scale                   # [tb, S]
+            visible = key_idx[None, :] <= q_pos[r0:r1, None]
+            sc = np.where(visible, sc, -np.inf)
+            m = np.max(sc, axis=-1, keepdims=True)
+            e = np.where(visible, np.exp(sc - m), 0.0)
+            w = e / np.sum(e, axis=-1, keepdims=True)
+            out[h, r0:r1] = w @ v[g]
+    return out
+
+
+# ---------------------------------------------------------------- weights
+
+class LayerW:
+    """One decoder layer in float64, unmerged as in the state dict printed on
+    "手写Qwen3-0.6B推理" §打印模型结构 (all projections stored [out, in],
+    applied as y = x W^T, no bias)."""
+
+    KEYS = ("input_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo",
+            "post_norm", "wg", "wu", "wd")
+
+    def __init__(self, bits: dict):
+        for key in self.KEYS:
+            setattr(self, key, widen_bf16(bits[key]))
+
+
+class Model:
+    """Widened model: embedding (tied lm_head), final norm, layers."""
+
+    def __init__(self, bits: dict, cfg: Cfg = QWEN3):
+        self.cfg = cfg
+        self.embed = widen_bf16(bits["embed"])
+        self.final_norm = widen_bf16(bits["final_norm"])
+        self.layers = [LayerW(lw) for lw in bits["layers"]]
+
+
+class KVCache:
+    """Per-layer K (after q/k-norm and RoPE) and raw V, [B, Hkv, S_max, D]
+    ("古法手撕简易LLM推理器" §核心计算函数与Transformer层: the cache keeps the
+    projected, normalised, rotated K and the projected V)."""
+
+    def __init__(self, cfg: Cfg, n_layers: int, batch: int, max_seq: int):
+        shape = (batch, cfg.n_kv_heads, max_seq, cfg.head_dim)
+        self.k = [np.zeros(shape) for _ in range(n_layers)]
+        self.v = [np.zeros(shape) for _ in range(n_layers)]
+        self.max_seq = max_seq
+
+
+# ---------------------------------------------------------------- model steps
+
+def embed(model: Model, ids) -> np.ndarray:
+    """x = E[ids], no scaling ("手写Qwen3-0.6B推理" §Qwen3Model;
+    "第 3 章" §3.1)."""
+    return model.embed[np.asarray(ids, dtype=np.int64)]
+
+
+def layer_forward(w: LayerW, x: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                  start_pos, cfg: Cfg = QWEN3) -> np.ndarray:
+    """One pre-norm decoder layer on x [B, T, C]; returns the new residual.
+
+    h = x + Attn(RMSNorm_in(x)); out = h + MLP(RMSNorm_post(h))
+    ("手写Qwen3-0.6B推理" §Qwen3DecoderLayer; "第 3 章" §3.2).
+    Attention: q/k/v projections, per-head RMSNorm of q and k with a
+    head_dim-long gain shared by all heads, RoPE on q and k at absolute
+    positions start..start+T-1, K/V written into the cache at those rows,
+    causal GQA over cache rows 0..p, head-major concat, o_proj
+    ("手写Qwen3-0.6B推理" §Attention; "古法手撕简易LLM推理器"
+    §核心计算函数与Transformer层).  MLP: down(silu(gate x) * up x)
+    ("手写Qwen3-0.6B推理" §MLP).
+
+    start_pos is an int or one int per sequence.  k_cache/v_cache are
+    [B, Hkv, S_max, D] and are updated in place."""
+    b_sz, t_len, _ = x.shape
+    hq, hkv, d = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    starts = np.broadcast_to(np.asarray(start_pos, dtype=np.int64), (b_sz,))
+    pos = starts[:, None] + np.arange(t_len)[None, :]             # [B, T]
+
+    h = rmsnorm(x, w.input_norm, cfg.eps)
+    q = (h @ w.wq.T).reshape(b_sz, t_len, hq, d)
+    k = (h @ w.wk.T).reshape(b_sz, t_len, hkv, d)
+    v = (h @ w.wv.T).reshape(b_sz, t_len, hkv, d)
+    q = rmsnorm(q, w.q_norm, cfg.eps)
+    k = rmsnorm(k, w.k_norm, cfg.eps)
+    q = rope(q, pos, cfg.theta)
+    k = rope(k, pos, cfg.theta)
+
+    o = np.empty((b_sz, t_len, hq * d))
+    for b in range(b_sz):
+        p0 = int(starts[b])
+        k_cache[b, :, p0:p0 + t_len] = k[b].transpose(1, 0, 2)
+        v_cache[b, :, p0:p0 + t_len] = v[b].transpose(1, 0, 2)
+        n_keys = p0 + t_len
+        ob = attention(q[b].transpose(1, 0, 2), k_cache[b, :, :n_keys], v_cache[b, :, :n_keys], pos[b])
+        o[b] = ob.transpose(1, 0, 2).reshape(t_len, hq * d)       # head h -> columns h*D..h*D+D-1
+
+    x = x + o @ w.wo.T
+    h2 = rmsnorm(x, w.post_norm, cfg.eps)
+    return x + (silu(h2 @ w.wg.T) * (h2 @ w.wu.T)) @ w.wd.T
+
+
+def final_logits(model: Model, x_last: np.ndarray) -> np.ndarray:
+    """logits = RMSNorm_f(x) E^T with the lm_head tied to the embedding
+    ("手写Qwen3-0.6B推理" §Qwen3Model; only each sequence's last row is
+    projected, "第 3 章" §4.1)."""
+    return rmsnorm(x_last, model.final_norm, model.cfg.eps) @ model.embed.T
+
+
+def argmax_lowest(logits: np.ndarray) -> np.ndarray:
+    """Greedy choice: index of the maximum, the lowest index among equal
+    maxima ("手写Qwen3-0.6B推理" §推理; "第 3 章" §4.3).  np.argmax returns
+    the first occurrence (and the first NaN if any)."""
+    return np.argmax(np.atleast_2d(logits), axis=-1).astype(np.int64)
+
+
+def prefill(model: Model, ids, max_seq: int | None = None, n_layers: int | None = None):
+    """Prefill a batch of equal-length prompts ids [B, T] from position 0.
+
+    Returns (logits of each sequence's last position [B, V], next ids [B],
+    KV cache, final residual [B, T, C])
+    ("古法手撕简易LLM推理器" §prefill与predict: prefill then lastOutputToken)."""
+    ids = np.asarray(ids)
+    b_sz, t_len = ids.shape
+    nl = len(model.layers) if n_layers is None else n_layers
+    cache = KVCache(model.cfg, nl, b_sz, max_seq or t_len)
+    x = embed(model, ids)
+    for li in range(nl):
+        x = layer_forward(model.layers[li], x, cache.k[li], cache.v[li], 0, model.cfg)
+    logits = final_logits(model, x[:, -1, :])
+    return logits, argmax_lowest(logits), cache, x
+
+
+def decode_step(model: Model, cache: KVCache, ids, positions):
+    """One greedy step: each sequence b feeds token ids[b] at position
+    positions[b] (its current length) and attends to cache rows 0..p
+    ("古法手撕简易LLM推理器" §prefill与predict, predict loop).
+    Returns (logits [B, V], next ids [B])."""
+    ids = np.asarray(ids).reshape(-1)
+    x = embed(model, ids[:, None])                                  # [B, 1, C]
+    for li, w in enumerate(model.layers):
+        x = layer_forward(w, x, cache.k[li], cache.v[li], np.asarray(positions), model.cfg)
+    logits = final_logits(model, x[:, 0, :])
+    return logits, argmax_lowest(logits)
+
+
+def generate_nocache(model: Model, prompt, n_new: int, eos_id: int | None = None):
+    """Greedy generation that recomputes the whole prefix each step, as the
+    loops on "手写Qwen3-0.6B推理" §推理 and "第 3 章" §4.2 do.  0 new tokens
+    means no model call; EOS, when met, is kept in the output."""
+    tokens = [int(t) for t in np.asarray(prompt).reshape(-1)]
+    out = []
+    for _ in range(n_new):
+        logits, nxt, _, _ = prefill(model, np.asarray([tokens]))
+        tok = int(nxt[0])
+        out.append(tok)
+        tokens.append(tok)
+        if eos_id is not None and tok == eos_id:
+            break
+    return out
+
+
+def generate_cached(model: Model, prompt, n_new: int, forced=None):
+    """Greedy generation with the KV cache: prefill, then one decode step per
+    token.  With ``forced`` (a token list), the step inputs are taken from it
+    instead of the oracle's own choices (teacher forcing).  Returns
+    (tokens chosen by the oracle, per-step logits list)."""
+    prompt = np.asarray(prompt).reshape(1, -1)
+    t_len = prompt.shape[1]
+    logits, nxt, cache, _ = prefill(model, prompt, max_seq=t_len + max(n_new, 1))
+    chosen, all_logits = [int(nxt[0])], [logits[0]]
+    inp = int(nxt[0]) if forced is None else int(forced[0])
+    for i in range(1, n_new):
+        lg, nx = decode_step(model, cache, [inp], [t_len + i - 1])
+        chosen.append(int(nx[0]))
+        all_logits.append(lg[0])
+        inp = int(nx[0]) if forced is None else int(forced[i])
+    return chosen[:n_new], all_logits[:n_new]
