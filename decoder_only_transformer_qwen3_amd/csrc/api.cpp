@@ -1,0 +1,255 @@
+// C-ABI entry points: validate on the host, carve the caller's workspace,
+// enqueue the kernel chain on the caller's stream.  No allocation, no
+// synchronisation, no state kept between calls.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "../../include/q3.h"
+#include "common.hpp"
+#include "launch.hpp"
+#include "validate.hpp"
+
+using namespace q3;
+
+namespace {
+
+// Skinny-GEMM K splits: o_proj K = 2048 -> 4 x 512, down K = 3072 -> 6 x 512.
+constexpr int SPLIT_O = 4;
+constexpr int SPLIT_DOWN = 6;
+
+struct Ws {
+  float* resid;
+  uint16_t *h, *qkv, *qr, *ao, *act, *fh;
+  float *part, *apart, *logits;
+};
+
+Ws carve(void* base, int32_t batch, int32_t n_tokens) {
+  const q3v::WsLayout L = q3v::ws_layout(batch, n_tokens);
+  char* p = static_cast<char*>(base);
+  Ws w;
+  w.resid = reinterpret_cast<float*>(p + L.resid);
+  w.h = reinterpret_cast<uint16_t*>(p + L.h);
+  w.qkv = reinterpret_cast<uint16_t*>(p + L.qkv);
+  w.qr = reinterpret_cast<uint16_t*>(p + L.qr);
+  w.ao = reinterpret_cast<uint16_t*>(p + L.ao);
+  w.act = reinterpret_cast<uint16_t*>(p + L.act);
+  w.part = reinterpret_cast<float*>(p + L.part);
+  w.apart = reinterpret_cast<float*>(p + L.apart);
+  w.logits = reinterpret_cast<float*>(p + L.logits);
+  w.fh = reinterpret_cast<uint16_t*>(p + L.fh);
+  return w;
+}
+
+struct LayerCtx {
+  const q3_layer_weights* w;
+  const float *cos, *sin;
+  uint16_t *kl, *vl;
+  int B, T, max_seq, start;
+  const int32_t* pos_dev;  // per-sequence start positions on the device (decode), or null
+  int dec_splits;          // decode-attention splits (T == 1 only)
+  float* resid;
+  Ws ws;
+  hipStream_t s;
+};
+
+inline const uint16_t* U(const void* p) { return static_cast<const uint16_t*>(p); }
+
+// One decoder layer ("手写Qwen3-0.6B推理" §Qwen3DecoderLayer).  `pending`
+// counts split-K partial sums of the previous down projection that still
+// have to be added to the residual; they are folded into this layer's input
+// norm, and this layer's own down-projection partials are left pending.
+void run_layer(const LayerCtx& c, int& pending) {
+  const int M = c.B * c.T;
+  const bool skinny = M <= q3v::SKINNY_MAX_ROWS;
+  const q3_layer_weights* w = c.w;
+  // input RMSNorm (+ deferred residual add)
+  launch_rmsnorm(c.resid, c.ws.part, pending, M, U(w->input_norm), c.ws.h, M, 1, 0, c.s);
+  pending = 0;
+  // merged q|k|v projection
+  if (skinny)
+    launch_gemm_skinny(c.ws.h, U(w->w_qkv), c.ws.qkv, M, QKV_N, C, QKV_N, 1, EPI_BF16, c.s);
+  else
+    launch_gemm_tiled(c.ws.h, U(w->w_qkv), c.ws.qkv, M, QKV_N, C, QKV_N, EPI_BF16, c.s);
+  // q/k RMSNorm + RoPE, K/V into the cache
+  launch_qknorm_rope(c.ws.qkv, U(w->q_norm), U(w->k_norm), c.cos, c.sin, c.ws.qr, c.kl, c.vl, c.B, c.T, c.max_seq,
+                     c.pos_dev, c.start, c.s);
+  // causal GQA attention
+  if (c.T == 1)
+    launch_attn_decode(c.ws.qr, c.kl, c.vl, c.ws.apart, c.ws.ao, c.B, c.max_seq, c.pos_dev, c.start, c.dec_splits,
+                       c.s);
+  else
+    launch_attn_prefill(c.ws.qr, c.kl, c.vl, c.ws.ao, c.B, c.T, c.start, c.max_seq, c.s);
+  // o_proj + residual, post-attention RMSNorm
+  if (skinny) {
+    launch_gemm_skinny(c.ws.ao, U(w->w_o), c.ws.part, M, C, QDIM, C, SPLIT_O, EPI_PARTIAL, c.s);
+    launch_rmsnorm(c.resid, c.ws.part, SPLIT_O, M, U(w->post_norm), c.ws.h, M, 1, 0, c.s);
+  } else {
+    launch_gemm_tiled(c.ws.ao, U(w->w_o), c.resid, M, C, QDIM, C, EPI_ADD_F32, c.s);
+    launch_rmsnorm(c.resid, nullptr, 0, M, U(w->post_norm), c.ws.h, M, 1, 0, c.s);
+  }
+  // gate|up projection with silu(gate) * up, then down + residual
+  if (skinny) {
+    launch_gemm_skinny(c.ws.h, U(w->w_gate_up), c.ws.act, M, 2 * I, C, I, 1, EPI_SILU, c.s);
+    launch_gemm_skinny(c.ws.act, U(w->w_down), c.ws.part, M, C, I, C, SPLIT_DOWN, EPI_PARTIAL, c.s);
+    pending = SPLIT_DOWN;
+  } else {
+    launch_gemm_tiled(c.ws.h, U(w->w_gate_up), c.ws.act, M, 2 * I, C, I, EPI_SILU, c.s);
+    launch_gemm_tiled(c.ws.act, U(w->w_down), c.resid, M, C, I, C, EPI_ADD_F32, c.s);
+  }
+}
+
+// Final RMSNorm on each sequence's last row, tied lm_head, argmax
+// ("手写Qwen3-0.6B推理" §Qwen3Model; "第 3 章" §4.1 and §4.3).
+void run_head(const q3_model* m, const Ws& ws, float* resid, int pending, int B, int T, float* logits,
+              int32_t* next_ids, int32_t* seq_lens, int seq_mode, int seq_val, hipStream_t s) {
+  const int part_rows = B * T;
+  launch_rmsnorm(resid, ws.part, pending, part_rows, U(m->final_norm), ws.fh, B, T, T - 1, s);
+  for (int r0 = 0; r0 < B; r0 += q3v::SKINNY_MAX_ROWS) {
+    const int rows = (B - r0) < q3v::SKINNY_MAX_ROWS ? (B - r0) : q3v::SKINNY_MAX_ROWS;
+    launch_gemm_skinny(ws.fh + (size_t)r0 * C, U(m->embed), logits + (size_t)r0 * V, rows, V, C, V, 1, EPI_F32, s);
+  }
+  launch_argmax(logits, B, V, V, next_ids, seq_lens, seq_mode, seq_val, s);
+}
+
+inline int launch_status() { return hipGetLastError() == hipSuccess ? Q3_OK : Q3_ERR_HIP; }
+
+inline uint16_t* layer_cache(void* base, int layer, const q3_kv* kv) {
+  return static_cast<uint16_t*>(base) + (size_t)layer * kv->batch * HKV * kv->max_seq * D;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* q3_status_str(int status) {
+  switch (status) {
+    case Q3_OK: return "ok";
+    case Q3_ERR_NULL: return "a required pointer is NULL";
+    case Q3_ERR_SHAPE: return "invalid batch, token count or cache shape";
+    case Q3_ERR_POSITION: return "positions exceed the cache capacity or the maximum position";
+    case Q3_ERR_ALIGN: return "a pointer is not suitably aligned";
+    case Q3_ERR_WORKSPACE: return "workspace smaller than q3_workspace_bytes()";
+    case Q3_ERR_HIP: return "a HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int q3_rope_table_host(float* cos_out, float* sin_out) {
+  if (!cos_out || !sin_out) return Q3_ERR_NULL;
+  double inv[ROPE_HALF];
+  for (int i = 0; i < ROPE_HALF; ++i) inv[i] = pow(1e6, -(2.0 * i) / (double)D);
+  for (int p = 0; p < MAXPOS; ++p)
+    for (int i = 0; i < ROPE_HALF; ++i) {
+      const double a = (double)p * inv[i];
+      cos_out[(size_t)p * ROPE_HALF + i] = (float)cos(a);
+      sin_out[(size_t)p * ROPE_HALF + i] = (float)sin(a);
+    }
+  return Q3_OK;
+}
+
+size_t q3_workspace_bytes(int32_t batch, int32_t n_tokens) {
+  if (batch < 1 || n_tokens < 1) return 0;
+  return q3v::ws_layout(batch, n_tokens).total;
+}
+
+int q3_layer_forward(const q3_layer_weights* w, const float* rope_cos, const float* rope_sin, void* k_layer,
+                     void* v_layer, int32_t batch, int32_t n_tokens, int32_t max_seq, int32_t start_pos,
+                     float* residual, void* ws, size_t ws_bytes, void* stream) {
+  const int st = q3v::check_layer_call(w, rope_cos, rope_sin, k_layer, v_layer, batch, n_tokens, max_seq, start_pos,
+                                       residual, ws, ws_bytes);
+  if (st != Q3_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  LayerCtx c;
+  c.w = w;
+  c.cos = rope_cos;
+  c.sin = rope_sin;
+  c.kl = static_cast<uint16_t*>(k_layer);
+  c.vl = static_cast<uint16_t*>(v_layer);
+  c.B = batch;
+  c.T = n_tokens;
+  c.max_seq = max_seq;
+  c.start = start_pos;
+  c.pos_dev = nullptr;
+  c.dec_splits = q3v::decode_splits(batch, start_pos + 1);
+  c.resid = residual;
+  c.ws = carve(ws, batch, n_tokens);
+  c.s = s;
+  int pending = 0;
+  run_layer(c, pending);
+  if (pending)  // fold the down-projection partials into the caller's residual
+    launch_rmsnorm(residual, c.ws.part, pending, batch * n_tokens, nullptr, nullptr, batch * n_tokens, 1, 0, s);
+  return launch_status();
+}
+
+int q3_prefill(const q3_model* m, const q3_kv* kv, int32_t batch, int32_t prompt_len, const int32_t* ids,
+               float* last_logits, int32_t* next_ids, int32_t* seq_lens, void* ws, size_t ws_bytes, void* stream) {
+  const int st =
+      q3v::check_prefill_call(m, kv, batch, prompt_len, ids, last_logits, next_ids, seq_lens, ws, ws_bytes);
+  if (st != Q3_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const Ws wsp = carve(ws, batch, prompt_len);
+  const int M = batch * prompt_len;
+  launch_embed(ids, U(m->embed), wsp.resid, M, s);
+  LayerCtx c;
+  c.cos = m->rope_cos;
+  c.sin = m->rope_sin;
+  c.B = batch;
+  c.T = prompt_len;
+  c.max_seq = kv->max_seq;
+  c.start = 0;
+  c.pos_dev = nullptr;
+  c.dec_splits = q3v::decode_splits(batch, 1);
+  c.resid = wsp.resid;
+  c.ws = wsp;
+  c.s = s;
+  int pending = 0;
+  for (int l = 0; l < NL; ++l) {
+    c.w = &m->layer[l];
+    c.kl = layer_cache(kv->k, l, kv);
+    c.vl = layer_cache(kv->v, l, kv);
+    run_layer(c, pending);
+  }
+  run_head(m, wsp, wsp.resid, pending, batch, prompt_len, last_logits ? last_logits : wsp.logits, next_ids, seq_lens,
+           1, prompt_len, s);
+  return launch_status();
+}
+
+int q3_decode_step(const q3_model* m, const q3_kv* kv, int32_t batch, const int32_t* in_ids, int32_t* seq_lens,
+                   int32_t max_len_hint, float* logits, int32_t* out_ids, void* ws, size_t ws_bytes, void* stream) {
+  const int st =
+      q3v::check_decode_call(m, kv, batch, in_ids, seq_lens, max_len_hint, logits, out_ids, ws, ws_bytes);
+  if (st != Q3_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const Ws wsp = carve(ws, batch, 1);
+  launch_embed(in_ids, U(m->embed), wsp.resid, batch, s);
+  LayerCtx c;
+  c.cos = m->rope_cos;
+  c.sin = m->rope_sin;
+  c.B = batch;
+  c.T = 1;
+  c.max_seq = kv->max_seq;
+  c.start = 0;
+  c.pos_dev = seq_lens;
+  c.dec_splits = q3v::decode_splits(batch, max_len_hint);
+  c.resid = wsp.resid;
+  c.ws = wsp;
+  c.s = s;
+  int pending = 0;
+  for (int l = 0; l < NL; ++l) {
+    c.w = &m->layer[l];
+    c.kl = layer_cache(kv->k, l, kv);
+    c.vl = layer_cache(kv->v, l, kv);
+    run_layer(c, pending);
+  }
+  run_head(m, wsp, wsp.resid, pending, batch, 1, logits ? logits : wsp.logits, out_ids, seq_lens, 2, 0, s);
+  return launch_status();
+}
+
+int q3_argmax(const float* logits, int32_t rows, int32_t vocab, int64_t row_stride, int32_t* out_idx, void* stream) {
+  const int st = q3v::check_argmax_call(logits, rows, vocab, row_stride, out_idx);
+  if (st != Q3_OK) return st;
+  launch_argmax(logits, rows, vocab, row_stride, out_idx, nullptr, 0, 0, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+// Skinny GEMM for decode-sized row counts (M <= 64 tokens):
+//   out = X[M, K] * W[N, K]^T
+// Bandwidth-bound on the weights, so every weight byte is read exactly once
+// per call and streamed straight from HBM into MFMA operands (no LDS
+// staging).  The transposed product C^T = W X^T is formed with
+// v_mfma_f32_16x16x32_bf16: the A operand is 16 weight rows, the B operand
+// is 16 tokens, so one MFMA row block covers 16 output features.
+//
+// Lane layout of the 16x16x32 MFMA (lane l, element j of the 8-wide operand):
+//   A: row l%16, k-slot (l/16, j);  B: column l%16, k-slot (l/16, j);
+//   C: column l%16, rows 4*(l/16) + i, i = 0..3.
+// The mapping of k-slots to actual k is free as long as A and B agree; here
+// k-slot (q, j) of k-step s is k = 32*s + 8*q + j, so the 4 lanes of one
+// weight row read 64 contiguous bytes per step.
+//
+// Work split: one workgroup (4 waves) per 16 weight rows and K range
+// (grid.y splits K).  The 4 waves take interleaved 32-wide k-steps, are
+// reduced through LDS, and the epilogue runs once per output element.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace q3 {
+
+template <int NB, int EPI, int U>
+__global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+                                                     void* __restrict__ out, int M, int N, int K, int ldo,
+                                                     int kspan) {
+  __shared__ float red[4][NB * 16][17];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, qd = l >> 4;
+  const int rb = blockIdx.x, split = blockIdx.y;
+  int wrow;
+  if constexpr (EPI == EPI_SILU) {
+    // rows 0..7 of the block are gate rows, 8..15 the matching up rows
+    const int half = N >> 1;
+    wrow = (r < 8) ? rb * 8 + r : half + rb * 8 + (r - 8);
+  } else {
+    wrow = rb * 16 + r;
+  }
+  const size_t k_base = (size_t)split * kspan + qd * 8;
+  const uint16_t* wp = W + (size_t)wrow * K + k_base;
+  const uint16_t* xp[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    int m = nb * 16 + r;
+    m = m < M ? m : M - 1;
+    xp[nb] = X + (size_t)m * K + k_base;
+  }
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = kspan >> 5;  // 32-wide k-steps in this workgroup's range
+  for (int s0 = w; s0 < nsteps; s0 += 4 * U) {
+    u32x4 a[U];
+    u32x4 bx[U][NB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + (size_t)(s0 + 4 * u) * 32));
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) bx[u][nb] = *reinterpret_cast<const u32x4*>(xp[nb] + (size_t)(s0 + 4 * u) * 32);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u]), as_bf16x8(bx[u][nb]), acc[nb], 0, 0, 0);
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[w][nb * 16 + r][4 * qd + i] = acc[nb][i];
+  __syncthreads();
+
+  const int t = threadIdx.x;
+  if constexpr (EPI == EPI_SILU) {
+    // out[m][rb*8 + j] = silu(gate) * up
+    for (int e = t; e < NB * 16 * 8; e += 256) {
+      const int m = e >> 3, j = e & 7;
+      if (m >= M) continue;
+      const float gsum = red[0][m][j] + red[1][m][j] + red[2][m][j] + red[3][m][j];
+      const float usum = red[0][m][8 + j] + red[1][m][8 + j] + red[2][m][8 + j] + red[3][m][8 + j];
+      const float sg = gsum / (1.0f + __expf(-gsum));
+      reinterpret_cast<uint16_t*>(out)[(size_t)m * ldo + rb * 8 + j] = (uint16_t)f2bf(sg * usum);
+    }
+  } else {
+    if (t < NB * 16 * 4) {
+      const int m = t >> 2, ng = t & 3;
+      if (m < M) {
+        f32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = red[0][m][4 * ng + i] + red[1][m][4 * ng + i] + red[2][m][4 * ng + i] + red[3][m][4 * ng + i];
+        const int n = rb * 16 + 4 * ng;
+        if constexpr (EPI == EPI_BF16) {
+          u32x2 o;
+          o.x = pack_bf2(v[0], v[1]);
+          o.y = pack_bf2(v[2], v[3]);
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + (size_t)m * ldo + n) = o;
+        } else if constexpr (EPI == EPI_F32) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)m * ldo + n) = v;
+        } else if constexpr (EPI == EPI_ADD_F32) {
+          f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)m * ldo + n);
+          *dst = *dst + v;
+        } else {  // EPI_PARTIAL
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + ((size_t)split * M + m) * N + n) = v;
+        }
+      }
+    }
+  }
+}
+
+template <int NB, int EPI>
+static void launch_nb(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo, int n_split,
+                      hipStream_t s) {
+  const int kspan = K / n_split;
+  const int rows_per_block = 16;
+  const int gx = (EPI == EPI_SILU) ? (N / 2) / 8 : N / rows_per_block;
+  // Each wave takes kspan/128 steps; unroll by 8 when that divides evenly.
+  if (((kspan >> 5) % 32) == 0)
+    hipLaunchKernelGGL((k_gemm_skinny<NB, EPI, 8>), dim3(gx, n_split), dim3(256), 0, s, X, W, out, M, N, K, ldo, kspan);
+  else
+    hipLaunchKernelGGL((k_gemm_skinny<NB, EPI, 4>), dim3(gx, n_split), dim3(256), 0, s, X, W, out, M, N, K, ldo, kspan);
+}
+
+template <int EPI>
+static void launch_epi(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo, int n_split,
+                       hipStream_t s) {
+  const int nb = (M + 15) / 16;
+  switch (nb) {
+    case 1: launch_nb<1, EPI>(X, W, out, M, N, K, ldo, n_split, s); break;
+    case 2: launch_nb<2, EPI>(X, W, out, M, N, K, ldo, n_split, s); break;
+    case 3: launch_nb<3, EPI>(X, W, out, M, N, K, ldo, n_split, s); break;
+    default: launch_nb<4, EPI>(X, W, out, M, N, K, ldo, n_split, s); break;
+  }
+}
+
+void launch_gemm_skinny(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo, int n_split,
+                        Epi epi, hipStream_t s) {
+  switch (epi) {
+    case EPI_BF16: launch_epi<EPI_BF16>(X, W, out, M, N, K, ldo, n_split, s); break;
+    case EPI_F32: launch_epi<EPI_F32>(X, W, out, M, N, K, ldo, n_split, s); break;
+    case EPI_ADD_F32: launch_epi<EPI_ADD_F32>(X, W, out, M, N, K, ldo, n_split, s); break;
+    case EPI_SILU: launch_epi<EPI_SILU>(X, W, out, M, N, K, ldo, n_split, s); break;
+    case EPI_PARTIAL: launch_epi<EPI_PARTIAL>(X, W, out, M, N, K, ldo, n_split, s); break;
+  }
+}
+
+}  // namespace q3

@@ -1,0 +1,60 @@
+// Host-side launchers of the gfx950 kernels (internal to libq3).
+// Every launcher only enqueues on the given stream; shapes are validated
+// by the C-ABI entry points before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q3 {
+
+enum Epi : int {
+  EPI_BF16 = 0,     // out bf16 [M, ldo] (column offset = output row of W)
+  EPI_F32 = 1,      // out f32 [M, ldo]
+  EPI_ADD_F32 = 2,  // out f32 [M, ldo] += result (residual add)
+  EPI_SILU = 3,     // W rows are [gate; up]; out bf16 [M, ldo] = silu(gate) * up
+  EPI_PARTIAL = 4,  // out f32 [split][M][N] partial sums over a K range
+};
+
+// x[m] = E[ids[m]] widened to f32 (one row of 1024 per token).
+void launch_embed(const int32_t* ids, const uint16_t* E, float* resid, int M, hipStream_t s);
+
+// For r < n_rows, row = r*row_step + row_off:
+//   resid[row] += sum_{j < n_part} part[j][row]      (written back when n_part > 0)
+//   out[r] = bf16(resid[row] / sqrt(mean(resid[row]^2) + eps) * gamma)   (when out != null)
+// part is [n_part][part_rows][1024].
+void launch_rmsnorm(float* resid, const float* part, int n_part, int part_rows, const uint16_t* gamma,
+                    uint16_t* out, int n_rows, int row_step, int row_off, hipStream_t s);
+
+// Per-head q/k RMSNorm + NeoX RoPE + KV-cache write for M = B*T rows of the
+// merged qkv projection.  Position of row b*T+t is (pos_dev ? pos_dev[b] : start) + t.
+void launch_qknorm_rope(const uint16_t* qkv, const uint16_t* q_norm, const uint16_t* k_norm,
+                        const float* rope_cos, const float* rope_sin, uint16_t* q_out, uint16_t* k_cache,
+                        uint16_t* v_cache, int B, int T, int max_seq, const int32_t* pos_dev, int start,
+                        hipStream_t s);
+
+// MFMA tiled GEMM, out = X[M,K] * W[N,K]^T with the chosen epilogue.
+// Requires N % 128 == 0 (EPI_SILU: N = 2*ldo-columns, (N/2) % 64 == 0), K % 64 == 0.
+void launch_gemm_tiled(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo,
+                       Epi epi, hipStream_t s);
+
+// MFMA skinny GEMM for M <= 64 rows (weight streaming), split into n_split K ranges.
+// Requires N % 16 == 0 and (K / n_split) % 512 == 0; EPI_PARTIAL writes [n_split][M][N].
+void launch_gemm_skinny(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo,
+                        int n_split, Epi epi, hipStream_t s);
+
+// Causal GQA flash attention over the cache for B x T queries at positions start..start+T-1.
+void launch_attn_prefill(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out,
+                         int B, int T, int start, int max_seq, hipStream_t s);
+
+// Split-K decode attention (one query per sequence) + log-sum-exp merge.
+void launch_attn_decode(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, float* part,
+                        uint16_t* out, int B, int max_seq, const int32_t* pos_dev, int start, int n_split,
+                        hipStream_t s);
+
+// Row argmax (lowest index on ties, first NaN wins).  seq_mode: 0 none,
+// 1 seq_lens[r] = seq_val, 2 seq_lens[r] += 1 (done after the argmax).
+void launch_argmax(const float* logits, int rows, int vocab, int64_t row_stride, int32_t* out_idx,
+                   int32_t* seq_lens, int seq_mode, int seq_val, hipStream_t s);
+
+}  // namespace q3

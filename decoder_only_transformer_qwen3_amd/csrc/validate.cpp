@@ -1,0 +1,121 @@
+// Host-only validation of C-ABI arguments (see validate.hpp).  The order of
+// checks fixes which code a call with several faults gets:
+// NULL, then SHAPE, then POSITION, then ALIGN, then WORKSPACE.
+#include "validate.hpp"
+
+namespace q3v {
+
+static inline size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+static inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+static inline bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+WsLayout ws_layout(int32_t batch, int32_t n_tokens) {
+  WsLayout L{};
+  if (batch < 1 || n_tokens < 1) return L;
+  const size_t M = (size_t)batch * (size_t)n_tokens;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = up256(off + bytes);
+    return at;
+  };
+  L.resid = take(M * Q3_HIDDEN * 4);
+  L.h = take(M * Q3_HIDDEN * 2);
+  L.qkv = take(M * Q3_QKV_ROWS * 2);
+  L.qr = take(M * Q3_N_HEADS * Q3_HEAD_DIM * 2);
+  L.ao = take(M * Q3_N_HEADS * Q3_HEAD_DIM * 2);
+  L.act = take(M * Q3_INTER * 2);
+  L.part = take(M <= (size_t)SKINNY_MAX_ROWS ? (size_t)PART_MAX_SPLIT * M * Q3_HIDDEN * 4 : 0);
+  L.apart = take(n_tokens == 1 ? (size_t)batch * Q3_N_HEADS * DEC_SPLIT_MAX * (Q3_HEAD_DIM + 2) * 4 : 0);
+  L.logits = take((size_t)batch * Q3_VOCAB * 4);
+  L.fh = take((size_t)batch * Q3_HIDDEN * 2);
+  L.total = off;
+  return L;
+}
+
+int decode_splits(int32_t batch, int32_t ctx) {
+  const int target_workgroups = 2048;
+  const int pairs = batch * Q3_N_KV_HEADS;
+  int s = (target_workgroups + pairs - 1) / pairs;
+  const int cap = (ctx + 63) / 64;
+  if (s > cap) s = cap;
+  if (s > DEC_SPLIT_MAX) s = DEC_SPLIT_MAX;
+  if (s < 1) s = 1;
+  return s;
+}
+
+static int layer_ptrs_null(const q3_layer_weights* w) {
+  return !w->input_norm || !w->w_qkv || !w->q_norm || !w->k_norm || !w->w_o || !w->post_norm || !w->w_gate_up ||
+         !w->w_down;
+}
+static int layer_ptrs_misaligned(const q3_layer_weights* w) {
+  return !al16(w->input_norm) || !al16(w->w_qkv) || !al16(w->q_norm) || !al16(w->k_norm) || !al16(w->w_o) ||
+         !al16(w->post_norm) || !al16(w->w_gate_up) || !al16(w->w_down);
+}
+static int model_null(const q3_model* m) {
+  if (!m->embed || !m->final_norm || !m->rope_cos || !m->rope_sin) return 1;
+  for (int l = 0; l < Q3_N_LAYERS; ++l)
+    if (layer_ptrs_null(&m->layer[l])) return 1;
+  return 0;
+}
+static int model_misaligned(const q3_model* m) {
+  if (!al16(m->embed) || !al16(m->final_norm) || !al16(m->rope_cos) || !al16(m->rope_sin)) return 1;
+  for (int l = 0; l < Q3_N_LAYERS; ++l)
+    if (layer_ptrs_misaligned(&m->layer[l])) return 1;
+  return 0;
+}
+
+int check_layer_call(const q3_layer_weights* w, const float* rope_cos, const float* rope_sin, const void* k_layer,
+                     const void* v_layer, int32_t batch, int32_t n_tokens, int32_t max_seq, int32_t start_pos,
+                     const float* residual, const void* ws, size_t ws_bytes) {
+  if (!w || !rope_cos || !rope_sin || !k_layer || !v_layer || !residual || !ws) return Q3_ERR_NULL;
+  if (layer_ptrs_null(w)) return Q3_ERR_NULL;
+  if (batch < 1 || n_tokens < 1 || max_seq < 1 || max_seq > Q3_MAX_POS) return Q3_ERR_SHAPE;
+  if ((int64_t)batch * n_tokens > MAX_TOKENS) return Q3_ERR_SHAPE;
+  if (start_pos < 0 || (int64_t)start_pos + n_tokens > max_seq) return Q3_ERR_POSITION;
+  if (layer_ptrs_misaligned(w) || !al16(rope_cos) || !al16(rope_sin) || !al16(k_layer) || !al16(v_layer) ||
+      !al16(residual) || !al16(ws))
+    return Q3_ERR_ALIGN;
+  if (ws_bytes < ws_layout(batch, n_tokens).total) return Q3_ERR_WORKSPACE;
+  return Q3_OK;
+}
+
+int check_prefill_call(const q3_model* m, const q3_kv* kv, int32_t batch, int32_t prompt_len, const int32_t* ids,
+                       const float* last_logits, const int32_t* next_ids, const int32_t* seq_lens, const void* ws,
+                       size_t ws_bytes) {
+  if (!m || !kv || !ids || !next_ids || !seq_lens || !ws) return Q3_ERR_NULL;
+  if (model_null(m) || !kv->k || !kv->v) return Q3_ERR_NULL;
+  if (kv->batch < 1 || kv->max_seq < 1 || kv->max_seq > Q3_MAX_POS) return Q3_ERR_SHAPE;
+  if (batch < 1 || batch > kv->batch || prompt_len < 1) return Q3_ERR_SHAPE;
+  if ((int64_t)batch * prompt_len > MAX_TOKENS) return Q3_ERR_SHAPE;
+  if (prompt_len > kv->max_seq) return Q3_ERR_POSITION;
+  if (model_misaligned(m) || !al16(kv->k) || !al16(kv->v) || !al4(ids) || !al4(next_ids) || !al4(seq_lens) ||
+      (last_logits && !al16(last_logits)) || !al16(ws))
+    return Q3_ERR_ALIGN;
+  if (ws_bytes < ws_layout(batch, prompt_len).total) return Q3_ERR_WORKSPACE;
+  return Q3_OK;
+}
+
+int check_decode_call(const q3_model* m, const q3_kv* kv, int32_t batch, const int32_t* in_ids,
+                      const int32_t* seq_lens, int32_t max_len_hint, const float* logits, const int32_t* out_ids,
+                      const void* ws, size_t ws_bytes) {
+  if (!m || !kv || !in_ids || !seq_lens || !out_ids || !ws) return Q3_ERR_NULL;
+  if (model_null(m) || !kv->k || !kv->v) return Q3_ERR_NULL;
+  if (kv->batch < 1 || kv->max_seq < 1 || kv->max_seq > Q3_MAX_POS) return Q3_ERR_SHAPE;
+  if (batch < 1 || batch > kv->batch) return Q3_ERR_SHAPE;
+  if (max_len_hint < 1 || max_len_hint > kv->max_seq) return Q3_ERR_POSITION;
+  if (model_misaligned(m) || !al16(kv->k) || !al16(kv->v) || !al4(in_ids) || !al4(seq_lens) || !al4(out_ids) ||
+      (logits && !al16(logits)) || !al16(ws))
+    return Q3_ERR_ALIGN;
+  if (ws_bytes < ws_layout(batch, 1).total) return Q3_ERR_WORKSPACE;
+  return Q3_OK;
+}
+
+int check_argmax_call(const float* logits, int32_t rows, int32_t vocab, int64_t row_stride, const int32_t* out_idx) {
+  if (!logits || !out_idx) return Q3_ERR_NULL;
+  if (rows < 1 || vocab < 1 || row_stride < vocab) return Q3_ERR_SHAPE;
+  if (!al4(logits) || !al4(out_idx)) return Q3_ERR_ALIGN;
+  return Q3_OK;
+}
+
+}  // namespace q3v

@@ -1,0 +1,43 @@
+// Host-only argument validation and workspace layout for the C ABI.
+// Plain C++ (no HIP), so it is also built and tested on its own with
+// g++ and the address/undefined-behaviour sanitizers.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/q3.h"
+
+namespace q3v {
+
+constexpr int PART_MAX_SPLIT = 8;    // skinny-GEMM K splits held in the workspace
+constexpr int DEC_SPLIT_MAX = 64;    // decode-attention splits held in the workspace
+constexpr int SKINNY_MAX_ROWS = 64;  // row counts up to this use the skinny GEMM
+constexpr int64_t MAX_TOKENS = 1 << 22;
+
+struct WsLayout {
+  size_t resid, h, qkv, qr, ao, act, part, apart, logits, fh;
+  size_t total;
+};
+
+// Byte offsets of every workspace region for `batch` x `n_tokens` (256-B aligned).
+WsLayout ws_layout(int32_t batch, int32_t n_tokens);
+
+// Number of decode-attention splits for `batch` sequences of at most `ctx` keys.
+int decode_splits(int32_t batch, int32_t ctx);
+
+int check_layer_call(const q3_layer_weights* w, const float* rope_cos, const float* rope_sin, const void* k_layer,
+                     const void* v_layer, int32_t batch, int32_t n_tokens, int32_t max_seq, int32_t start_pos,
+                     const float* residual, const void* ws, size_t ws_bytes);
+
+int check_prefill_call(const q3_model* m, const q3_kv* kv, int32_t batch, int32_t prompt_len, const int32_t* ids,
+                       const float* last_logits, const int32_t* next_ids, const int32_t* seq_lens, const void* ws,
+                       size_t ws_bytes);
+
+int check_decode_call(const q3_model* m, const q3_kv* kv, int32_t batch, const int32_t* in_ids,
+                      const int32_t* seq_lens, int32_t max_len_hint, const float* logits, const int32_t* out_ids,
+                      const void* ws, size_t ws_bytes);
+
+int check_argmax_call(const float* logits, int32_t rows, int32_t vocab, int64_t row_stride, const int32_t* out_idx);
+
+}  // namespace q3v

@@ -1,0 +1,208 @@
+/*
+ * q3.h -- C ABI of the Qwen3-0.6B-shape decoder forward on MI355X (gfx950).
+ *
+ * The model computed is the Qwen3 decoder as the source pages define it:
+ *   - "手写Qwen3-0.6B推理": sections Qwen3Model, Qwen3DecoderLayer,
+ *     Qwen3RMSNorm, Attention, Rope, MLP, 推理 (greedy argmax loop);
+ *   - "第 3 章 前向与生成（代码走读）": 3.2 (fused residual + RMSNorm),
+ *     3.3 (merged QKV projection, q/k norm, RoPE, causal GQA),
+ *     3.4 (merged gate/up + silu(gate)*up), 4.1 (lm_head on the last
+ *     position only), 4.3 (greedy argmax);
+ *   - "古法手撕简易LLM推理器": sections 工具函数 (RMSNorm, RoPE table,
+ *     SiLU), 核心计算函数与Transformer层 (KV cache holds normed+rotated K
+ *     and raw V), prefill与predict (prefill, then one token per step with a
+ *     growing offset);
+ *   - "Pytorch手写大模型推理": section 模型 (configuration values).
+ *
+ * Shapes are fixed at compile time (Qwen3-0.6B): hidden C = 1024, 16 query
+ * heads, 8 KV heads, head_dim D = 128, intermediate I = 3072, vocab
+ * V = 151936, 28 layers, RMSNorm eps = 1e-6, RoPE theta = 1e6,
+ * max position 40960.  Only batch, token count, positions and cache
+ * capacity vary at run time.
+ *
+ * Conventions
+ *   - Every floating-point weight and activation buffer is bfloat16 (raw
+ *     16-bit patterns) unless stated; the residual stream is float32.
+ *   - Every projection weight is row-major [out, in] and applied as
+ *     y = x W^T (no bias).
+ *   - All pointers are DEVICE pointers unless stated, 16-byte aligned.
+ *   - The caller owns all memory.  The library never allocates, never
+ *     frees, keeps no state between calls and never synchronises: each
+ *     call validates its arguments on the host, enqueues kernels on
+ *     `stream` (a hipStream_t; NULL = the default stream) and returns.
+ *   - On a validation error nothing is enqueued and nothing is written.
+ *     Device-side faults surface at the caller's next synchronisation.
+ *   - Calls that share a workspace or KV cache must be ordered on one
+ *     stream; concurrent calls on different streams need their own
+ *     workspaces.
+ */
+#ifndef Q3_H
+#define Q3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q3_HIDDEN 1024
+#define Q3_N_HEADS 16
+#define Q3_N_KV_HEADS 8
+#define Q3_HEAD_DIM 128
+#define Q3_INTER 3072
+#define Q3_VOCAB 151936
+#define Q3_N_LAYERS 28
+#define Q3_MAX_POS 40960
+#define Q3_QKV_ROWS 4096     /* 2048 q rows | 1024 k rows | 1024 v rows */
+#define Q3_GATE_UP_ROWS 6144 /* 3072 gate rows | 3072 up rows */
+
+/* Status codes returned by every entry point. */
+enum {
+  Q3_OK = 0,
+  Q3_ERR_NULL = -1,      /* a required pointer is NULL */
+  Q3_ERR_SHAPE = -2,     /* batch/token count < 1, or above a stated limit */
+  Q3_ERR_POSITION = -3,  /* positions exceed the cache capacity or 40960 */
+  Q3_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned */
+  Q3_ERR_WORKSPACE = -5, /* workspace smaller than q3_workspace_bytes() */
+  Q3_ERR_HIP = -6        /* a kernel launch failed (hipGetLastError) */
+};
+
+/* One decoder layer ("手写Qwen3-0.6B推理" §打印模型结构 lists the tensors;
+ * the merged row order follows "第 3 章" §3.3 and §3.4). */
+typedef struct {
+  const void *input_norm; /* [1024]        input_layernorm gain           */
+  const void *w_qkv;      /* [4096, 1024]  rows 0..2047 q_proj,
+                                            2048..3071 k_proj, 3072..4095 v_proj */
+  const void *q_norm;     /* [128]         shared by the 16 query heads   */
+  const void *k_norm;     /* [128]         shared by the 8 KV heads       */
+  const void *w_o;        /* [1024, 2048]  o_proj                         */
+  const void *post_norm;  /* [1024]        post_attention_layernorm gain  */
+  const void *w_gate_up;  /* [6144, 1024]  rows 0..3071 gate_proj,
+                                            3072..6143 up_proj             */
+  const void *w_down;     /* [1024, 3072]  down_proj                      */
+} q3_layer_weights;
+
+/* Whole model.  The lm_head is tied to the embedding
+ * ("手写Qwen3-0.6B推理" §Qwen3Model; tie_word_embeddings on
+ * "Pytorch手写大模型推理" §模型). */
+typedef struct {
+  const void *embed;      /* [151936, 1024] embedding and lm_head         */
+  const void *final_norm; /* [1024]                                       */
+  q3_layer_weights layer[Q3_N_LAYERS];
+  const float *rope_cos;  /* [40960, 64] float32, from q3_rope_table_host */
+  const float *rope_sin;  /* [40960, 64] float32                          */
+} q3_model;
+
+/* KV cache: K after q/k-norm and RoPE, raw V ("古法手撕简易LLM推理器"
+ * §核心计算函数与Transformer层), each bf16
+ * [28][batch][8][max_seq][128] contiguous.  Row p of a sequence holds
+ * position p. */
+typedef struct {
+  void *k;
+  void *v;
+  int32_t batch;
+  int32_t max_seq;        /* 1 .. 40960 */
+} q3_kv;
+
+/* Human-readable text for a status code (static storage). */
+const char *q3_status_str(int status);
+
+/* HOST function.  Fills the RoPE tables cos_out/sin_out (host memory,
+ * float32 [40960, 64] each): entry [p, i] = cos/sin(p * 1e6^(-2i/128)),
+ * evaluated in double precision and rounded once to float32
+ * ("古法手撕简易LLM推理器" §工具函数 precomputes the same table up to
+ * max_position_embeddings; "手写Qwen3-0.6B推理" §Rope gives the inverse
+ * frequencies).  Dimension i < 64 pairs with i + 64 (half-swap form), so
+ * the 128-wide table of the pages is these 64 columns twice.
+ * Returns Q3_ERR_NULL on NULL pointers. */
+int q3_rope_table_host(float *cos_out, float *sin_out);
+
+/* Bytes of device workspace needed by a q3_layer_forward,
+ * q3_prefill or q3_decode_step call with `batch` sequences of
+ * `n_tokens` new tokens each (n_tokens = 1 for q3_decode_step).
+ * Returns 0 for non-positive arguments. */
+size_t q3_workspace_bytes(int32_t batch, int32_t n_tokens);
+
+/* One decoder layer over batch x n_tokens new tokens at positions
+ * start_pos .. start_pos + n_tokens - 1 of every sequence
+ * ("手写Qwen3-0.6B推理" §Qwen3DecoderLayer: h = x + Attn(RMSNorm(x)),
+ * out = h + MLP(RMSNorm(h)); attention per §Attention with q/k RMSNorm,
+ * NeoX RoPE, causal GQA where query head h reads KV head h/2, scale
+ * 1/sqrt(128); MLP per §MLP).
+ *   w           layer weights (device pointers inside a HOST struct)
+ *   rope_cos/sin  [40960, 64] float32 device tables
+ *   k_layer, v_layer  this layer's cache, bf16 [batch][8][max_seq][128];
+ *               rows start_pos .. start_pos+n_tokens-1 are written, rows
+ *               0 .. start_pos-1 must already hold the earlier positions.
+ *   residual    in/out float32 [batch * n_tokens, 1024], row b*n_tokens+t.
+ *   ws          device workspace of at least
+ *               q3_workspace_bytes(batch, n_tokens) bytes.
+ * Errors: Q3_ERR_NULL, Q3_ERR_SHAPE (batch < 1, n_tokens < 1,
+ * max_seq < 1 or > 40960), Q3_ERR_POSITION (start_pos < 0 or
+ * start_pos + n_tokens > max_seq), Q3_ERR_ALIGN, Q3_ERR_WORKSPACE,
+ * Q3_ERR_HIP. */
+int q3_layer_forward(const q3_layer_weights *w, const float *rope_cos, const float *rope_sin,
+                     void *k_layer, void *v_layer, int32_t batch, int32_t n_tokens,
+                     int32_t max_seq, int32_t start_pos, float *residual, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/* Prefill of `batch` prompts of equal length prompt_len from position 0
+ * ("古法手撕简易LLM推理器" §prefill与predict: prefill then the next-token
+ * choice; "第 3 章" §4.1: logits only at each sequence's last position).
+ *   kv          cache (HOST struct of device pointers); rows
+ *               0 .. prompt_len-1 of every layer are overwritten.
+ *   ids         int32 [batch, prompt_len], values in [0, 151936).
+ *   last_logits float32 [batch, 151936] logits of the last position, or
+ *               NULL to skip writing them.
+ *   next_ids    int32 [batch]: greedy argmax of those logits (lowest
+ *               index among equal maxima).
+ *   seq_lens    int32 [batch]: set to prompt_len.
+ * Errors: Q3_ERR_NULL, Q3_ERR_SHAPE (batch < 1 or > kv->batch,
+ * prompt_len < 1), Q3_ERR_POSITION (prompt_len > kv->max_seq),
+ * Q3_ERR_ALIGN, Q3_ERR_WORKSPACE (q3_workspace_bytes(batch, prompt_len)),
+ * Q3_ERR_HIP. */
+int q3_prefill(const q3_model *m, const q3_kv *kv, int32_t batch, int32_t prompt_len,
+               const int32_t *ids, float *last_logits, int32_t *next_ids, int32_t *seq_lens,
+               void *ws, size_t ws_bytes, void *stream);
+
+/* One greedy decode step for `batch` sequences ("古法手撕简易LLM推理器"
+ * §prefill与predict, predict loop): sequence b feeds token in_ids[b] at
+ * position seq_lens[b], appends its K/V at that cache row, attends to rows
+ * 0 .. seq_lens[b], and on exit out_ids[b] holds the argmax of its logits
+ * and seq_lens[b] has grown by one.  Lengths may differ per sequence.
+ *   in_ids      int32 [batch] (may alias out_ids).
+ *   seq_lens    int32 [batch] device lengths (read and advanced on device,
+ *               so consecutive steps need no host round trip).
+ *   max_len_hint  host-side upper bound on max(seq_lens) + 1; only sizes
+ *               the attention split.  Must be in 1 .. kv->max_seq.  Any
+ *               device length below kv->max_seq is handled correctly
+ *               whatever the hint; a length >= kv->max_seq is a caller
+ *               error: its cache write is skipped and its outputs are
+ *               unspecified (no out-of-bounds access).
+ *   logits      float32 [batch, 151936], or NULL.
+ * Errors: Q3_ERR_NULL, Q3_ERR_SHAPE (batch < 1 or > kv->batch),
+ * Q3_ERR_POSITION (max_len_hint out of range), Q3_ERR_ALIGN,
+ * Q3_ERR_WORKSPACE (q3_workspace_bytes(batch, 1)), Q3_ERR_HIP. */
+int q3_decode_step(const q3_model *m, const q3_kv *kv, int32_t batch, const int32_t *in_ids,
+                   int32_t *seq_lens, int32_t max_len_hint, float *logits, int32_t *out_ids,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/* Row-wise greedy argmax ("手写Qwen3-0.6B推理" §推理; "第 3 章" §4.3):
+ * out_idx[r] = lowest index v with logits[r*row_stride + v] equal to the
+ * row maximum (a NaN counts as larger than every number; the first NaN
+ * wins).
+ *   logits      float32, `rows` rows of `vocab` values, row_stride
+ *               elements apart (row_stride >= vocab; 16-byte aligned rows
+ *               are faster but not required).
+ *   out_idx     int32 [rows].
+ * Errors: Q3_ERR_NULL, Q3_ERR_SHAPE (rows < 1, vocab < 1,
+ * row_stride < vocab), Q3_ERR_HIP. */
+int q3_argmax(const float *logits, int32_t rows, int32_t vocab, int64_t row_stride,
+              int32_t *out_idx, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q3_H */

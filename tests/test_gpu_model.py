@@ -1,0 +1,159 @@
+"""GPU parity of the full 28-layer stack (q3_prefill, q3_decode_step)
+against the float64 oracle, through the C ABI.
+
+Greedy tokens follow the protocol in gpu_common.check_greedy_step: the GPU
+runs free, the oracle is teacher-forced on the GPU's tokens, every step's
+logits must be within the relative tolerance, and a token may differ from
+the oracle's argmax only at a near tie inside the measured error.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from decoder_only_transformer_qwen3_amd import inputs as I
+
+from gpu_common import GreedyReport, REL_TOL, check_greedy_step, log, rel_err
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decoder_only_transformer_qwen3_amd import binding, device
+    return binding, device
+
+
+@pytest.fixture(scope="module")
+def models(lib):
+    B, dev = lib
+    log("[model] generating 28-layer random-init weights (seed 0)")
+    bits = I.model_weights(0)
+    dm = dev.DeviceModel(bits)
+    om = O.Model(bits)
+    return dm, om
+
+
+def test_prefill_then_64_greedy_steps(lib, models):
+    """Full stack, batch 1, 128-token prompt, prefill then 64 greedy decode steps."""
+    B, dev = lib
+    dm, om = models
+    T, steps = 128, 64
+    ids = I.token_ids(1, (1, T))
+    kv = dev.DeviceKV(1, T + steps)
+    ids_d = torch.from_numpy(ids).cuda()
+    logits = torch.empty((1, B.VOCAB), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+    seq = torch.empty(1, dtype=torch.int32, device="cuda")
+    ws, nb = dev.workspace(1, T)
+    log("[model] prefill 1 x 128")
+    B.q3_prefill(dm.struct, kv.struct, 1, T, ids_d, logits, nxt, seq, ws, nb)
+    torch.cuda.synchronize()
+    assert int(seq.item()) == T
+    gpu_logits = [logits.cpu().numpy()[0].copy()]
+    gpu_tokens = [int(nxt.item())]
+    # the returned token is the argmax of the returned logits, exactly
+    assert gpu_tokens[0] == int(np.argmax(gpu_logits[0]))
+    wsd, nbd = dev.workspace(1, 1)
+    for i in range(steps):
+        B.q3_decode_step(dm.struct, kv.struct, 1, nxt, seq, T + steps, logits, nxt, wsd, nbd)
+        torch.cuda.synchronize()
+        lg = logits.cpu().numpy()[0].copy()
+        tok = int(nxt.item())
+        assert tok == int(np.argmax(lg))
+        gpu_logits.append(lg)
+        gpu_tokens.append(tok)
+    assert int(seq.item()) == T + steps
+    log(f"[model] gpu tokens: {gpu_tokens}")
+
+    log("[model] oracle, teacher-forced on the GPU tokens")
+    _, o_logits = O.generate_cached(om, ids, steps + 1, forced=gpu_tokens)
+    rep = GreedyReport()
+    for i in range(steps + 1):
+        check_greedy_step(rep, gpu_tokens[i], gpu_logits[i], o_logits[i])
+    if rep.strict_prefix is None:
+        rep.strict_prefix = steps + 1
+    log(f"[model] greedy report: {rep}")
+
+
+def test_decode_sequences_of_different_lengths(lib, models):
+    """Batch 4 decode where each sequence sits at its own length."""
+    B, dev = lib
+    dm, om = models
+    T0, lens = 24, [24, 17, 9, 21]
+    ids = I.token_ids(2, (4, T0 + 3))
+    kv = dev.DeviceKV(4, 40)
+    ws, nb = dev.workspace(4, T0)
+    nxt = torch.empty(4, dtype=torch.int32, device="cuda")
+    seq = torch.empty(4, dtype=torch.int32, device="cuda")
+    B.q3_prefill(dm.struct, kv.struct, 4, T0, torch.from_numpy(np.ascontiguousarray(ids[:, :T0])).cuda(), None,
+                 nxt, seq, ws, nb)
+    # truncate sequences to their own lengths; feed the next prompt token of each
+    seq.copy_(torch.tensor(lens, dtype=torch.int32))
+    feed = torch.tensor([int(ids[b, lens[b]]) for b in range(4)], dtype=torch.int32, device="cuda")
+    logits = torch.empty((4, B.VOCAB), dtype=torch.float32, device="cuda")
+    wsd, nbd = dev.workspace(4, 1)
+    B.q3_decode_step(dm.struct, kv.struct, 4, feed, seq, 40, logits, nxt, wsd, nbd)
+    torch.cuda.synchronize()
+    got = logits.cpu().numpy()
+    assert seq.cpu().numpy().tolist() == [n + 1 for n in lens]
+    for b in range(4):
+        ref, _, _, _ = O.prefill(om, ids[b:b + 1, :lens[b] + 1])
+        e = rel_err(got[b], ref[0])
+        log(f"   seq {b} (len {lens[b]}): logits rel={e:.3e}")
+        assert e <= REL_TOL
+        assert int(nxt[b].item()) == int(np.argmax(got[b]))
+
+
+def test_prefill_batch_rows_are_independent_8x4096(lib, models):
+    """Prefill-bound shape 8 x 4096: each sequence's logits equal (bit for bit)
+    those of the same prompt prefilled alone; tokens are the exact argmax."""
+    B, dev = lib
+    dm, om = models
+    Bn, T = 8, 4096
+    ids = I.token_ids(4, (Bn, T))
+    kv = dev.DeviceKV(Bn, T)
+    ws, nb = dev.workspace(Bn, T)
+    logits = torch.empty((Bn, B.VOCAB), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(Bn, dtype=torch.int32, device="cuda")
+    seq = torch.empty(Bn, dtype=torch.int32, device="cuda")
+    log("[model] prefill 8 x 4096")
+    B.q3_prefill(dm.struct, kv.struct, Bn, T, torch.from_numpy(ids).cuda(), logits, nxt, seq, ws, nb)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    assert np.all(np.isfinite(lg))
+    np.testing.assert_array_equal(nxt.cpu().numpy(), np.argmax(lg, axis=1))
+    del kv, ws
+    kv1 = dev.DeviceKV(1, T)
+    ws1, nb1 = dev.workspace(1, T)
+    for b in (0, 6):
+        l1 = torch.empty((1, B.VOCAB), dtype=torch.float32, device="cuda")
+        B.q3_prefill(dm.struct, kv1.struct, 1, T, torch.from_numpy(np.ascontiguousarray(ids[b:b + 1])).cuda(), l1,
+                     nxt[:1], seq[:1], ws1, nb1)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(l1.cpu().numpy()[0], lg[b])
+
+
+def test_prefill_tiled_path_parity(lib, models):
+    """Full stack on the tiled-GEMM + flash-attention path (2 x 300 tokens)."""
+    B, dev = lib
+    dm, om = models
+    ids = I.token_ids(5, (2, 300))
+    kv = dev.DeviceKV(2, 300)
+    ws, nb = dev.workspace(2, 300)
+    logits = torch.empty((2, B.VOCAB), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(2, dtype=torch.int32, device="cuda")
+    seq = torch.empty(2, dtype=torch.int32, device="cuda")
+    B.q3_prefill(dm.struct, kv.struct, 2, 300, torch.from_numpy(ids).cuda(), logits, nxt, seq, ws, nb)
+    torch.cuda.synchronize()
+    got = logits.cpu().numpy()
+    ref, _, _, _ = O.prefill(om, ids)
+    rep = GreedyReport()
+    for b in range(2):
+        e = rel_err(got[b], ref[b])
+        log(f"   seq {b}: logits rel={e:.3e}")
+        check_greedy_step(rep, int(nxt[b].item()), got[b], ref[b])
+    log(f"[model] {rep}")
