@@ -1,0 +1,313 @@
+"""Benchmark of the Qwen3-0.6B-shape forward on one MI355X.
+
+Default workload (the one the headline metric is quoted on): the full
+28-layer stack with random-init bf16 weights, batch 1, a 128-token prompt of
+uniform random ids, prefill, then 64 greedy decode steps with the KV cache.
+One "step" is that whole job; it is captured once as a HIP graph (prefill
+graph + decode-loop graph) and replayed.  value = (prompt + generated
+tokens) / second.
+
+Other workloads (--workload) measure the decode-bound (batch 32, 2048 cached
+positions, 128 steps), prefill-bound (8 x 4096) and long-context (batch 4,
+32768 cached positions, 64 steps) shapes; their setup prefill is untimed.
+
+Besides the JSON line's headline value, the script times the dominant
+kernel in isolation with HIP events on the stream it runs on (through the
+library's q3_linear entry point, same kernel and shape as inside the step)
+for the roofline object, and times the float64 CPU oracle on a bounded
+sample of the same workload for the cpu_baseline object.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill & decode tokens/s (Qwen3-0.6B shape, bf16) + % MFMA/HBM peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+WORKLOADS = {
+    # name: (batch, prompt_len, decode_steps, prefill_timed)
+    "prefill128_decode64": (1, 128, 64, True),
+    "decode_b32_ctx2048": (32, 2048, 128, False),
+    "prefill_8x4096": (8, 4096, 0, True),
+    "decode_b4_ctx32768": (4, 32768, 64, False),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="prefill128_decode64", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-iters", type=int, default=200)
+    return ap.parse_args()
+
+
+class Runner:
+    """Holds device state for one workload and runs prefill / decode phases."""
+
+    def __init__(self, torch, B, dev, dm, batch, prompt_len, steps):
+        self.torch, self.B, self.dev, self.dm = torch, B, dev, dm
+        self.batch, self.T, self.steps = batch, prompt_len, steps
+        from decoder_only_transformer_qwen3_amd import inputs as I
+        self.ids_np = I.token_ids(1000 + batch, (batch, prompt_len))
+        self.ids = torch.from_numpy(self.ids_np).cuda()
+        self.max_seq = prompt_len + max(steps, 1)
+        self.kv = dev.DeviceKV(batch, self.max_seq)
+        self.ws_p, self.nb_p = dev.workspace(batch, prompt_len)
+        self.ws_d, self.nb_d = dev.workspace(batch, 1)
+        self.nxt = torch.zeros(batch, dtype=torch.int32, device="cuda")
+        self.seq = torch.zeros(batch, dtype=torch.int32, device="cuda")
+        self.nxt0 = torch.zeros_like(self.nxt)
+        self.seq0 = torch.zeros_like(self.seq)
+
+    def prefill(self):
+        B = self.B
+        B.q3_prefill(self.dm.struct, self.kv.struct, self.batch, self.T, self.ids, None, self.nxt, self.seq,
+                     self.ws_p, self.nb_p)
+
+    def save_state(self):
+        self.nxt0.copy_(self.nxt)
+        self.seq0.copy_(self.seq)
+
+    def restore_state(self):
+        self.nxt.copy_(self.nxt0)
+        self.seq.copy_(self.seq0)
+
+    def decode_loop(self):
+        B = self.B
+        for _ in range(self.steps):
+            B.q3_decode_step(self.dm.struct, self.kv.struct, self.batch, self.nxt, self.seq, self.max_seq, None,
+                             self.nxt, self.ws_d, self.nb_d)
+
+
+def capture(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm the allocator-free path once on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, capture_error_mode="thread_local"):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def dominant_kernel(torch, B, dev, dm, workload, iters):
+    """Time the dominant kernel alone with HIP events on the current stream.
+
+    Decode workloads: the tied lm_head weight stream at the workload's batch
+    (skinny MFMA GEMM, HBM-bound); prefill: the gate/up projection with the
+    SiLU epilogue at M = batch * prompt_len (tiled MFMA GEMM, MFMA-bound)."""
+    batch, T, steps, _ = WORKLOADS[workload]
+    stream = torch.cuda.current_stream()
+    if workload == "prefill_8x4096":
+        M, N, K = batch * T, 2 * B.INTER, B.HIDDEN
+        x = torch.randn((M, K), device="cuda").to(torch.bfloat16)
+        out = torch.empty((M, N // 2), dtype=torch.bfloat16, device="cuda")
+        w = dm.layers[0].w_gate_up
+        fn = lambda: B.q3_linear(x, w, out, M, N, K, N // 2, B.Q3_EPI_SILU_GATE)
+        flops = 2.0 * M * N * K
+        name, bound = "k_gemm_tiled<EPI_SILU> (gate_up, M=%d N=%d K=%d)" % (M, N, K), "mfma"
+        algo = flops
+    else:
+        M, N, K = batch, B.VOCAB, B.HIDDEN
+        x = torch.randn((M, K), device="cuda").to(torch.bfloat16)
+        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        w = dm.embed
+        fn = lambda: B.q3_linear(x, w, out, M, N, K, N, B.Q3_EPI_STORE_F32)
+        algo = float(N * K * 2 + M * K * 2 + M * N * 4)  # weights once + activations + logits
+        name, bound = "k_gemm_skinny<EPI_F32> (lm_head, M=%d N=%d K=%d)" % (M, N, K), "hbm"
+    for _ in range(5):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * iters)]
+    for i in range(iters):
+        ev[2 * i].record(stream)
+        fn()
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    durs = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(iters)]) * 1e-3  # s
+    t = float(np.mean(durs))
+    if bound == "hbm":
+        achieved, peak, unit = algo / t / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = algo / t / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+    return {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": None, "kernel": name,
+            "avg_launch_us": round(t * 1e6, 2), "algorithmic_per_launch": algo}
+
+
+def cpu_baseline(workload, bits):
+    """The float64 oracle on a bounded sample of the workload (host cores)."""
+    import oracle as O
+    from decoder_only_transformer_qwen3_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        ncores = len(os.sched_getaffinity(0))
+        threadpool_limits(limits=ncores)
+        info = threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    batch, T, steps, _ = WORKLOADS[workload]
+    t0 = time.perf_counter()
+    om = O.Model(bits)
+    setup = time.perf_counter() - t0
+    ids = I.token_ids(1000 + batch, (batch, T))[:1]
+    if workload == "prefill128_decode64":
+        n_dec = steps  # the whole workload: prefill + every decode step
+        t0 = time.perf_counter()
+        _, nxt, cache, _ = O.prefill(om, ids, max_seq=T + n_dec)
+        tok = int(nxt[0])
+        for i in range(n_dec):
+            _, nx = O.decode_step(om, cache, [tok], [T + i])
+            tok = int(nx[0])
+        el = time.perf_counter() - t0
+        sample = f"sequence 0: {T}-token prefill + {n_dec} greedy decode steps ({T + n_dec} tokens)"
+        toks = T + n_dec
+    elif workload == "prefill_8x4096":
+        Tp = 1024
+        t0 = time.perf_counter()
+        O.prefill(om, ids[:, :Tp])
+        el = time.perf_counter() - t0
+        sample = f"sequence 0, first {Tp} prompt tokens: prefill"
+        toks = Tp
+    else:
+        # decode-bound: the oracle decodes the whole batch at once; a float64 KV cache of the
+        # workload's length would not fit in host memory, so the steps run over a 16-token cache
+        Tp, n_dec = 16, 4
+        idsb = I.token_ids(1000 + batch, (batch, T))[:, :Tp]
+        _, nxt, cache, _ = O.prefill(om, idsb, max_seq=Tp + n_dec)
+        toks_in = nxt
+        t0 = time.perf_counter()
+        for i in range(n_dec):
+            _, toks_in = O.decode_step(om, cache, toks_in, np.full(batch, Tp + i))
+        el = time.perf_counter() - t0
+        sample = (f"batch {batch}: {n_dec} greedy decode steps over a {Tp}-token cache "
+                  f"(untimed {Tp}-token prefill)")
+        toks = batch * n_dec
+    return {"value": round(toks / el, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample, "seconds": round(el, 2), "weights_setup_s": round(setup, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+    import torch
+    from decoder_only_transformer_qwen3_amd import binding as B
+    from decoder_only_transformer_qwen3_amd import device as dev
+    from decoder_only_transformer_qwen3_amd import inputs as I
+
+    torch.cuda.set_device(0)
+    batch, T, steps, prefill_timed = WORKLOADS[args.workload]
+    log(f"[bench] workload {args.workload}: batch {batch}, prompt {T}, decode steps {steps}")
+    bits = I.model_weights(0)
+    dm = dev.DeviceModel(bits)
+    r = Runner(torch, B, dev, dm, batch, T, steps)
+
+    use_graph = not args.no_graph
+    # setup prefill (untimed); decode-only workloads restart from this state each step
+    r.prefill()
+    torch.cuda.synchronize()
+    r.save_state()
+
+    if prefill_timed:
+        phase_a, phase_b = r.prefill, (r.decode_loop if steps > 0 else None)
+    else:
+        phase_a, phase_b = None, (lambda: (r.restore_state(), r.decode_loop()))
+    g_a = g_b = None
+    if use_graph:
+        try:
+            if phase_a is not None:
+                g_a = capture(torch, phase_a)
+            if phase_b is not None:
+                r.prefill()  # capture's warm-up run of the decode loop starts from a fresh prefill state
+                torch.cuda.synchronize()
+                g_b = capture(torch, phase_b)
+        except Exception as e:  # pragma: no cover
+            log(f"[bench] graph capture failed ({e}); running eagerly")
+            g_a = g_b = None
+            use_graph = False
+
+    stream = torch.cuda.current_stream()
+
+    def one_step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        if phase_a is not None:
+            g_a.replay() if g_a is not None else phase_a()
+        if ev:
+            ev[1].record(stream)
+        if phase_b is not None:
+            g_b.replay() if g_b is not None else phase_b()
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    step_ms = wall * 1e3 / args.steps
+
+    tokens_prefill = batch * T if prefill_timed else 0
+    tokens_decode = batch * steps
+    value = (tokens_prefill + tokens_decode) / (step_ms * 1e-3)
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (random-init weights N(0,0.02), uniform random token ids)",
+        "config": {"workload": args.workload, "layers": 28, "batch": batch, "prompt_len": T,
+                   "decode_steps": steps, "prefill_timed": prefill_timed, "hip_graph": use_graph,
+                   "parallelism": "single GPU"},
+        "prefill_ms": round(pre_ms, 4), "decode_ms": round(dec_ms, 4),
+        "prefill_tok_s": round(tokens_prefill / (pre_ms * 1e-3), 1) if prefill_timed else None,
+        "decode_tok_s": round(tokens_decode / (dec_ms * 1e-3), 1) if steps > 0 else None,
+    }
+    try:
+        out["roofline"] = dominant_kernel(torch, B, dev, dm, args.workload, args.kernel_iters)
+    except Exception as e:  # pragma: no cover
+        log(f"[bench] kernel timing failed: {e}")
+        out["roofline"] = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the float64 oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(args.workload, bits)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -61,9 +61,12 @@ _prefill = _sig("q3_prefill", ctypes.c_int, ctypes.POINTER(q3_model), ctypes.POI
 _decode = _sig("q3_decode_step", ctypes.c_int, ctypes.POINTER(q3_model), ctypes.POINTER(q3_kv), _i32, _vp,
                _vp, _i32, _vp, _vp, _vp, _sz, _vp)
 _argmax = _sig("q3_argmax", ctypes.c_int, _vp, _i32, _i32, _i64, _vp, _vp)
+_linear = _sig("q3_linear", ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp)
+
+Q3_EPI_STORE_BF16, Q3_EPI_STORE_F32, Q3_EPI_ADD_F32, Q3_EPI_SILU_GATE = 0, 1, 2, 3
 
 EXPORTS = ("q3_status_str", "q3_rope_table_host", "q3_workspace_bytes", "q3_layer_forward",
-           "q3_prefill", "q3_decode_step", "q3_argmax")
+           "q3_prefill", "q3_decode_step", "q3_argmax", "q3_linear")
 
 
 class Q3Error(RuntimeError):
@@ -146,4 +149,11 @@ def q3_argmax(logits, rows, vocab, row_stride, out_idx, stream=None, check=True)
     st = _argmax(_ptr(logits), rows, vocab, row_stride, _ptr(out_idx), _stream(stream))
     if check:
         _check(st, "q3_argmax")
+    return st
+
+
+def q3_linear(x, w, out, m, n, k, ldo, epilogue, stream=None, check=True) -> int:
+    st = _linear(_ptr(x), _ptr(w), _ptr(out), m, n, k, ldo, epilogue, _stream(stream))
+    if check:
+        _check(st, "q3_linear")
     return st

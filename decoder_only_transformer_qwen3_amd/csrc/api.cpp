@@ -11,6 +11,10 @@
 
 using namespace q3;
 
+static_assert(Q3_EPI_STORE_BF16 == EPI_BF16 && Q3_EPI_STORE_F32 == EPI_F32 && Q3_EPI_ADD_F32 == EPI_ADD_F32 &&
+                  Q3_EPI_SILU_GATE == EPI_SILU,
+              "public epilogue ids must match the kernel epilogue ids");
+
 namespace {
 
 // Skinny-GEMM K splits: o_proj K = 2048 -> 4 x 512, down K = 3072 -> 6 x 512.
@@ -242,6 +246,19 @@ int q3_decode_step(const q3_model* m, const q3_kv* kv, int32_t batch, const int3
     run_layer(c, pending);
   }
   run_head(m, wsp, wsp.resid, pending, batch, 1, logits ? logits : wsp.logits, out_ids, seq_lens, 2, 0, s);
+  return launch_status();
+}
+
+int q3_linear(const void* x, const void* w, void* out, int32_t m, int32_t n, int32_t k, int32_t ldo, int32_t epilogue,
+              void* stream) {
+  const int st = q3v::check_linear_call(x, w, out, m, n, k, ldo, epilogue);
+  if (st != Q3_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const Epi e = static_cast<Epi>(epilogue);  // Q3_EPI_* values equal the internal epilogue ids
+  if (m <= q3v::SKINNY_MAX_ROWS)
+    launch_gemm_skinny(U(x), U(w), out, m, n, k, ldo, 1, e, s);
+  else
+    launch_gemm_tiled(U(x), U(w), out, m, n, k, ldo, e, s);
   return launch_status();
 }
 

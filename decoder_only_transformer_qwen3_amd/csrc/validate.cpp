@@ -111,6 +111,18 @@ int check_decode_call(const q3_model* m, const q3_kv* kv, int32_t batch, const i
   return Q3_OK;
 }
 
+int check_linear_call(const void* x, const void* w, const void* out, int32_t m, int32_t n, int32_t k, int32_t ldo,
+                      int32_t epilogue) {
+  if (!x || !w || !out) return Q3_ERR_NULL;
+  if (epilogue < Q3_EPI_STORE_BF16 || epilogue > Q3_EPI_SILU_GATE) return Q3_ERR_SHAPE;
+  if (m < 1 || n < 128 || k < 512 || (n % 128) != 0 || (k % 512) != 0) return Q3_ERR_SHAPE;
+  if ((int64_t)m > MAX_TOKENS) return Q3_ERR_SHAPE;
+  const int32_t out_cols = epilogue == Q3_EPI_SILU_GATE ? n / 2 : n;
+  if (ldo < out_cols || (ldo % 4) != 0) return Q3_ERR_SHAPE;
+  if (!al16(x) || !al16(w) || !al16(out)) return Q3_ERR_ALIGN;
+  return Q3_OK;
+}
+
 int check_argmax_call(const float* logits, int32_t rows, int32_t vocab, int64_t row_stride, const int32_t* out_idx) {
   if (!logits || !out_idx) return Q3_ERR_NULL;
   if (rows < 1 || vocab < 1 || row_stride < vocab) return Q3_ERR_SHAPE;

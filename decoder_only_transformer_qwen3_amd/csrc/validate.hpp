@@ -38,6 +38,9 @@ int check_decode_call(const q3_model* m, const q3_kv* kv, int32_t batch, const i
                       const int32_t* seq_lens, int32_t max_len_hint, const float* logits, const int32_t* out_ids,
                       const void* ws, size_t ws_bytes);
 
+int check_linear_call(const void* x, const void* w, const void* out, int32_t m, int32_t n, int32_t k, int32_t ldo,
+                      int32_t epilogue);
+
 int check_argmax_call(const float* logits, int32_t rows, int32_t vocab, int64_t row_stride, const int32_t* out_idx);
 
 }  // namespace q3v

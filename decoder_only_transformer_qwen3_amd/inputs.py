@@ -118,17 +118,23 @@ def layer_weights(seed: int, i: int, d: Dims = QWEN3_0P6B, std: float = 0.02) ->
 
 
 def model_weights(seed: int = 0, d: Dims = QWEN3_0P6B, n_layers: int | None = None,
-                  std: float = 0.02) -> dict:
+                  std: float = 0.02, threads: int = 8) -> dict:
     """Full model: {'embed', 'final_norm', 'layers': [layer dicts]} as bf16 bits.
 
-    The lm_head is tied to ``embed`` (no separate tensor).
+    The lm_head is tied to ``embed`` (no separate tensor).  Tensors are drawn
+    in parallel threads; each has its own stream, so the result does not
+    depend on the thread count.
     """
+    from concurrent.futures import ThreadPoolExecutor
     n = d.n_layers if n_layers is None else n_layers
-    return {
-        "embed": normal_bf16(seed, "model.embed_tokens.weight", (d.vocab, d.hidden), std=std),
-        "final_norm": normal_bf16(seed, "model.norm.weight", (d.hidden,), std=std, mean=1.0),
-        "layers": [layer_weights(seed, i, d, std) for i in range(n)],
-    }
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        emb = ex.submit(normal_bf16, seed, "model.embed_tokens.weight", (d.vocab, d.hidden), std)
+        layers = list(ex.map(lambda i: layer_weights(seed, i, d, std), range(n)))
+        return {
+            "embed": emb.result(),
+            "final_norm": normal_bf16(seed, "model.norm.weight", (d.hidden,), std=std, mean=1.0),
+            "layers": layers,
+        }
 
 
 def token_ids(seed: int, shape, vocab: int = QWEN3_0P6B.vocab) -> np.ndarray:

@@ -201,6 +201,29 @@ int q3_decode_step(const q3_model *m, const q3_kv *kv, int32_t batch, const int3
 int q3_argmax(const float *logits, int32_t rows, int32_t vocab, int64_t row_stride,
               int32_t *out_idx, void *stream);
 
+
+/* Epilogues of q3_linear. */
+enum {
+  Q3_EPI_STORE_BF16 = 0, /* out bf16 [m, ldo]:  out[i, j] = (x W^T)[i, j]            */
+  Q3_EPI_STORE_F32 = 1,  /* out f32  [m, ldo]                                         */
+  Q3_EPI_ADD_F32 = 2,    /* out f32  [m, ldo] += x W^T  (residual add)                */
+  Q3_EPI_SILU_GATE = 3   /* W is [gate; up] with n rows; out bf16 [m, ldo] holds
+                            silu(x Wg^T) * (x Wu^T), n/2 columns                      */
+};
+
+/* Helper: one projection y = x W^T on the same MFMA GEMM kernels the model
+ * uses (skinny weight-streaming kernel for m <= 64 rows, LDS-tiled kernel
+ * above), e.g. the tied lm_head of "手写Qwen3-0.6B推理" §Qwen3Model or a
+ * merged projection of "第 3 章" §3.3/§3.4.
+ *   x    bf16 [m, k] row-major;  w  bf16 [n, k] row-major ([out, in]).
+ *   out  see the epilogue; ldo is its row stride in elements (>= n, or
+ *        >= n/2 for Q3_EPI_SILU_GATE).
+ * Requirements: m >= 1, n % 128 == 0, k % 512 == 0.
+ * Errors: Q3_ERR_NULL, Q3_ERR_SHAPE (sizes, ldo or epilogue invalid),
+ * Q3_ERR_ALIGN (16-byte alignment), Q3_ERR_HIP. */
+int q3_linear(const void *x, const void *w, void *out, int32_t m, int32_t n, int32_t k, int32_t ldo,
+              int32_t epilogue, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

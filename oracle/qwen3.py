@@ -61,9 +61,13 @@ QWEN3 = Cfg()
 
 def widen_bf16(bits) -> np.ndarray:
     """bfloat16 bit patterns -> float64, exactly (a bf16 value is the top
-    half of a float32)."""
-    b = np.asarray(bits, dtype=np.uint16)
-    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    half of a float32).  Large arrays go through torch's CPU bf16 -> f64
+    conversion (multi-threaded, also exact)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    if b.size >= (1 << 20):
+        import torch
+        return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    return np.left_shift(b, 16, dtype=np.uint32).view(np.float32).astype(np.float64)
 
 
 # ---------------------------------------------------------------- elementwise

@@ -121,6 +121,14 @@ def test_prefill_decode_argmax_reject_bad_arguments(B):
     st = B.q3_decode_step(m, kv, 4, 0x600000, None, 100, None, 0x610000, 0x700000, dneed, stream=0, check=False)
     assert st == B.Q3_ERR_NULL
     assert B.q3_argmax(0x800000, 2, 10, 5, 0x900000, stream=0, check=False) == B.Q3_ERR_SHAPE
+    lin = lambda *a: B.q3_linear(*a, stream=0, check=False)
+    assert lin(None, 0x1000, 0x2000, 1, 128, 512, 128, 0) == B.Q3_ERR_NULL
+    assert lin(0x1000, 0x2000, 0x3000, 1, 100, 512, 128, 0) == B.Q3_ERR_SHAPE
+    assert lin(0x1000, 0x2000, 0x3000, 1, 128, 500, 128, 0) == B.Q3_ERR_SHAPE
+    assert lin(0x1000, 0x2000, 0x3000, 1, 128, 512, 64, 0) == B.Q3_ERR_SHAPE
+    assert lin(0x1000, 0x2000, 0x3000, 0, 128, 512, 128, 0) == B.Q3_ERR_SHAPE
+    assert lin(0x1000, 0x2000, 0x3000, 1, 128, 512, 128, 7) == B.Q3_ERR_SHAPE
+    assert lin(0x1008, 0x2000, 0x3000, 1, 128, 512, 128, 0) == B.Q3_ERR_ALIGN
     assert B.q3_argmax(None, 2, 10, 10, 0x900000, stream=0, check=False) == B.Q3_ERR_NULL
 
 
