@@ -69,7 +69,7 @@ class Runner:
         from decoder_only_transformer_qwen3_amd import inputs as I
         self.ids_np = I.token_ids(1000 + batch, (batch, prompt_len))
         self.ids = torch.from_numpy(self.ids_np).cuda()
-        self.max_seq = prompt_len + max(steps, 1)
+        self.max_seq = (prompt_len + max(steps, 1) + 7) // 8 * 8  # capacity: a multiple of 8
         self.kv = dev.DeviceKV(batch, self.max_seq)
         self.ws_p, self.nb_p = dev.workspace(batch, prompt_len)
         self.ws_d, self.nb_d = dev.workspace(batch, 1)
@@ -94,8 +94,8 @@ class Runner:
     def decode_loop(self):
         B = self.B
         for _ in range(self.steps):
-            B.q3_decode_step(self.dm.struct, self.kv.struct, self.batch, self.nxt, self.seq, self.max_seq, None,
-                             self.nxt, self.ws_d, self.nb_d)
+            B.q3_decode_step(self.dm.struct, self.kv.struct, self.batch, self.nxt, self.seq,
+                             self.T + self.steps, None, self.nxt, self.ws_d, self.nb_d)
 
 
 def capture(torch, fn):

@@ -25,6 +25,7 @@ struct Ws {
   float* resid;
   uint16_t *h, *qkv, *qr, *ao, *act, *fh;
   float *part, *apart, *logits;
+  void* amax;
 };
 
 Ws carve(void* base, int32_t batch, int32_t n_tokens) {
@@ -40,6 +41,7 @@ Ws carve(void* base, int32_t batch, int32_t n_tokens) {
   w.part = reinterpret_cast<float*>(p + L.part);
   w.apart = reinterpret_cast<float*>(p + L.apart);
   w.logits = reinterpret_cast<float*>(p + L.logits);
+  w.amax = p + L.amax;
   w.fh = reinterpret_cast<uint16_t*>(p + L.fh);
   return w;
 }
@@ -108,11 +110,14 @@ void run_head(const q3_model* m, const Ws& ws, float* resid, int pending, int B,
               int32_t* next_ids, int32_t* seq_lens, int seq_mode, int seq_val, hipStream_t s) {
   const int part_rows = B * T;
   launch_rmsnorm(resid, ws.part, pending, part_rows, U(m->final_norm), ws.fh, B, T, T - 1, s);
+  // logits plus each 16-row weight block's (max, argmax) per sequence
+  constexpr int n_part = V / 16;
   for (int r0 = 0; r0 < B; r0 += q3v::SKINNY_MAX_ROWS) {
     const int rows = (B - r0) < q3v::SKINNY_MAX_ROWS ? (B - r0) : q3v::SKINNY_MAX_ROWS;
-    launch_gemm_skinny(ws.fh + (size_t)r0 * C, U(m->embed), logits + (size_t)r0 * V, rows, V, C, V, 1, EPI_F32, s);
+    launch_gemm_skinny(ws.fh + (size_t)r0 * C, U(m->embed), logits + (size_t)r0 * V, rows, V, C, V, 1, EPI_LOGITS, s,
+                       static_cast<char*>(ws.amax) + (size_t)r0 * n_part * 8);
   }
-  launch_argmax(logits, B, V, V, next_ids, seq_lens, seq_mode, seq_val, s);
+  launch_argmax_partials(ws.amax, B, n_part, next_ids, seq_lens, seq_mode, seq_val, s);
 }
 
 inline int launch_status() { return hipGetLastError() == hipSuccess ? Q3_OK : Q3_ERR_HIP; }

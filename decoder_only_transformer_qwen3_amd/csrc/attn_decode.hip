@@ -8,8 +8,9 @@
 // Keys are processed in sub-chunks of up to 512: pass 1 computes scores
 // into LDS (16 lanes per key row, 16 B per lane, row sums over the 16
 // lanes with DPP), the sub-chunk's softmax statistics are merged into a
-// running (max, sum), and pass 2 accumulates p * V with the same lane
-// layout.  Each split writes unnormalised (o, m, l) in the log2 domain; the
+// running (max, sum), and pass 2 accumulates p * V over the blocked V
+// cache (8 positions x 128 dims per 2 KB block): lane l owns dims 2l and
+// 2l+1 and reads their 8 positions as two 16 B loads.  Each split writes unnormalised (o, m, l) in the log2 domain; the
 // merge kernel combines splits with the usual log-sum-exp rescaling.  The
 // key range of a split is derived from the sequence's own device length,
 // so the result is exact whatever split count the host picked.
@@ -22,16 +23,6 @@ namespace q3 {
 
 constexpr int DEC_SUB = 512;  // keys per LDS sub-chunk
 constexpr int PART_STRIDE = D + 2;
-
-// Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15); every lane of
-// the row receives the total.
-__device__ __forceinline__ float row16_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false));  // row_half_mirror
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false));  // row_mirror
-  return v;
-}
 
 __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
                                                      const uint16_t* __restrict__ v_cache, float* __restrict__ part,
@@ -65,13 +56,12 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict_
     qf1[2 * e + 1] = bf_hi(q1[e]);
   }
   const uint16_t* kb = k_cache + ((size_t)b * HKV + g) * max_seq * D + d0;
-  const uint16_t* vb = v_cache + ((size_t)b * HKV + g) * max_seq * D + d0;
+  const uint16_t* vb = v_cache + ((size_t)b * HKV + g) * max_seq * D + 2 * l * VBLK;
   const float sl2 = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
 
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-  float acc0[8], acc1[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc0[e] = acc1[e] = 0.f;
+  // acc[h][e]: head 2g+h, dim 2l+e
+  float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
 
   for (int c0 = k0; c0 < k1; c0 += DEC_SUB) {
     const int c1 = (c0 + DEC_SUB) < k1 ? (c0 + DEC_SUB) : k1;
@@ -128,52 +118,54 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict_
       const float alpha = exp2f(m_run[h] - m_new[h]);
       l_run[h] = l_run[h] * alpha + stat[h][2] + stat[h][3];
       m_run[h] = m_new[h];
-      float* acc = h ? acc1 : acc0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+      acc[h][0] *= alpha;
+      acc[h][1] *= alpha;
     }
-    // ---- pass 2: acc += p * V
-    for (int base = c0; base < c1; base += 64) {
-      u32x4 vv[4];
+    // ---- pass 2: acc += p * V, one 8-position block per wave step
+    for (int blk0 = c0 + 8 * w; blk0 < c1; blk0 += 64) {
+      u32x4 vv[2][2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        int key = base + 16 * u + 4 * w + krow;
-        key = key < c1 ? key : c1 - 1;
-        vv[u] = *reinterpret_cast<const u32x4*>(vb + (size_t)key * D);
+      for (int u = 0; u < 2; ++u) {
+        const int pb = blk0 + 32 * u;
+        if (pb < c1) {
+          const uint16_t* src = vb + (size_t)pb * D;
+          vv[u][0] = *reinterpret_cast<const u32x4*>(src);
+          vv[u][1] = *reinterpret_cast<const u32x4*>(src + VBLK);
+        }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int key = base + 16 * u + 4 * w + krow;
-        const bool ok = key < c1;
-        const float p0 = ok ? sc[0][key - c0] : 0.f;
-        const float p1 = ok ? sc[1][key - c0] : 0.f;
+      for (int u = 0; u < 2; ++u) {
+        const int pb = blk0 + 32 * u;
+        if (pb >= c1) continue;
+        const int valid = c1 - pb;  // positions beyond the range get p = 0 and a zeroed value
+        float pr[2][8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x0 = bf_lo(vv[u][e]), x1 = bf_hi(vv[u][e]);
-          acc0[2 * e] += p0 * x0;
-          acc0[2 * e + 1] += p0 * x1;
-          acc1[2 * e] += p1 * x0;
-          acc1[2 * e + 1] += p1 * x1;
+        for (int h = 0; h < 2; ++h) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&sc[h][pb - c0]);
+          const f32x4 bq = *reinterpret_cast<const f32x4*>(&sc[h][pb - c0 + 4]);
+          pr[h][0] = a.x; pr[h][1] = a.y; pr[h][2] = a.z; pr[h][3] = a.w;
+          pr[h][4] = bq.x; pr[h][5] = bq.y; pr[h][6] = bq.z; pr[h][7] = bq.w;
         }
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const uint32_t word = vv[u][e][k >> 1];
+            float x = (k & 1) ? bf_hi(word) : bf_lo(word);
+            x = k < valid ? x : 0.f;
+            acc[0][e] += (k < valid ? pr[0][k] : 0.f) * x;
+            acc[1][e] += (k < valid ? pr[1][k] : 0.f) * x;
+          }
       }
     }
     __syncthreads();  // sc is rewritten by the next sub-chunk
   }
 
-  // ---- reduce acc over the 4 key rows of a wave, then over the 4 waves
+  // ---- reduce acc over the 4 waves
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    acc0[e] += __shfl_xor(acc0[e], 16, 64);
-    acc0[e] += __shfl_xor(acc0[e], 32, 64);
-    acc1[e] += __shfl_xor(acc1[e], 16, 64);
-    acc1[e] += __shfl_xor(acc1[e], 32, 64);
-  }
-  if (l < 16) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      red[w][0][d0 + e] = acc0[e];
-      red[w][1][d0 + e] = acc1[e];
-    }
+  for (int h = 0; h < 2; ++h) {
+    red[w][h][2 * l] = acc[h][0];
+    red[w][h][2 * l + 1] = acc[h][1];
   }
   __syncthreads();
   {

@@ -30,14 +30,37 @@ __device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// float32 -> bfloat16 bits, round to nearest even; NaN stays NaN.
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// float32 -> bfloat16 (round to nearest even, NaN stays NaN); gfx950 does
+// this in hardware (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  bf16x2 r;
+  r.x = (__bf16)lo;
+  r.y = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
 }
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+
+// Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15); every lane of
+// the row receives the total.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false));  // row_half_mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false));  // row_mirror
+  return v;
+}
+
+// V cache layout: per (sequence, KV head) the positions are grouped in
+// blocks of 8; a block stores its 128 dims x 8 positions dim-major, so
+// element (p, d) sits at ((p / 8) * 128 + d) * 8 + p % 8.  Eight consecutive
+// positions of one dim are 16 contiguous bytes (an MFMA operand chunk), and
+// a block of 8 positions is 2 KB of contiguous memory.
+constexpr int VBLK = 8;
+__device__ __forceinline__ size_t vblk_index(int p, int d) {
+  return ((size_t)(p >> 3) * D + d) * VBLK + (p & 7);
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 

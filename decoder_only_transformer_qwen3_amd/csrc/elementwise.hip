@@ -77,59 +77,105 @@ void launch_rmsnorm(float* resid, const float* part, int n_part, int part_rows, 
 }
 
 // ---------------------------------------------------------------- q/k norm + RoPE + KV write
-// One wave per (token, head slot): slots 0..15 are query heads, 16..23 key
-// heads, 24..31 value heads.  Lane l holds dimensions l and l + 64, which
-// are exactly a RoPE pair in the half-swap (NeoX) form, so the rotation
-// needs no cross-lane traffic:
-//   y = x / sqrt(mean(x^2) + eps) * gamma             ("手写Qwen3-0.6B推理" §Attention, q_norm/k_norm)
-//   (y_l, y_{l+64}) -> (y_l c - y_{l+64} s, y_{l+64} c + y_l s)
-//   with c, s = cos, sin(p * 1e6^(-2l/128))           (§Rope; "古法手撕简易LLM推理器" §RoPE的细节)
-// K (normed + rotated) and raw V go to cache row p ("古法手撕简易LLM推理器"
-// §核心计算函数与Transformer层).
-__global__ __launch_bounds__(256) void k_qknorm_rope(const uint16_t* __restrict__ qkv,
-                                                     const uint16_t* __restrict__ q_norm,
-                                                     const uint16_t* __restrict__ k_norm,
-                                                     const float* __restrict__ rope_cos,
-                                                     const float* __restrict__ rope_sin, uint16_t* __restrict__ q_out,
-                                                     uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
-                                                     int B, int T, int max_seq, const int32_t* __restrict__ pos_dev,
-                                                     int start) {
+// Per-head RMSNorm of q and k with a head_dim-long gain shared by all heads
+// ("手写Qwen3-0.6B推理" §Attention, q_norm/k_norm), then NeoX RoPE at the
+// token's absolute position ("手写Qwen3-0.6B推理" §Rope; half-swap pairing
+// per "古法手撕简易LLM推理器" §RoPE的细节):
+//   y = x / sqrt(mean(x^2) + eps) * gamma
+//   (y_i, y_{i+64}) -> (y_i c - y_{i+64} s, y_{i+64} c + y_i s),  c, s = cos, sin(p * 1e6^(-2i/128)).
+// One wave handles 4 of the 24 q/k heads of one token; 16 lanes per head,
+// lane j holds dims 4j..4j+3 and 64+4j..64+4j+3, so every RoPE pair stays
+// inside the lane and the head's sum of squares is a 16-lane DPP row sum.
+// Rotated K goes to cache row p ("古法手撕简易LLM推理器"
+// §核心计算函数与Transformer层 keeps normed, rotated K in the cache).
+__global__ __launch_bounds__(256) void k_qk_norm_rope(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_norm,
+                                                      const uint16_t* __restrict__ k_norm,
+                                                      const float* __restrict__ rope_cos,
+                                                      const float* __restrict__ rope_sin, uint16_t* __restrict__ q_out,
+                                                      uint16_t* __restrict__ k_cache, int B, int T, int max_seq,
+                                                      const int32_t* __restrict__ pos_dev, int start) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + wave;
-  const int m = gw >> 5, slot = gw & 31;
+  const int m = gw / 6, hg = gw - m * 6;
   if (m >= B * T) return;
   const int b = m / T, t = m - b * T;
   const int p = (pos_dev ? pos_dev[b] : start) + t;
-  const bool in_cache = p >= 0 && p < max_seq;
-  const uint16_t* src = qkv + (size_t)m * QKV_N + slot * D;
-  const uint32_t b0 = src[lane], b1 = src[lane + 64];
-  if (slot >= HQ + HKV) {  // value head: raw copy into the cache
-    if (in_cache) {
-      uint16_t* dst = v_cache + (((size_t)b * HKV + (slot - HQ - HKV)) * max_seq + p) * D;
-      dst[lane] = (uint16_t)b0;
-      dst[lane + 64] = (uint16_t)b1;
-    }
-    return;
-  }
-  const float x0 = bf2f(b0), x1 = bf2f(b1);
-  const uint16_t* g = slot < HQ ? q_norm : k_norm;
-  const float ss = wave_sum(x0 * x0 + x1 * x1);
+  const int head = hg * 4 + (lane >> 4);  // 0..15 query heads, 16..23 key heads
+  const int j4 = 4 * (lane & 15);
+  const uint16_t* src = qkv + (size_t)m * QKV_N + head * D;
+  const u32x2 lo = *reinterpret_cast<const u32x2*>(src + j4);
+  const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 64 + j4);
+  float x[4] = {bf_lo(lo.x), bf_hi(lo.x), bf_lo(lo.y), bf_hi(lo.y)};
+  float y[4] = {bf_lo(hi.x), bf_hi(hi.x), bf_lo(hi.y), bf_hi(hi.y)};
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ss += x[i] * x[i] + y[i] * y[i];
+  ss = row16_sum(ss);
   const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + EPS);
-  const float y0 = x0 * rinv * bf2f(g[lane]);
-  const float y1 = x1 * rinv * bf2f(g[lane + 64]);
+  const uint16_t* gm = head < HQ ? q_norm : k_norm;
+  const u32x2 g0 = *reinterpret_cast<const u32x2*>(gm + j4);
+  const u32x2 g1 = *reinterpret_cast<const u32x2*>(gm + 64 + j4);
+  const float ga[4] = {bf_lo(g0.x), bf_hi(g0.x), bf_lo(g0.y), bf_hi(g0.y)};
+  const float gb[4] = {bf_lo(g1.x), bf_hi(g1.x), bf_lo(g1.y), bf_hi(g1.y)};
   const int pc = p < 0 ? 0 : (p >= MAXPOS ? MAXPOS - 1 : p);
-  const float c = rope_cos[(size_t)pc * ROPE_HALF + lane];
-  const float sn = rope_sin[(size_t)pc * ROPE_HALF + lane];
-  const uint16_t o0 = (uint16_t)f2bf(y0 * c - y1 * sn);
-  const uint16_t o1 = (uint16_t)f2bf(y1 * c + y0 * sn);
-  if (slot < HQ) {
-    uint16_t* dst = q_out + (size_t)m * QDIM + slot * D;
-    dst[lane] = o0;
-    dst[lane + 64] = o1;
-  } else if (in_cache) {
-    uint16_t* dst = k_cache + (((size_t)b * HKV + (slot - HQ)) * max_seq + p) * D;
-    dst[lane] = o0;
-    dst[lane + 64] = o1;
+  const f32x4 c = *reinterpret_cast<const f32x4*>(rope_cos + (size_t)pc * ROPE_HALF + j4);
+  const f32x4 sn = *reinterpret_cast<const f32x4*>(rope_sin + (size_t)pc * ROPE_HALF + j4);
+  float o0[4], o1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = x[i] * rinv * ga[i], bb = y[i] * rinv * gb[i];
+    o0[i] = a * c[i] - bb * sn[i];
+    o1[i] = bb * c[i] + a * sn[i];
+  }
+  const u32x2 w0 = {pack_bf2(o0[0], o0[1]), pack_bf2(o0[2], o0[3])};
+  const u32x2 w1 = {pack_bf2(o1[0], o1[1]), pack_bf2(o1[2], o1[3])};
+  uint16_t* dst;
+  if (head < HQ) {
+    dst = q_out + (size_t)m * QDIM + head * D;
+  } else {
+    if (p < 0 || p >= max_seq) return;
+    dst = k_cache + (((size_t)b * HKV + (head - HQ)) * max_seq + p) * D;
+  }
+  *reinterpret_cast<u32x2*>(dst + j4) = w0;
+  *reinterpret_cast<u32x2*>(dst + 64 + j4) = w1;
+}
+
+// Raw V of the new tokens into the blocked V cache (8 positions x 128 dims
+// per 2 KB block).  One workgroup per (8-position block, KV head,
+// sequence): the block's tokens are staged in LDS and written back as
+// position-contiguous 8-byte groups; positions outside the call's range are
+// left untouched (they may hold earlier tokens).
+__global__ __launch_bounds__(256) void k_v_store(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ v_cache, int B,
+                                                 int T, int max_seq, const int32_t* __restrict__ pos_dev, int start) {
+  __shared__ uint16_t tile[VBLK][D];
+  const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int p_first = (pos_dev ? pos_dev[b] : start);
+  const int pb = (p_first >> 3) + blockIdx.x;  // position block
+  const int p_lo = p_first > pb * VBLK ? p_first : pb * VBLK;
+  const int p_hi = (p_first + T) < (pb + 1) * VBLK ? (p_first + T) : (pb + 1) * VBLK;
+  if (p_first < 0 || p_lo >= p_hi || pb * VBLK >= max_seq) return;
+  {
+    const int tt = tid >> 5, d4 = 4 * (tid & 31);
+    const int p = pb * VBLK + tt;
+    u32x2 v = {0u, 0u};
+    if (p >= p_lo && p < p_hi) {
+      const size_t m = (size_t)b * T + (p - p_first);
+      v = *reinterpret_cast<const u32x2*>(qkv + m * QKV_N + (HQ + HKV) * D + g * D + d4);
+    }
+    *reinterpret_cast<u32x2*>(&tile[tt][d4]) = v;
+  }
+  __syncthreads();
+  const int d = tid >> 1, h4 = 4 * (tid & 1);
+  uint16_t* dst = v_cache + ((size_t)b * HKV + g) * max_seq * D + ((size_t)pb * D + d) * VBLK + h4;
+  const int q0 = pb * VBLK + h4;
+  if (q0 >= p_lo && q0 + 4 <= p_hi) {
+    const u32x2 w = {(uint32_t)tile[h4][d] | ((uint32_t)tile[h4 + 1][d] << 16),
+                     (uint32_t)tile[h4 + 2][d] | ((uint32_t)tile[h4 + 3][d] << 16)};
+    *reinterpret_cast<u32x2*>(dst) = w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (q0 + i >= p_lo && q0 + i < p_hi) dst[i] = tile[h4 + i][d];
   }
 }
 
@@ -137,9 +183,12 @@ void launch_qknorm_rope(const uint16_t* qkv, const uint16_t* q_norm, const uint1
                         const float* rope_cos, const float* rope_sin, uint16_t* q_out, uint16_t* k_cache,
                         uint16_t* v_cache, int B, int T, int max_seq, const int32_t* pos_dev, int start,
                         hipStream_t s) {
-  const int waves = B * T * 32;
-  hipLaunchKernelGGL(k_qknorm_rope, dim3((waves + 3) / 4), dim3(256), 0, s, qkv, q_norm, k_norm, rope_cos,
-                     rope_sin, q_out, k_cache, v_cache, B, T, max_seq, pos_dev, start);
+  const int waves = B * T * 6;
+  hipLaunchKernelGGL(k_qk_norm_rope, dim3((waves + 3) / 4), dim3(256), 0, s, qkv, q_norm, k_norm, rope_cos, rope_sin,
+                     q_out, k_cache, B, T, max_seq, pos_dev, start);
+  // an unaligned run of T positions touches at most T/8 + 2 blocks
+  const int nblk = T / VBLK + 2;
+  hipLaunchKernelGGL(k_v_store, dim3(nblk, HKV, B), dim3(256), 0, s, qkv, v_cache, B, T, max_seq, pos_dev, start);
 }
 
 // ---------------------------------------------------------------- argmax
@@ -152,22 +201,7 @@ __device__ __forceinline__ bool am_better(float a, int ia, float b, int ib) {
   return a > b || (a == b && ia < ib);
 }
 
-__global__ __launch_bounds__(1024) void k_argmax(const float* __restrict__ logits, int vocab, int64_t stride,
-                                                 int32_t* __restrict__ out_idx, int32_t* __restrict__ seq_lens,
-                                                 int seq_mode, int seq_val) {
-  __shared__ float sv[16];
-  __shared__ int si[16];
-  const int r = blockIdx.x;
-  const float* row = logits + (size_t)r * stride;
-  float best = -INFINITY;
-  int bi = 0x7fffffff;
-  for (int i = threadIdx.x; i < vocab; i += 1024) {
-    const float v = row[i];
-    if (am_better(v, i, best, bi)) {
-      best = v;
-      bi = i;
-    }
-  }
+__device__ __forceinline__ void am_wave_block_reduce(float& best, int& bi, float* sv, int* si) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const float ov = __shfl_xor(best, o, 64);
@@ -184,23 +218,117 @@ __global__ __launch_bounds__(1024) void k_argmax(const float* __restrict__ logit
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    float b = sv[0];
-    int i = si[0];
-    for (int w = 1; w < 16; ++w)
-      if (am_better(sv[w], si[w], b, i)) {
-        b = sv[w];
-        i = si[w];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w)
+      if (am_better(sv[w], si[w], best, bi)) {
+        best = sv[w];
+        bi = si[w];
       }
-    out_idx[r] = i;
-    if (seq_mode == 1) seq_lens[r] = seq_val;
-    if (seq_mode == 2) seq_lens[r] += 1;
   }
+}
+
+__device__ __forceinline__ void am_finish(int r, int bi, int32_t* out_idx, int32_t* seq_lens, int seq_mode,
+                                          int seq_val) {
+  out_idx[r] = bi;
+  if (seq_mode == 1) seq_lens[r] = seq_val;
+  if (seq_mode == 2) seq_lens[r] += 1;
+}
+
+// One block of 1024 threads per row; 16 B loads when the row is 16-byte
+// aligned, 8 loads in flight per thread.
+__global__ __launch_bounds__(1024) void k_argmax(const float* __restrict__ logits, int vocab, int64_t stride,
+                                                 int32_t* __restrict__ out_idx, int32_t* __restrict__ seq_lens,
+                                                 int seq_mode, int seq_val) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const float* row = logits + (size_t)r * stride;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  int i0 = 0;
+  if ((reinterpret_cast<uintptr_t>(row) & 15) == 0) {
+    const int nvec = vocab >> 2;
+    const f32x4* rv = reinterpret_cast<const f32x4*>(row);
+    for (int base = 0; base < nvec; base += 1024 * 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * 1024 + tid;
+        v[u] = i < nvec ? rv[i] : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * 1024 + tid;
+        if (i < nvec)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (am_better(v[u][e], 4 * i + e, best, bi)) {
+              best = v[u][e];
+              bi = 4 * i + e;
+            }
+      }
+    }
+    i0 = nvec << 2;
+  }
+  for (int base = i0; base < vocab; base += 1024 * 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * 1024 + tid;
+      v[u] = i < vocab ? row[i] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * 1024 + tid;
+      if (i < vocab && am_better(v[u], i, best, bi)) {
+        best = v[u];
+        bi = i;
+      }
+    }
+  }
+  am_wave_block_reduce(best, bi, sv, si);
+  if (tid == 0) am_finish(r, bi, out_idx, seq_lens, seq_mode, seq_val);
 }
 
 void launch_argmax(const float* logits, int rows, int vocab, int64_t row_stride, int32_t* out_idx,
                    int32_t* seq_lens, int seq_mode, int seq_val, hipStream_t s) {
   hipLaunchKernelGGL(k_argmax, dim3(rows), dim3(1024), 0, s, logits, vocab, row_stride, out_idx, seq_lens, seq_mode,
                      seq_val);
+}
+
+// Reduce the lm_head's per-block (value, index) candidates of one row.
+__global__ __launch_bounds__(1024) void k_argmax_partials(const float2* __restrict__ part, int n_part,
+                                                          int32_t* __restrict__ out_idx,
+                                                          int32_t* __restrict__ seq_lens, int seq_mode, int seq_val) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const float2* row = part + (size_t)r * n_part;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int base = 0; base < n_part; base += 1024 * 4) {
+    float2 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = base + u * 1024 + tid;
+      v[u] = i < n_part ? row[i] : make_float2(-INFINITY, __int_as_float(0x7fffffff));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = __float_as_int(v[u].y);
+      if (am_better(v[u].x, idx, best, bi)) {
+        best = v[u].x;
+        bi = idx;
+      }
+    }
+  }
+  am_wave_block_reduce(best, bi, sv, si);
+  if (tid == 0) am_finish(r, bi, out_idx, seq_lens, seq_mode, seq_val);
+}
+
+void launch_argmax_partials(const void* part, int rows, int n_part, int32_t* out_idx, int32_t* seq_lens,
+                            int seq_mode, int seq_val, hipStream_t s) {
+  hipLaunchKernelGGL(k_argmax_partials, dim3(rows), dim3(1024), 0, s, static_cast<const float2*>(part), n_part,
+                     out_idx, seq_lens, seq_mode, seq_val);
 }
 
 }  // namespace q3

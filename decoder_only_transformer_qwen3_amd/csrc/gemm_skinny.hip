@@ -21,10 +21,16 @@
 
 namespace q3 {
 
+__device__ __forceinline__ bool am_better2(float a, int ia, float b, int ib) {
+  const bool an = a != a, bn = b != b;
+  if (an || bn) return an && (!bn || ia < ib);
+  return a > b || (a == b && ia < ib);
+}
+
 template <int NB, int EPI, int U>
 __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                                                      void* __restrict__ out, int M, int N, int K, int ldo,
-                                                     int kspan) {
+                                                     int kspan, void* __restrict__ amax_part) {
   __shared__ float red[4][NB * 16][17];
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, qd = l >> 4;
   const int rb = blockIdx.x, split = blockIdx.y;
@@ -85,7 +91,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
   } else {
     if (t < NB * 16 * 4) {
       const int m = t >> 2, ng = t & 3;
-      if (m < M) {
+      if (m < M) {  // whole groups of 4 lanes share m, so the shuffles below stay inside active groups
         f32x4 v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = red[0][m][4 * ng + i] + red[1][m][4 * ng + i] + red[2][m][4 * ng + i] + red[3][m][4 * ng + i];
@@ -97,6 +103,30 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
           *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + (size_t)m * ldo + n) = o;
         } else if constexpr (EPI == EPI_F32) {
           *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)m * ldo + n) = v;
+        } else if constexpr (EPI == EPI_LOGITS) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)m * ldo + n) = v;
+          // this block's greedy candidate for row m: lowest index among equal maxima, NaN first
+          float bv = v[0];
+          int bi = n;
+#pragma unroll
+          for (int i = 1; i < 4; ++i)
+            if (am_better2(v[i], n + i, bv, bi)) {
+              bv = v[i];
+              bi = n + i;
+            }
+#pragma unroll
+          for (int o = 1; o <= 2; o <<= 1) {
+            const float ov = __shfl_xor(bv, o, 64);
+            const int oi = __shfl_xor(bi, o, 64);
+            if (am_better2(ov, oi, bv, bi)) {
+              bv = ov;
+              bi = oi;
+            }
+          }
+          if (ng == 0) {
+            float2* ap = reinterpret_cast<float2*>(amax_part) + (size_t)m * gridDim.x + rb;
+            *ap = make_float2(bv, __int_as_float(bi));
+          }
         } else if constexpr (EPI == EPI_ADD_F32) {
           f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)m * ldo + n);
           *dst = *dst + v;
@@ -110,32 +140,35 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
 
 template <int NB, int EPI>
 static void launch_nb(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo, int n_split,
-                      hipStream_t s) {
+                      hipStream_t s, void* amax_part) {
   const int kspan = K / n_split;
   const int rows_per_block = 16;
   const int gx = (EPI == EPI_SILU) ? (N / 2) / 8 : N / rows_per_block;
   // Each wave takes kspan/128 steps; unroll by 8 when that divides evenly.
   if (((kspan >> 5) % 32) == 0)
-    hipLaunchKernelGGL((k_gemm_skinny<NB, EPI, 8>), dim3(gx, n_split), dim3(256), 0, s, X, W, out, M, N, K, ldo, kspan);
+    hipLaunchKernelGGL((k_gemm_skinny<NB, EPI, 8>), dim3(gx, n_split), dim3(256), 0, s, X, W, out, M, N, K, ldo, kspan,
+                       amax_part);
   else
-    hipLaunchKernelGGL((k_gemm_skinny<NB, EPI, 4>), dim3(gx, n_split), dim3(256), 0, s, X, W, out, M, N, K, ldo, kspan);
+    hipLaunchKernelGGL((k_gemm_skinny<NB, EPI, 4>), dim3(gx, n_split), dim3(256), 0, s, X, W, out, M, N, K, ldo, kspan,
+                       amax_part);
 }
 
 template <int EPI>
 static void launch_epi(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo, int n_split,
-                       hipStream_t s) {
+                       hipStream_t s, void* amax_part = nullptr) {
   const int nb = (M + 15) / 16;
   switch (nb) {
-    case 1: launch_nb<1, EPI>(X, W, out, M, N, K, ldo, n_split, s); break;
-    case 2: launch_nb<2, EPI>(X, W, out, M, N, K, ldo, n_split, s); break;
-    case 3: launch_nb<3, EPI>(X, W, out, M, N, K, ldo, n_split, s); break;
-    default: launch_nb<4, EPI>(X, W, out, M, N, K, ldo, n_split, s); break;
+    case 1: launch_nb<1, EPI>(X, W, out, M, N, K, ldo, n_split, s, amax_part); break;
+    case 2: launch_nb<2, EPI>(X, W, out, M, N, K, ldo, n_split, s, amax_part); break;
+    case 3: launch_nb<3, EPI>(X, W, out, M, N, K, ldo, n_split, s, amax_part); break;
+    default: launch_nb<4, EPI>(X, W, out, M, N, K, ldo, n_split, s, amax_part); break;
   }
 }
 
 void launch_gemm_skinny(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo, int n_split,
-                        Epi epi, hipStream_t s) {
+                        Epi epi, hipStream_t s, void* amax_part) {
   switch (epi) {
+    case EPI_LOGITS: launch_epi<EPI_LOGITS>(X, W, out, M, N, K, ldo, n_split, s, amax_part); break;
     case EPI_BF16: launch_epi<EPI_BF16>(X, W, out, M, N, K, ldo, n_split, s); break;
     case EPI_F32: launch_epi<EPI_F32>(X, W, out, M, N, K, ldo, n_split, s); break;
     case EPI_ADD_F32: launch_epi<EPI_ADD_F32>(X, W, out, M, N, K, ldo, n_split, s); break;

@@ -14,6 +14,7 @@ enum Epi : int {
   EPI_ADD_F32 = 2,  // out f32 [M, ldo] += result (residual add)
   EPI_SILU = 3,     // W rows are [gate; up]; out bf16 [M, ldo] = silu(gate) * up
   EPI_PARTIAL = 4,  // out f32 [split][M][N] partial sums over a K range
+  EPI_LOGITS = 5,   // out f32 [M, ldo] and, per 16-column block, the block's (max, argmax) per row
 };
 
 // x[m] = E[ids[m]] widened to f32 (one row of 1024 per token).
@@ -41,7 +42,7 @@ void launch_gemm_tiled(const uint16_t* X, const uint16_t* W, void* out, int M, i
 // MFMA skinny GEMM for M <= 64 rows (weight streaming), split into n_split K ranges.
 // Requires N % 16 == 0 and (K / n_split) % 512 == 0; EPI_PARTIAL writes [n_split][M][N].
 void launch_gemm_skinny(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo,
-                        int n_split, Epi epi, hipStream_t s);
+                        int n_split, Epi epi, hipStream_t s, void* amax_part = nullptr);
 
 // Causal GQA flash attention over the cache for B x T queries at positions start..start+T-1.
 void launch_attn_prefill(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out,
@@ -51,6 +52,11 @@ void launch_attn_prefill(const uint16_t* q, const uint16_t* k_cache, const uint1
 void launch_attn_decode(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, float* part,
                         uint16_t* out, int B, int max_seq, const int32_t* pos_dev, int start, int n_split,
                         hipStream_t s);
+
+// Final greedy choice from the lm_head's per-block (max, argmax) partials:
+// part is [rows][n_part] of (float value, int index).  seq_mode as below.
+void launch_argmax_partials(const void* part, int rows, int n_part, int32_t* out_idx, int32_t* seq_lens,
+                            int seq_mode, int seq_val, hipStream_t s);
 
 // Row argmax (lowest index on ties, first NaN wins).  seq_mode: 0 none,
 // 1 seq_lens[r] = seq_val, 2 seq_lens[r] += 1 (done after the argmax).

@@ -28,6 +28,7 @@ WsLayout ws_layout(int32_t batch, int32_t n_tokens) {
   L.part = take(M <= (size_t)SKINNY_MAX_ROWS ? (size_t)PART_MAX_SPLIT * M * Q3_HIDDEN * 4 : 0);
   L.apart = take(n_tokens == 1 ? (size_t)batch * Q3_N_HEADS * DEC_SPLIT_MAX * (Q3_HEAD_DIM + 2) * 4 : 0);
   L.logits = take((size_t)batch * Q3_VOCAB * 4);
+  L.amax = take((size_t)batch * (Q3_VOCAB / 16) * 8);
   L.fh = take((size_t)batch * Q3_HIDDEN * 2);
   L.total = off;
   return L;
@@ -70,7 +71,7 @@ int check_layer_call(const q3_layer_weights* w, const float* rope_cos, const flo
                      const float* residual, const void* ws, size_t ws_bytes) {
   if (!w || !rope_cos || !rope_sin || !k_layer || !v_layer || !residual || !ws) return Q3_ERR_NULL;
   if (layer_ptrs_null(w)) return Q3_ERR_NULL;
-  if (batch < 1 || n_tokens < 1 || max_seq < 1 || max_seq > Q3_MAX_POS) return Q3_ERR_SHAPE;
+  if (batch < 1 || n_tokens < 1 || max_seq < 8 || max_seq > Q3_MAX_POS || (max_seq % 8) != 0) return Q3_ERR_SHAPE;
   if ((int64_t)batch * n_tokens > MAX_TOKENS) return Q3_ERR_SHAPE;
   if (start_pos < 0 || (int64_t)start_pos + n_tokens > max_seq) return Q3_ERR_POSITION;
   if (layer_ptrs_misaligned(w) || !al16(rope_cos) || !al16(rope_sin) || !al16(k_layer) || !al16(v_layer) ||
@@ -85,7 +86,7 @@ int check_prefill_call(const q3_model* m, const q3_kv* kv, int32_t batch, int32_
                        size_t ws_bytes) {
   if (!m || !kv || !ids || !next_ids || !seq_lens || !ws) return Q3_ERR_NULL;
   if (model_null(m) || !kv->k || !kv->v) return Q3_ERR_NULL;
-  if (kv->batch < 1 || kv->max_seq < 1 || kv->max_seq > Q3_MAX_POS) return Q3_ERR_SHAPE;
+  if (kv->batch < 1 || kv->max_seq < 8 || kv->max_seq > Q3_MAX_POS || (kv->max_seq % 8) != 0) return Q3_ERR_SHAPE;
   if (batch < 1 || batch > kv->batch || prompt_len < 1) return Q3_ERR_SHAPE;
   if ((int64_t)batch * prompt_len > MAX_TOKENS) return Q3_ERR_SHAPE;
   if (prompt_len > kv->max_seq) return Q3_ERR_POSITION;
@@ -101,7 +102,7 @@ int check_decode_call(const q3_model* m, const q3_kv* kv, int32_t batch, const i
                       const void* ws, size_t ws_bytes) {
   if (!m || !kv || !in_ids || !seq_lens || !out_ids || !ws) return Q3_ERR_NULL;
   if (model_null(m) || !kv->k || !kv->v) return Q3_ERR_NULL;
-  if (kv->batch < 1 || kv->max_seq < 1 || kv->max_seq > Q3_MAX_POS) return Q3_ERR_SHAPE;
+  if (kv->batch < 1 || kv->max_seq < 8 || kv->max_seq > Q3_MAX_POS || (kv->max_seq % 8) != 0) return Q3_ERR_SHAPE;
   if (batch < 1 || batch > kv->batch) return Q3_ERR_SHAPE;
   if (max_len_hint < 1 || max_len_hint > kv->max_seq) return Q3_ERR_POSITION;
   if (model_misaligned(m) || !al16(kv->k) || !al16(kv->v) || !al4(in_ids) || !al4(seq_lens) || !al4(out_ids) ||

@@ -95,14 +95,18 @@ typedef struct {
 } q3_model;
 
 /* KV cache: K after q/k-norm and RoPE, raw V ("古法手撕简易LLM推理器"
- * §核心计算函数与Transformer层), each bf16
- * [28][batch][8][max_seq][128] contiguous.  Row p of a sequence holds
- * position p. */
+ * §核心计算函数与Transformer层), bf16, one region of
+ * max_seq * 128 elements per (layer, sequence, KV head), regions ordered
+ * [28][batch][8]:
+ *   K region: position-major, element (p, d) at p * 128 + d;
+ *   V region: blocks of 8 positions, dim-major inside a block, element
+ *             (p, d) at ((p / 8) * 128 + d) * 8 + p % 8.
+ * Both are caller-allocated, 28 * batch * 8 * max_seq * 128 * 2 bytes each. */
 typedef struct {
   void *k;
   void *v;
   int32_t batch;
-  int32_t max_seq;        /* 1 .. 40960 */
+  int32_t max_seq;        /* multiple of 8, 8 .. 40960 */
 } q3_kv;
 
 /* Human-readable text for a status code (static storage). */
@@ -132,14 +136,15 @@ size_t q3_workspace_bytes(int32_t batch, int32_t n_tokens);
  * 1/sqrt(128); MLP per §MLP).
  *   w           layer weights (device pointers inside a HOST struct)
  *   rope_cos/sin  [40960, 64] float32 device tables
- *   k_layer, v_layer  this layer's cache, bf16 [batch][8][max_seq][128];
- *               rows start_pos .. start_pos+n_tokens-1 are written, rows
- *               0 .. start_pos-1 must already hold the earlier positions.
+ *   k_layer, v_layer  this layer's cache regions for `batch` sequences in
+ *               the q3_kv layouts (max_seq a multiple of 8); positions
+ *               start_pos .. start_pos+n_tokens-1 are written, positions
+ *               0 .. start_pos-1 must already hold the earlier tokens.
  *   residual    in/out float32 [batch * n_tokens, 1024], row b*n_tokens+t.
  *   ws          device workspace of at least
  *               q3_workspace_bytes(batch, n_tokens) bytes.
  * Errors: Q3_ERR_NULL, Q3_ERR_SHAPE (batch < 1, n_tokens < 1,
- * max_seq < 1 or > 40960), Q3_ERR_POSITION (start_pos < 0 or
+ * max_seq not a multiple of 8 in 8 .. 40960), Q3_ERR_POSITION (start_pos < 0 or
  * start_pos + n_tokens > max_seq), Q3_ERR_ALIGN, Q3_ERR_WORKSPACE,
  * Q3_ERR_HIP. */
 int q3_layer_forward(const q3_layer_weights *w, const float *rope_cos, const float *rope_sin,
@@ -159,7 +164,7 @@ int q3_layer_forward(const q3_layer_weights *w, const float *rope_cos, const flo
  *               index among equal maxima).
  *   seq_lens    int32 [batch]: set to prompt_len.
  * Errors: Q3_ERR_NULL, Q3_ERR_SHAPE (batch < 1 or > kv->batch,
- * prompt_len < 1), Q3_ERR_POSITION (prompt_len > kv->max_seq),
+ * prompt_len < 1, kv->max_seq invalid), Q3_ERR_POSITION (prompt_len > kv->max_seq),
  * Q3_ERR_ALIGN, Q3_ERR_WORKSPACE (q3_workspace_bytes(batch, prompt_len)),
  * Q3_ERR_HIP. */
 int q3_prefill(const q3_model *m, const q3_kv *kv, int32_t batch, int32_t prompt_len,
@@ -181,8 +186,8 @@ int q3_prefill(const q3_model *m, const q3_kv *kv, int32_t batch, int32_t prompt
  *               error: its cache write is skipped and its outputs are
  *               unspecified (no out-of-bounds access).
  *   logits      float32 [batch, 151936], or NULL.
- * Errors: Q3_ERR_NULL, Q3_ERR_SHAPE (batch < 1 or > kv->batch),
- * Q3_ERR_POSITION (max_len_hint out of range), Q3_ERR_ALIGN,
+ * Errors: Q3_ERR_NULL, Q3_ERR_SHAPE (batch < 1 or > kv->batch,
+ * kv->max_seq invalid), Q3_ERR_POSITION (max_len_hint out of range), Q3_ERR_ALIGN,
  * Q3_ERR_WORKSPACE (q3_workspace_bytes(batch, 1)), Q3_ERR_HIP. */
 int q3_decode_step(const q3_model *m, const q3_kv *kv, int32_t batch, const int32_t *in_ids,
                    int32_t *seq_lens, int32_t max_len_hint, float *logits, int32_t *out_ids,

@@ -26,6 +26,19 @@ def bf16_tensor_to_f64(t) -> np.ndarray:
     return O.widen_bf16(t.detach().view(torch.int16).cpu().numpy().view(np.uint16))
 
 
+def v_blocked_to_dense(v: np.ndarray) -> np.ndarray:
+    """[..., S, D] array read from the blocked V cache (blocks of 8 positions,
+    dim-major inside a block) -> position-major [..., S, D]."""
+    *lead, S, Dd = v.shape
+    return v.reshape(*lead, S // 8, Dd, 8).swapaxes(-1, -2).reshape(*lead, S, Dd)
+
+
+def v_dense_to_blocked(v: np.ndarray) -> np.ndarray:
+    """Inverse of v_blocked_to_dense (the array keeps its [..., S, D] shape)."""
+    *lead, S, Dd = v.shape
+    return np.ascontiguousarray(v.reshape(*lead, S // 8, 8, Dd).swapaxes(-1, -2)).reshape(*lead, S, Dd)
+
+
 def cache_fill_bits(seed: int, shape) -> np.ndarray:
     """Synthetic earlier-position cache content: N(0, 1) bf16 bits."""
     return I.normal_bf16(seed, "cache_fill", shape, std=1.0)

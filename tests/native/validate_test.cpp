@@ -71,6 +71,8 @@ int main() {
   EXPECT_EQ(check_layer_call(&w, cs, cs, kl, vl, 0, 16, 64, 0, res, ws, need), Q3_ERR_SHAPE);
   EXPECT_EQ(check_layer_call(&w, cs, cs, kl, vl, 2, 0, 64, 0, res, ws, need), Q3_ERR_SHAPE);
   EXPECT_EQ(check_layer_call(&w, cs, cs, kl, vl, 2, 16, 40961, 0, res, ws, need), Q3_ERR_SHAPE);
+  EXPECT_EQ(check_layer_call(&w, cs, cs, kl, vl, 2, 16, 60, 0, res, ws, need), Q3_ERR_SHAPE);  // not a multiple of 8
+  EXPECT_EQ(check_layer_call(&w, cs, cs, kl, vl, 2, 16, 4, 0, res, ws, need), Q3_ERR_SHAPE);
   EXPECT_EQ(check_layer_call(&w, cs, cs, kl, vl, 2, 16, 64, 49, res, ws, need), Q3_ERR_POSITION);
   EXPECT_EQ(check_layer_call(&w, cs, cs, kl, vl, 2, 16, 64, 48, res, ws, need), Q3_OK);
   EXPECT_EQ(check_layer_call(&w, cs, cs, kl, vl, 2, 16, 64, -1, res, ws, need), Q3_ERR_POSITION);
@@ -97,6 +99,8 @@ int main() {
   EXPECT_EQ(check_prefill_call(&m, &kv, 4, 128, ids, nullptr, nid, sl, ws, pneed - 256), Q3_ERR_WORKSPACE);
   q3_model mn = m; mn.layer[27].w_o = nullptr;
   EXPECT_EQ(check_prefill_call(&mn, &kv, 4, 128, ids, nullptr, nid, sl, ws, pneed), Q3_ERR_NULL);
+  q3_kv kc = kv; kc.max_seq = 250;
+  EXPECT_EQ(check_prefill_call(&m, &kc, 4, 128, ids, nullptr, nid, sl, ws, pneed), Q3_ERR_SHAPE);
   q3_kv kb = kv; kb.max_seq = 40961;
   EXPECT_EQ(check_prefill_call(&m, &kb, 4, 128, ids, nullptr, nid, sl, ws, pneed), Q3_ERR_SHAPE);
 

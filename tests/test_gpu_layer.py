@@ -14,7 +14,8 @@ import pytest
 import oracle as O
 from decoder_only_transformer_qwen3_amd import inputs as I
 
-from gpu_common import REL_TOL, bf16_tensor_to_f64, cache_fill_bits, log, rel_err
+from gpu_common import (REL_TOL, bf16_tensor_to_f64, cache_fill_bits, log, rel_err, v_blocked_to_dense,
+                        v_dense_to_blocked)
 
 pytestmark = pytest.mark.gpu
 
@@ -54,13 +55,13 @@ def run_layer_case(lib, layer0, rope, batch, T, start, max_seq, check_seqs=None,
         kc_bits[:, :, :start] = cache_fill_bits(seed + 1, (batch, B.N_KV_HEADS, start, B.HEAD_DIM))
         vc_bits[:, :, :start] = cache_fill_bits(seed + 2, (batch, B.N_KV_HEADS, start, B.HEAD_DIM))
     kc = dev.to_device_bf16(kc_bits)
-    vc = dev.to_device_bf16(vc_bits)
+    vc = dev.to_device_bf16(v_dense_to_blocked(vc_bits))
     resid = torch.from_numpy(O.widen_bf16(x_bits).astype(np.float32)).cuda().reshape(batch * T, B.HIDDEN)
     ws, nbytes = dev.workspace(batch, T)
     B.q3_layer_forward(dl.struct(), rope[0], rope[1], kc, vc, batch, T, max_seq, start, resid, ws, nbytes)
     torch.cuda.synchronize()
     got = resid.cpu().numpy().astype(np.float64).reshape(batch, T, B.HIDDEN)
-    kg, vg = bf16_tensor_to_f64(kc), bf16_tensor_to_f64(vc)
+    kg, vg = bf16_tensor_to_f64(kc), v_blocked_to_dense(bf16_tensor_to_f64(vc))
     assert np.all(np.isfinite(got))
 
     seqs = range(batch) if check_seqs is None else check_seqs
@@ -75,7 +76,9 @@ def run_layer_case(lib, layer0, rope, batch, T, start, max_seq, check_seqs=None,
         ev = rel_err(vg[b, :, start:start + T], vo[0, :, start:start + T])
         # earlier rows and rows past the new ones are untouched
         np.testing.assert_array_equal(kg[b, :, :start], ko[0, :, :start])
+        np.testing.assert_array_equal(vg[b, :, :start], vo[0, :, :start])
         np.testing.assert_array_equal(kg[b, :, start + T:], 0.0)
+        np.testing.assert_array_equal(vg[b, :, start + T:], 0.0)
         log(f"   seq {b}: residual rel={e:.3e} K rel={ek:.3e} V rel={ev:.3e}")
         assert e <= REL_TOL and ek <= REL_TOL and ev <= REL_TOL
         worst = max(worst, e)
@@ -91,7 +94,9 @@ def run_layer_case(lib, layer0, rope, batch, T, start, max_seq, check_seqs=None,
     (3, 1, 700, 1024),    # decode-shaped, host start position
     (1, 1, 0, 8),         # single key
     (2, 1, 4095, 4096),   # decode into the last cache row
-    (5, 3, 10, 13),       # tiny chunk, several sequences, cache full afterwards
+    (5, 3, 13, 16),       # tiny chunk, several sequences, cache full afterwards
+    (2, 11, 53, 72),      # unaligned chunk spanning three 8-position V blocks
+    (1, 200, 0, 200),     # 128-position query tiles with a ragged last tile
 ])
 def test_layer_forward_parity(lib, layer0, rope, batch, T, start, max_seq):
     run_layer_case(lib, layer0, rope, batch, T, start, max_seq)

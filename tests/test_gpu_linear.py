@@ -35,7 +35,7 @@ SHAPES = [  # (name, n, k)
 ]
 
 
-@pytest.mark.parametrize("m", [1, 7, 16, 33, 64, 65, 200])
+@pytest.mark.parametrize("m", [1, 7, 16, 33, 64, 65, 200, 2048, 2100])
 @pytest.mark.parametrize("name,n,k", SHAPES)
 def test_linear_all_epilogues(lib, m, name, n, k):
     B, dev = lib
@@ -98,7 +98,7 @@ def test_decode_graph_replay_matches_eager(lib):
     dm = dev.DeviceModel(bits)
     T, steps, batch = 32, 4, 3
     ids = torch.from_numpy(I.token_ids(6, (batch, T))).cuda()
-    kv = dev.DeviceKV(batch, T + steps)
+    kv = dev.DeviceKV(batch, (T + steps + 7) // 8 * 8)
     ws, nb = dev.workspace(batch, T)
     wsd, nbd = dev.workspace(batch, 1)
     nxt = torch.zeros(batch, dtype=torch.int32, device="cuda")

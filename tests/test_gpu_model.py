@@ -142,7 +142,7 @@ def test_prefill_tiled_path_parity(lib, models):
     B, dev = lib
     dm, om = models
     ids = I.token_ids(5, (2, 300))
-    kv = dev.DeviceKV(2, 300)
+    kv = dev.DeviceKV(2, 304)
     ws, nb = dev.workspace(2, 300)
     logits = torch.empty((2, B.VOCAB), dtype=torch.float32, device="cuda")
     nxt = torch.empty(2, dtype=torch.int32, device="cuda")
