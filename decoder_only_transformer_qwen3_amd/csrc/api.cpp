@@ -24,7 +24,9 @@ constexpr int SPLIT_DOWN = 6;
 struct Ws {
   float* resid;
   uint16_t *h, *qkv, *qr, *ao, *act, *fh;
-  float *part, *apart, *logits;
+  float *part, *apart, *logits, *ssq;
+  int* tick;  // 64 column-block tickets, then batch * 8 attention tickets
+  int n_tick;
   void* amax;
 };
 
@@ -43,6 +45,9 @@ Ws carve(void* base, int32_t batch, int32_t n_tokens) {
   w.logits = reinterpret_cast<float*>(p + L.logits);
   w.amax = p + L.amax;
   w.fh = reinterpret_cast<uint16_t*>(p + L.fh);
+  w.ssq = reinterpret_cast<float*>(p + L.ssq);
+  w.tick = reinterpret_cast<int*>(p + L.tick);
+  w.n_tick = q3v::ticket_count(batch);
   return w;
 }
 
@@ -54,68 +59,125 @@ struct LayerCtx {
   const int32_t* pos_dev;  // per-sequence start positions on the device (decode), or null
   int dec_splits;          // decode-attention splits (T == 1 only)
   float* resid;
+  const uint16_t* gamma_next;  // gain of the norm that follows this layer, or null
   Ws ws;
   hipStream_t s;
 };
 
 inline const uint16_t* U(const void* p) { return static_cast<const uint16_t*>(p); }
 
-// One decoder layer ("手写Qwen3-0.6B推理" §Qwen3DecoderLayer).  `pending`
-// counts split-K partial sums of the previous down projection that still
-// have to be added to the residual; they are folded into this layer's input
-// norm, and this layer's own down-projection partials are left pending.
-void run_layer(const LayerCtx& c, int& pending) {
+inline bool skinny_rows(int M) { return M <= q3v::SKINNY_MAX_ROWS; }
+
+// Skinny GEMM whose input is the norm-folded operand ws.h / ws.ssq.
+inline void skinny_normed(const LayerCtx& c, const void* W, void* out, int N, int ldo, Epi epi) {
+  SkinnyArgs a{};
+  a.X = c.ws.h;
+  a.W = U(W);
+  a.out = out;
+  a.M = c.B * c.T;
+  a.N = N;
+  a.K = C;
+  a.ldo = ldo;
+  a.ssq = c.ws.ssq;
+  a.ssq_ld = 64;
+  launch_gemm_skinny(a, 1, epi, c.s);
+}
+
+// Split-K skinny GEMM into the residual; the last workgroup per column block
+// adds the splits and prepares the next norm's operand (when gamma is set).
+inline void skinny_residual(const LayerCtx& c, const uint16_t* X, const void* W, int K, int n_split,
+                            const uint16_t* gamma) {
+  SkinnyArgs a{};
+  a.X = X;
+  a.W = U(W);
+  a.out = c.ws.part;
+  a.M = c.B * c.T;
+  a.N = C;
+  a.K = K;
+  a.ldo = C;
+  a.resid = c.resid;
+  a.gamma = gamma;
+  a.hg = c.ws.h;
+  a.ssq_out = c.ws.ssq;
+  a.counters = c.ws.tick;
+  launch_gemm_skinny(a, n_split, EPI_PARTIAL, c.s);
+}
+
+// One decoder layer ("手写Qwen3-0.6B推理" §Qwen3DecoderLayer).
+// Up to 64 rows (skinny path) the layer expects ws.h = bf16(gamma_in * r)
+// and ws.ssq = the row sums of squares, and leaves the same for gamma_next;
+// above that the norms run as separate kernels around the tiled GEMMs.
+void run_layer(const LayerCtx& c) {
   const int M = c.B * c.T;
-  const bool skinny = M <= q3v::SKINNY_MAX_ROWS;
+  const bool skinny = skinny_rows(M);
   const q3_layer_weights* w = c.w;
-  // input RMSNorm (+ deferred residual add)
-  launch_rmsnorm(c.resid, c.ws.part, pending, M, U(w->input_norm), c.ws.h, M, 1, 0, c.s);
-  pending = 0;
-  // merged q|k|v projection
-  if (skinny)
-    launch_gemm_skinny(c.ws.h, U(w->w_qkv), c.ws.qkv, M, QKV_N, C, QKV_N, 1, EPI_BF16, c.s);
-  else
-    launch_gemm_tiled(c.ws.h, U(w->w_qkv), c.ws.qkv, M, QKV_N, C, QKV_N, EPI_BF16, c.s);
-  // q/k RMSNorm + RoPE, K/V into the cache
-  launch_qknorm_rope(c.ws.qkv, U(w->q_norm), U(w->k_norm), c.cos, c.sin, c.ws.qr, c.kl, c.vl, c.B, c.T, c.max_seq,
-                     c.pos_dev, c.start, c.s);
-  // causal GQA attention
-  if (c.T == 1)
-    launch_attn_decode(c.ws.qr, c.kl, c.vl, c.ws.apart, c.ws.ao, c.B, c.max_seq, c.pos_dev, c.start, c.dec_splits,
-                       c.s);
-  else
-    launch_attn_prefill(c.ws.qr, c.kl, c.vl, c.ws.ao, c.B, c.T, c.start, c.max_seq, c.s);
-  // o_proj + residual, post-attention RMSNorm
+  // input RMSNorm + merged q|k|v projection
   if (skinny) {
-    launch_gemm_skinny(c.ws.ao, U(w->w_o), c.ws.part, M, C, QDIM, C, SPLIT_O, EPI_PARTIAL, c.s);
-    launch_rmsnorm(c.resid, c.ws.part, SPLIT_O, M, U(w->post_norm), c.ws.h, M, 1, 0, c.s);
+    skinny_normed(c, w->w_qkv, c.ws.qkv, QKV_N, QKV_N, EPI_BF16);
+  } else {
+    launch_rmsnorm(c.resid, nullptr, 0, M, U(w->input_norm), c.ws.h, M, 1, 0, c.s);
+    launch_gemm_tiled(c.ws.h, U(w->w_qkv), c.ws.qkv, M, QKV_N, C, QKV_N, EPI_BF16, c.s);
+  }
+  // q/k RMSNorm + RoPE, K/V into the cache, causal GQA attention
+  if (c.T == 1) {
+    launch_attn_decode(c.ws.qkv, U(w->q_norm), U(w->k_norm), c.cos, c.sin, c.kl, c.vl, c.ws.apart, c.ws.tick + 64,
+                       c.ws.ao, c.B, c.max_seq, c.pos_dev, c.start, c.dec_splits, c.s);
+  } else {
+    launch_qknorm_rope(c.ws.qkv, U(w->q_norm), U(w->k_norm), c.cos, c.sin, c.ws.qr, c.kl, c.vl, c.B, c.T,
+                       c.max_seq, c.pos_dev, c.start, c.s);
+    launch_attn_prefill(c.ws.qr, c.kl, c.vl, c.ws.ao, c.B, c.T, c.start, c.max_seq, c.s);
+  }
+  // o_proj + residual, post-attention RMSNorm, gate|up with silu(gate) * up, down + residual
+  if (skinny) {
+    skinny_residual(c, c.ws.ao, w->w_o, QDIM, SPLIT_O, U(w->post_norm));
+    skinny_normed(c, w->w_gate_up, c.ws.act, 2 * I, I, EPI_SILU);
+    skinny_residual(c, c.ws.act, w->w_down, I, SPLIT_DOWN, c.gamma_next);
   } else {
     launch_gemm_tiled(c.ws.ao, U(w->w_o), c.resid, M, C, QDIM, C, EPI_ADD_F32, c.s);
     launch_rmsnorm(c.resid, nullptr, 0, M, U(w->post_norm), c.ws.h, M, 1, 0, c.s);
-  }
-  // gate|up projection with silu(gate) * up, then down + residual
-  if (skinny) {
-    launch_gemm_skinny(c.ws.h, U(w->w_gate_up), c.ws.act, M, 2 * I, C, I, 1, EPI_SILU, c.s);
-    launch_gemm_skinny(c.ws.act, U(w->w_down), c.ws.part, M, C, I, C, SPLIT_DOWN, EPI_PARTIAL, c.s);
-    pending = SPLIT_DOWN;
-  } else {
     launch_gemm_tiled(c.ws.h, U(w->w_gate_up), c.ws.act, M, 2 * I, C, I, EPI_SILU, c.s);
     launch_gemm_tiled(c.ws.act, U(w->w_down), c.resid, M, C, I, C, EPI_ADD_F32, c.s);
   }
 }
 
 // Final RMSNorm on each sequence's last row, tied lm_head, argmax
-// ("手写Qwen3-0.6B推理" §Qwen3Model; "第 3 章" §4.1 and §4.3).
-void run_head(const q3_model* m, const Ws& ws, float* resid, int pending, int B, int T, float* logits,
-              int32_t* next_ids, int32_t* seq_lens, int seq_mode, int seq_val, hipStream_t s) {
-  const int part_rows = B * T;
-  launch_rmsnorm(resid, ws.part, pending, part_rows, U(m->final_norm), ws.fh, B, T, T - 1, s);
+// ("手写Qwen3-0.6B推理" §Qwen3Model; "第 3 章" §4.1 and §4.3).  On the
+// skinny path the last layer already left bf16(gamma_f * r) and the sums of
+// squares for every row; otherwise they are formed here for the B last rows.
+void run_head(const q3_model* m, const Ws& ws, int B, int T, float* logits, int32_t* next_ids, int32_t* seq_lens,
+              int seq_mode, int seq_val, hipStream_t s) {
+  const uint16_t* X;
+  const float* ssq;
+  int ldx, ssq_ld;
+  if (skinny_rows(B * T)) {
+    X = ws.h + (size_t)(T - 1) * C;
+    ldx = T * C;
+    ssq = ws.ssq + (size_t)(T - 1) * 64;
+    ssq_ld = T * 64;
+  } else {
+    launch_norm_operand(ws.resid, B, T, T - 1, U(m->final_norm), ws.fh, ws.ssq, nullptr, 0, s);
+    X = ws.fh;
+    ldx = C;
+    ssq = ws.ssq;
+    ssq_ld = 64;
+  }
   // logits plus each 16-row weight block's (max, argmax) per sequence
   constexpr int n_part = V / 16;
   for (int r0 = 0; r0 < B; r0 += q3v::SKINNY_MAX_ROWS) {
     const int rows = (B - r0) < q3v::SKINNY_MAX_ROWS ? (B - r0) : q3v::SKINNY_MAX_ROWS;
-    launch_gemm_skinny(ws.fh + (size_t)r0 * C, U(m->embed), logits + (size_t)r0 * V, rows, V, C, V, 1, EPI_LOGITS, s,
-                       static_cast<char*>(ws.amax) + (size_t)r0 * n_part * 8);
+    SkinnyArgs a{};
+    a.X = X + (size_t)r0 * ldx;
+    a.ldx = ldx;
+    a.W = U(m->embed);
+    a.out = logits + (size_t)r0 * V;
+    a.M = rows;
+    a.N = V;
+    a.K = C;
+    a.ldo = V;
+    a.amax_part = static_cast<char*>(ws.amax) + (size_t)r0 * n_part * 8;
+    a.ssq = ssq + (size_t)r0 * ssq_ld;
+    a.ssq_ld = ssq_ld;
+    launch_gemm_skinny(a, 1, EPI_LOGITS, s);
   }
   launch_argmax_partials(ws.amax, B, n_part, next_ids, seq_lens, seq_mode, seq_val, s);
 }
@@ -181,12 +243,14 @@ int q3_layer_forward(const q3_layer_weights* w, const float* rope_cos, const flo
   c.pos_dev = nullptr;
   c.dec_splits = q3v::decode_splits(batch, start_pos + 1);
   c.resid = residual;
+  c.gamma_next = nullptr;
   c.ws = carve(ws, batch, n_tokens);
   c.s = s;
-  int pending = 0;
-  run_layer(c, pending);
-  if (pending)  // fold the down-projection partials into the caller's residual
-    launch_rmsnorm(residual, c.ws.part, pending, batch * n_tokens, nullptr, nullptr, batch * n_tokens, 1, 0, s);
+  const int M = batch * n_tokens;
+  // the skinny path starts from the norm-folded operand; both paths start with zeroed tickets
+  launch_norm_operand(residual, skinny_rows(M) ? M : 0, 1, 0, U(w->input_norm), c.ws.h, c.ws.ssq, c.ws.tick,
+                      c.ws.n_tick, s);
+  run_layer(c);
   return launch_status();
 }
 
@@ -198,7 +262,9 @@ int q3_prefill(const q3_model* m, const q3_kv* kv, int32_t batch, int32_t prompt
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const Ws wsp = carve(ws, batch, prompt_len);
   const int M = batch * prompt_len;
-  launch_embed(ids, U(m->embed), wsp.resid, M, s);
+  const bool sk = skinny_rows(M);
+  launch_embed(ids, U(m->embed), wsp.resid, M, sk ? U(m->layer[0].input_norm) : nullptr, wsp.h, wsp.ssq, wsp.tick,
+               wsp.n_tick, s);
   LayerCtx c;
   c.cos = m->rope_cos;
   c.sin = m->rope_sin;
@@ -211,15 +277,14 @@ int q3_prefill(const q3_model* m, const q3_kv* kv, int32_t batch, int32_t prompt
   c.resid = wsp.resid;
   c.ws = wsp;
   c.s = s;
-  int pending = 0;
   for (int l = 0; l < NL; ++l) {
     c.w = &m->layer[l];
     c.kl = layer_cache(kv->k, l, kv);
     c.vl = layer_cache(kv->v, l, kv);
-    run_layer(c, pending);
+    c.gamma_next = U(l + 1 < NL ? m->layer[l + 1].input_norm : m->final_norm);
+    run_layer(c);
   }
-  run_head(m, wsp, wsp.resid, pending, batch, prompt_len, last_logits ? last_logits : wsp.logits, next_ids, seq_lens,
-           1, prompt_len, s);
+  run_head(m, wsp, batch, prompt_len, last_logits ? last_logits : wsp.logits, next_ids, seq_lens, 1, prompt_len, s);
   return launch_status();
 }
 
@@ -230,7 +295,9 @@ int q3_decode_step(const q3_model* m, const q3_kv* kv, int32_t batch, const int3
   if (st != Q3_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const Ws wsp = carve(ws, batch, 1);
-  launch_embed(in_ids, U(m->embed), wsp.resid, batch, s);
+  const bool sk = skinny_rows(batch);
+  launch_embed(in_ids, U(m->embed), wsp.resid, batch, sk ? U(m->layer[0].input_norm) : nullptr, wsp.h, wsp.ssq,
+               wsp.tick, wsp.n_tick, s);
   LayerCtx c;
   c.cos = m->rope_cos;
   c.sin = m->rope_sin;
@@ -243,14 +310,14 @@ int q3_decode_step(const q3_model* m, const q3_kv* kv, int32_t batch, const int3
   c.resid = wsp.resid;
   c.ws = wsp;
   c.s = s;
-  int pending = 0;
   for (int l = 0; l < NL; ++l) {
     c.w = &m->layer[l];
     c.kl = layer_cache(kv->k, l, kv);
     c.vl = layer_cache(kv->v, l, kv);
-    run_layer(c, pending);
+    c.gamma_next = U(l + 1 < NL ? m->layer[l + 1].input_norm : m->final_norm);
+    run_layer(c);
   }
-  run_head(m, wsp, wsp.resid, pending, batch, 1, logits ? logits : wsp.logits, out_ids, seq_lens, 2, 0, s);
+  run_head(m, wsp, batch, 1, logits ? logits : wsp.logits, out_ids, seq_lens, 2, 0, s);
   return launch_status();
 }
 

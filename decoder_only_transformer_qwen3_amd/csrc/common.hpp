@@ -62,6 +62,21 @@ __device__ __forceinline__ size_t vblk_index(int p, int d) {
   return ((size_t)(p >> 3) * D + d) * VBLK + (p & 7);
 }
 
+// Exchange between workgroups of one kernel without writing back or
+// invalidating the L2 caches: relaxed device-scope atomic loads and stores
+// carry the device-scope cache policy, so they are coherent across the
+// XCDs' separate L2 caches by themselves.  A producer stores its data with
+// st_dev, waits until the stores have completed (vm_drain), and only then
+// takes a ticket; the workgroup that draws the last ticket reads with
+// ld_dev.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ float wave_sum(float v) {

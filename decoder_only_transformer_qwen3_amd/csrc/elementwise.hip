@@ -8,23 +8,94 @@
 namespace q3 {
 
 // ---------------------------------------------------------------- embedding
-// x = E[id] with no scaling ("手写Qwen3-0.6B推理" §Qwen3Model).  One block of
-// 128 threads per token; each thread widens 8 bf16 values (one 16 B load).
-__global__ __launch_bounds__(128) void k_embed(const int32_t* __restrict__ ids, const uint16_t* __restrict__ E,
-                                               float* __restrict__ resid) {
-  const int m = blockIdx.x;
-  int id = ids[m];
-  id = id < 0 ? 0 : (id >= V ? V - 1 : id);  // out-of-range ids are clamped, never read out of bounds
-  const u32x4 w = *reinterpret_cast<const u32x4*>(E + (size_t)id * C + threadIdx.x * 8);
-  f32x4 a = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y)};
-  f32x4 b = {bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w)};
-  f32x4* dst = reinterpret_cast<f32x4*>(resid + (size_t)m * C) + threadIdx.x * 2;
-  dst[0] = a;
-  dst[1] = b;
+// x = E[id] with no scaling ("手写Qwen3-0.6B推理" §Qwen3Model), plus, when a
+// gain is given, the operand of the first layer's norm-folded projection:
+// hg = bf16(gamma * x) and the per-16-column sums of squares ssq[m][64]
+// (the GEMM applies 1 / rms(x) itself).  One wave per token; lane l owns
+// columns 16l .. 16l+15, i.e. column block l.  Block 0 also clears the
+// call's workgroup tickets.
+__device__ __forceinline__ void norm_operand_row(const float (&x)[16], int lane, const uint16_t* __restrict__ gamma,
+                                                 uint16_t* __restrict__ hg_row, float* __restrict__ ssq_row) {
+  const u32x4* gp = reinterpret_cast<const u32x4*>(gamma + 16 * lane);
+  const u32x4 g0 = gp[0], g1 = gp[1];
+  const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+  u32x4 o[2];
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    o[e >> 2][e & 3] = pack_bf2(x[2 * e] * bf_lo(gw[e]), x[2 * e + 1] * bf_hi(gw[e]));
+    ss += x[2 * e] * x[2 * e] + x[2 * e + 1] * x[2 * e + 1];
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(hg_row + 16 * lane);
+  dst[0] = o[0];
+  dst[1] = o[1];
+  ssq_row[lane] = ss;
 }
 
-void launch_embed(const int32_t* ids, const uint16_t* E, float* resid, int M, hipStream_t s) {
-  hipLaunchKernelGGL(k_embed, dim3(M), dim3(128), 0, s, ids, E, resid);
+__device__ __forceinline__ void clear_tickets(int* counters, int n) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < n; i += blockDim.x) counters[i] = 0;
+}
+
+__global__ __launch_bounds__(256) void k_embed(const int32_t* __restrict__ ids, const uint16_t* __restrict__ E,
+                                               float* __restrict__ resid, int M, const uint16_t* __restrict__ gamma,
+                                               uint16_t* __restrict__ hg, float* __restrict__ ssq,
+                                               int* __restrict__ counters, int n_counters) {
+  clear_tickets(counters, n_counters);
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  int id = ids[m];
+  id = id < 0 ? 0 : (id >= V ? V - 1 : id);  // out-of-range ids are clamped, never read out of bounds
+  const u32x4* src = reinterpret_cast<const u32x4*>(E + (size_t)id * C + 16 * lane);
+  const u32x4 w0 = src[0], w1 = src[1];
+  const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  float x[16];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    x[2 * e] = bf_lo(ww[e]);
+    x[2 * e + 1] = bf_hi(ww[e]);
+  }
+  f32x4* dst = reinterpret_cast<f32x4*>(resid + (size_t)m * C + 16 * lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = f32x4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
+  if (gamma) norm_operand_row(x, lane, gamma, hg + (size_t)m * C, ssq + (size_t)m * 64);
+}
+
+void launch_embed(const int32_t* ids, const uint16_t* E, float* resid, int M, const uint16_t* gamma, uint16_t* hg,
+                  float* ssq, int* counters, int n_counters, hipStream_t s) {
+  hipLaunchKernelGGL(k_embed, dim3((M + 3) / 4), dim3(256), 0, s, ids, E, resid, M, gamma, hg, ssq, counters,
+                     n_counters);
+}
+
+// Norm-folded operand of n_rows residual rows (row r of the output reads
+// resid row r*row_step + row_off): hg[r] = bf16(gamma * x), ssq[r][64].
+__global__ __launch_bounds__(256) void k_norm_operand(const float* __restrict__ resid, int n_rows, int row_step,
+                                                      int row_off, const uint16_t* __restrict__ gamma,
+                                                      uint16_t* __restrict__ hg, float* __restrict__ ssq,
+                                                      int* __restrict__ counters, int n_counters) {
+  clear_tickets(counters, n_counters);
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n_rows) return;
+  const f32x4* src = reinterpret_cast<const f32x4*>(resid + ((size_t)r * row_step + row_off) * C + 16 * lane);
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 v = src[i];
+    x[4 * i] = v.x;
+    x[4 * i + 1] = v.y;
+    x[4 * i + 2] = v.z;
+    x[4 * i + 3] = v.w;
+  }
+  norm_operand_row(x, lane, gamma, hg + (size_t)r * C, ssq + (size_t)r * 64);
+}
+
+void launch_norm_operand(const float* resid, int n_rows, int row_step, int row_off, const uint16_t* gamma,
+                         uint16_t* hg, float* ssq, int* counters, int n_counters, hipStream_t s) {
+  const int blocks = n_rows > 0 ? (n_rows + 3) / 4 : 1;  // one block still clears the tickets
+  hipLaunchKernelGGL(k_norm_operand, dim3(blocks), dim3(256), 0, s, resid, n_rows, row_step, row_off,
+                     gamma, hg, ssq, counters, n_counters);
 }
 
 // ---------------------------------------------------------------- RMSNorm

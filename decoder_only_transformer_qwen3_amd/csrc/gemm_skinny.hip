@@ -16,6 +16,19 @@
 // Work split: one workgroup (4 waves) per 16 weight rows and K range
 // (grid.y splits K).  The 4 waves take interleaved 32-wide k-steps, are
 // reduced through LDS, and the epilogue runs once per output element.
+//
+// Input RMSNorm folded into the GEMM ("手写Qwen3-0.6B推理" §Qwen3RMSNorm):
+// with h = gamma * r / rms(r), h W^T = (1 / rms(r)) * ((gamma * r) W^T), so
+// the producer of r stores X = bf16(gamma * r) and, per 16-column block j,
+// ssq[m][j] = sum of r^2 over the block; this kernel multiplies each output
+// row by 1 / sqrt(sum_j ssq[m][j] / 1024 + eps) in the epilogue.
+//
+// Split-K with an in-kernel finish (EPI_PARTIAL with a residual): every
+// workgroup stores its partial sums, and the last of the grid.y workgroups
+// of a 16-column block (an atomic ticket per block) adds all of them to the
+// float32 residual, and, when a gain is given, writes the next norm's
+// bf16(gamma * r) and the block's sum of squares ("第 3 章" §3.2 fuses the
+// residual add with the following norm in the same way).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -28,12 +41,16 @@ __device__ __forceinline__ bool am_better2(float a, int ia, float b, int ib) {
 }
 
 template <int NB, int EPI, int U>
-__global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
-                                                     void* __restrict__ out, int M, int N, int K, int ldo,
-                                                     int kspan, void* __restrict__ amax_part) {
+__global__ __launch_bounds__(256) void k_gemm_skinny(SkinnyArgs a) {
   __shared__ float red[4][NB * 16][17];
+  __shared__ float rsc[NB * 16];
+  __shared__ int last_ticket;
+  const uint16_t* __restrict__ X = a.X;
+  const uint16_t* __restrict__ W = a.W;
+  const int M = a.M, N = a.N, K = a.K, kspan = a.kspan;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, qd = l >> 4;
   const int rb = blockIdx.x, split = blockIdx.y;
+  const int t = threadIdx.x;
   int wrow;
   if constexpr (EPI == EPI_SILU) {
     // rows 0..7 of the block are gate rows, 8..15 the matching up rows
@@ -42,6 +59,15 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
   } else {
     wrow = rb * 16 + r;
   }
+  // norm statistics are loaded first so their latency hides behind the weight stream
+  const int sm = t >> 2;  // row whose 16 of 64 block sums this thread reads
+  f32x4 sq[4] = {};
+  const bool scaled = a.ssq != nullptr;
+  if (scaled && sm < M) {
+    const f32x4* sp = reinterpret_cast<const f32x4*>(a.ssq + (size_t)sm * a.ssq_ld + 16 * (t & 3));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sq[i] = sp[i];
+  }
   const size_t k_base = (size_t)split * kspan + qd * 8;
   const uint16_t* wp = W + (size_t)wrow * K + k_base;
   const uint16_t* xp[NB];
@@ -49,7 +75,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
   for (int nb = 0; nb < NB; ++nb) {
     int m = nb * 16 + r;
     m = m < M ? m : M - 1;
-    xp[nb] = X + (size_t)m * K + k_base;
+    xp[nb] = X + (size_t)m * a.ldx + k_base;
   }
   f32x4 acc[NB];
 #pragma unroll
@@ -57,10 +83,10 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
 
   const int nsteps = kspan >> 5;  // 32-wide k-steps in this workgroup's range
   for (int s0 = w; s0 < nsteps; s0 += 4 * U) {
-    u32x4 a[U];
+    u32x4 wa[U];
     u32x4 bx[U][NB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + (size_t)(s0 + 4 * u) * 32));
+    for (int u = 0; u < U; ++u) wa[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + (size_t)(s0 + 4 * u) * 32));
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -69,24 +95,31 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u]), as_bf16x8(bx[u][nb]), acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u]), as_bf16x8(bx[u][nb]), acc[nb], 0, 0, 0);
   }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[w][nb * 16 + r][4 * qd + i] = acc[nb][i];
+  if (scaled) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ss += (sq[i].x + sq[i].y) + (sq[i].z + sq[i].w);
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    if ((t & 3) == 0 && sm < NB * 16) rsc[sm] = 1.0f / sqrtf(ss * (1.0f / C) + EPS);
+  }
   __syncthreads();
-
-  const int t = threadIdx.x;
   if constexpr (EPI == EPI_SILU) {
     // out[m][rb*8 + j] = silu(gate) * up
     for (int e = t; e < NB * 16 * 8; e += 256) {
       const int m = e >> 3, j = e & 7;
       if (m >= M) continue;
-      const float gsum = red[0][m][j] + red[1][m][j] + red[2][m][j] + red[3][m][j];
-      const float usum = red[0][m][8 + j] + red[1][m][8 + j] + red[2][m][8 + j] + red[3][m][8 + j];
+      const float rs = scaled ? rsc[m] : 1.0f;
+      const float gsum = (red[0][m][j] + red[1][m][j] + red[2][m][j] + red[3][m][j]) * rs;
+      const float usum = (red[0][m][8 + j] + red[1][m][8 + j] + red[2][m][8 + j] + red[3][m][8 + j]) * rs;
       const float sg = gsum / (1.0f + __expf(-gsum));
-      reinterpret_cast<uint16_t*>(out)[(size_t)m * ldo + rb * 8 + j] = (uint16_t)f2bf(sg * usum);
+      reinterpret_cast<uint16_t*>(a.out)[(size_t)m * a.ldo + rb * 8 + j] = (uint16_t)f2bf(sg * usum);
     }
   } else {
     if (t < NB * 16 * 4) {
@@ -95,7 +128,10 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
         f32x4 v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = red[0][m][4 * ng + i] + red[1][m][4 * ng + i] + red[2][m][4 * ng + i] + red[3][m][4 * ng + i];
+        if (scaled) v *= rsc[m];
         const int n = rb * 16 + 4 * ng;
+        void* const out = a.out;
+        const int ldo = a.ldo;
         if constexpr (EPI == EPI_BF16) {
           u32x2 o;
           o.x = pack_bf2(v[0], v[1]);
@@ -124,57 +160,104 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
             }
           }
           if (ng == 0) {
-            float2* ap = reinterpret_cast<float2*>(amax_part) + (size_t)m * gridDim.x + rb;
+            float2* ap = reinterpret_cast<float2*>(a.amax_part) + (size_t)m * gridDim.x + rb;
             *ap = make_float2(bv, __int_as_float(bi));
           }
         } else if constexpr (EPI == EPI_ADD_F32) {
           f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)m * ldo + n);
           *dst = *dst + v;
-        } else {  // EPI_PARTIAL
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + ((size_t)split * M + m) * N + n) = v;
+        } else {  // EPI_PARTIAL (device-coherent stores: the last workgroup of the block reads them)
+          float* pp = reinterpret_cast<float*>(out) + ((size_t)split * M + m) * N + n;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st_dev(pp + i, v[i]);
         }
       }
     }
   }
+  if constexpr (EPI == EPI_PARTIAL) {
+    if (a.resid == nullptr) return;
+    // ticket: the last workgroup of this column block finishes it
+    vm_drain();
+    __syncthreads();
+    if (t == 0) last_ticket = atomicAdd(a.counters + rb, 1) == (int)gridDim.y - 1;
+    __syncthreads();
+    if (!last_ticket) return;
+    if (t < NB * 16 * 4) {
+      const int m = t >> 2, ng = t & 3;
+      const int n = rb * 16 + 4 * ng;
+      float ss = 0.f;
+      if (m < M) {
+        f32x4* rp = reinterpret_cast<f32x4*>(a.resid + (size_t)m * N + n);
+        f32x4 v = *rp;
+        const float* pp = reinterpret_cast<const float*>(a.out) + (size_t)m * N + n;
+        for (int sp = 0; sp < (int)gridDim.y; ++sp) {
+          const float* q = pp + (size_t)sp * M * N;
+          v += f32x4{ld_dev(q), ld_dev(q + 1), ld_dev(q + 2), ld_dev(q + 3)};
+        }
+        *rp = v;
+        if (a.gamma) {
+          const u32x2 g = *reinterpret_cast<const u32x2*>(a.gamma + n);
+          u32x2 o;
+          o.x = pack_bf2(v.x * bf_lo(g.x), v.y * bf_hi(g.x));
+          o.y = pack_bf2(v.z * bf_lo(g.y), v.w * bf_hi(g.y));
+          *reinterpret_cast<u32x2*>(a.hg + (size_t)m * N + n) = o;
+          ss = (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+        }
+      }
+      // groups of 4 lanes share m and are whole inside the wave
+      ss += __shfl_xor(ss, 1, 64);
+      ss += __shfl_xor(ss, 2, 64);
+      if (a.gamma && m < M && ng == 0) a.ssq_out[(size_t)m * 64 + rb] = ss;
+    }
+    if (t == 0) a.counters[rb] = 0;  // ready for the next call
+  }
 }
 
 template <int NB, int EPI>
-static void launch_nb(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo, int n_split,
-                      hipStream_t s, void* amax_part) {
-  const int kspan = K / n_split;
-  const int rows_per_block = 16;
-  const int gx = (EPI == EPI_SILU) ? (N / 2) / 8 : N / rows_per_block;
+static void launch_nb(const SkinnyArgs& a, int n_split, hipStream_t s) {
+  const int gx = (EPI == EPI_SILU) ? (a.N / 2) / 8 : a.N / 16;
   // Each wave takes kspan/128 steps; unroll by 8 when that divides evenly.
-  if (((kspan >> 5) % 32) == 0)
-    hipLaunchKernelGGL((k_gemm_skinny<NB, EPI, 8>), dim3(gx, n_split), dim3(256), 0, s, X, W, out, M, N, K, ldo, kspan,
-                       amax_part);
+  if (((a.kspan >> 5) % 32) == 0)
+    hipLaunchKernelGGL((k_gemm_skinny<NB, EPI, 8>), dim3(gx, n_split), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((k_gemm_skinny<NB, EPI, 4>), dim3(gx, n_split), dim3(256), 0, s, X, W, out, M, N, K, ldo, kspan,
-                       amax_part);
+    hipLaunchKernelGGL((k_gemm_skinny<NB, EPI, 4>), dim3(gx, n_split), dim3(256), 0, s, a);
 }
 
 template <int EPI>
-static void launch_epi(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo, int n_split,
-                       hipStream_t s, void* amax_part = nullptr) {
-  const int nb = (M + 15) / 16;
-  switch (nb) {
-    case 1: launch_nb<1, EPI>(X, W, out, M, N, K, ldo, n_split, s, amax_part); break;
-    case 2: launch_nb<2, EPI>(X, W, out, M, N, K, ldo, n_split, s, amax_part); break;
-    case 3: launch_nb<3, EPI>(X, W, out, M, N, K, ldo, n_split, s, amax_part); break;
-    default: launch_nb<4, EPI>(X, W, out, M, N, K, ldo, n_split, s, amax_part); break;
+static void launch_epi(const SkinnyArgs& a, int n_split, hipStream_t s) {
+  switch ((a.M + 15) / 16) {
+    case 1: launch_nb<1, EPI>(a, n_split, s); break;
+    case 2: launch_nb<2, EPI>(a, n_split, s); break;
+    case 3: launch_nb<3, EPI>(a, n_split, s); break;
+    default: launch_nb<4, EPI>(a, n_split, s); break;
+  }
+}
+
+void launch_gemm_skinny(SkinnyArgs a, int n_split, Epi epi, hipStream_t s) {
+  if (a.ldx == 0) a.ldx = a.K;
+  a.kspan = a.K / n_split;
+  switch (epi) {
+    case EPI_LOGITS: launch_epi<EPI_LOGITS>(a, n_split, s); break;
+    case EPI_BF16: launch_epi<EPI_BF16>(a, n_split, s); break;
+    case EPI_F32: launch_epi<EPI_F32>(a, n_split, s); break;
+    case EPI_ADD_F32: launch_epi<EPI_ADD_F32>(a, n_split, s); break;
+    case EPI_SILU: launch_epi<EPI_SILU>(a, n_split, s); break;
+    case EPI_PARTIAL: launch_epi<EPI_PARTIAL>(a, n_split, s); break;
   }
 }
 
 void launch_gemm_skinny(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo, int n_split,
                         Epi epi, hipStream_t s, void* amax_part) {
-  switch (epi) {
-    case EPI_LOGITS: launch_epi<EPI_LOGITS>(X, W, out, M, N, K, ldo, n_split, s, amax_part); break;
-    case EPI_BF16: launch_epi<EPI_BF16>(X, W, out, M, N, K, ldo, n_split, s); break;
-    case EPI_F32: launch_epi<EPI_F32>(X, W, out, M, N, K, ldo, n_split, s); break;
-    case EPI_ADD_F32: launch_epi<EPI_ADD_F32>(X, W, out, M, N, K, ldo, n_split, s); break;
-    case EPI_SILU: launch_epi<EPI_SILU>(X, W, out, M, N, K, ldo, n_split, s); break;
-    case EPI_PARTIAL: launch_epi<EPI_PARTIAL>(X, W, out, M, N, K, ldo, n_split, s); break;
-  }
+  SkinnyArgs a{};
+  a.X = X;
+  a.W = W;
+  a.out = out;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.ldo = ldo;
+  a.amax_part = amax_part;
+  launch_gemm_skinny(a, n_split, epi, s);
 }
 
 }  // namespace q3

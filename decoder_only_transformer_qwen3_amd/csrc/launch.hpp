@@ -17,8 +17,16 @@ enum Epi : int {
   EPI_LOGITS = 5,   // out f32 [M, ldo] and, per 16-column block, the block's (max, argmax) per row
 };
 
-// x[m] = E[ids[m]] widened to f32 (one row of 1024 per token).
-void launch_embed(const int32_t* ids, const uint16_t* E, float* resid, int M, hipStream_t s);
+// x[m] = E[ids[m]] widened to f32 (one row of 1024 per token); with a gain
+// also hg[m] = bf16(gamma * x[m]) and ssq[m][j] = sum of x^2 over columns
+// 16j..16j+15.  The first n_counters ints of `counters` are set to zero.
+void launch_embed(const int32_t* ids, const uint16_t* E, float* resid, int M, const uint16_t* gamma, uint16_t* hg,
+                  float* ssq, int* counters, int n_counters, hipStream_t s);
+
+// hg[r] = bf16(gamma * resid[r*row_step + row_off]) and ssq[r][64] for r < n_rows;
+// clears n_counters tickets.
+void launch_norm_operand(const float* resid, int n_rows, int row_step, int row_off, const uint16_t* gamma,
+                         uint16_t* hg, float* ssq, int* counters, int n_counters, hipStream_t s);
 
 // For r < n_rows, row = r*row_step + row_off:
 //   resid[row] += sum_{j < n_part} part[j][row]      (written back when n_part > 0)
@@ -41,6 +49,27 @@ void launch_gemm_tiled(const uint16_t* X, const uint16_t* W, void* out, int M, i
 
 // MFMA skinny GEMM for M <= 64 rows (weight streaming), split into n_split K ranges.
 // Requires N % 16 == 0 and (K / n_split) % 512 == 0; EPI_PARTIAL writes [n_split][M][N].
+struct SkinnyArgs {
+  const uint16_t* X;  // activations, row m at X + m * ldx (ldx = 0 means K)
+  const uint16_t* W;  // weights [N, K]
+  void* out;
+  int M, N, K, ldo, ldx, kspan;
+  void* amax_part;    // EPI_LOGITS: per-16-column (max, argmax) of each row
+  // Optional input-norm scale: X holds bf16(gamma * r); output row m is
+  // multiplied by 1 / sqrt(sum_{j<64} ssq[m * ssq_ld + j] / 1024 + eps).
+  const float* ssq;
+  int ssq_ld;
+  // EPI_PARTIAL finish (N == 1024, resid != null): the last workgroup of
+  // each 16-column block adds all K splits to resid [M][1024]; with a gain
+  // it also writes hg = bf16(gamma * r) [M][1024] and ssq_out [M][64].
+  // counters: 64 ints, zero on entry and left zero on exit.
+  float* resid;
+  const uint16_t* gamma;
+  uint16_t* hg;
+  float* ssq_out;
+  int* counters;
+};
+void launch_gemm_skinny(SkinnyArgs a, int n_split, Epi epi, hipStream_t s);
 void launch_gemm_skinny(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo,
                         int n_split, Epi epi, hipStream_t s, void* amax_part = nullptr);
 
@@ -48,8 +77,14 @@ void launch_gemm_skinny(const uint16_t* X, const uint16_t* W, void* out, int M, 
 void launch_attn_prefill(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out,
                          int B, int T, int start, int max_seq, hipStream_t s);
 
-// Split-K decode attention (one query per sequence) + log-sum-exp merge.
-void launch_attn_decode(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, float* part,
+// Split-K decode attention for one new token per sequence, from the raw
+// merged projection qkv [B][4096]: per-head q/k RMSNorm + RoPE of the new
+// token, its K/V written into the cache at its position, attention over
+// positions 0..p, and the log-sum-exp merge of the splits done by the last
+// workgroup of each (sequence, KV head) (counters: B*8 ints, zero on entry,
+// left zero).  out is [B][2048] bf16; part holds [B][16][n_split][130] f32.
+void launch_attn_decode(const uint16_t* qkv, const uint16_t* q_norm, const uint16_t* k_norm, const float* rope_cos,
+                        const float* rope_sin, uint16_t* k_cache, uint16_t* v_cache, float* part, int* counters,
                         uint16_t* out, int B, int max_seq, const int32_t* pos_dev, int start, int n_split,
                         hipStream_t s);
 

@@ -30,6 +30,8 @@ WsLayout ws_layout(int32_t batch, int32_t n_tokens) {
   L.logits = take((size_t)batch * Q3_VOCAB * 4);
   L.amax = take((size_t)batch * (Q3_VOCAB / 16) * 8);
   L.fh = take((size_t)batch * Q3_HIDDEN * 2);
+  L.ssq = take(M * 64 * 4);
+  L.tick = take((size_t)ticket_count(batch) * 4);
   L.total = off;
   return L;
 }

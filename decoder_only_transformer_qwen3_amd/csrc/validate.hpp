@@ -16,12 +16,15 @@ constexpr int SKINNY_MAX_ROWS = 64;  // row counts up to this use the skinny GEM
 constexpr int64_t MAX_TOKENS = 1 << 22;
 
 struct WsLayout {
-  size_t resid, h, qkv, qr, ao, act, part, apart, logits, amax, fh;
+  size_t resid, h, qkv, qr, ao, act, part, apart, logits, amax, fh, ssq, tick;
   size_t total;
 };
 
 // Byte offsets of every workspace region for `batch` x `n_tokens` (256-B aligned).
 WsLayout ws_layout(int32_t batch, int32_t n_tokens);
+
+// Workgroup tickets in the workspace: 64 column blocks + 8 per sequence.
+inline int ticket_count(int32_t batch) { return 64 + 8 * batch; }
 
 // Number of decode-attention splits for `batch` sequences of at most `ctx` keys.
 int decode_splits(int32_t batch, int32_t ctx);
