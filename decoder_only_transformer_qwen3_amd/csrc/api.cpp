@@ -20,6 +20,8 @@ namespace {
 // Skinny-GEMM K splits: o_proj K = 2048 -> 4 x 512, down K = 3072 -> 6 x 512.
 constexpr int SPLIT_O = 4;
 constexpr int SPLIT_DOWN = 6;
+// Row counts up to this run o_proj / down as a VALU GEMV without a K split.
+constexpr int GEMV_MAX_ROWS = 8;
 
 struct Ws {
   float* resid;
@@ -68,6 +70,9 @@ inline const uint16_t* U(const void* p) { return static_cast<const uint16_t*>(p)
 
 inline bool skinny_rows(int M) { return M <= q3v::SKINNY_MAX_ROWS; }
 
+// Partial sums of squares per residual row (see NSQ in common.hpp).
+inline int nsq_for(int M) { return M <= GEMV_MAX_ROWS ? NSQ : NSQ_BLK; }
+
 // Skinny GEMM whose input is the norm-folded operand ws.h / ws.ssq.
 inline void skinny_normed(const LayerCtx& c, const void* W, void* out, int N, int ldo, Epi epi) {
   SkinnyArgs a{};
@@ -79,26 +84,35 @@ inline void skinny_normed(const LayerCtx& c, const void* W, void* out, int N, in
   a.K = C;
   a.ldo = ldo;
   a.ssq = c.ws.ssq;
-  a.ssq_ld = 64;
+  a.ssq_n = nsq_for(a.M);
+  a.ssq_ld = a.ssq_n;
   launch_gemm_skinny(a, 1, epi, c.s);
 }
 
-// Split-K skinny GEMM into the residual; the last workgroup per column block
-// adds the splits and prepares the next norm's operand (when gamma is set).
+// Projection into the residual that also prepares the next norm's operand
+// (when gamma is set).  Up to 8 rows a VALU GEMV covers each column over the
+// whole K range; above that the MFMA skinny GEMM splits K and the last
+// workgroup per column block adds the splits.
 inline void skinny_residual(const LayerCtx& c, const uint16_t* X, const void* W, int K, int n_split,
                             const uint16_t* gamma) {
+  const int M = c.B * c.T;
+  if (M <= GEMV_MAX_ROWS) {
+    launch_gemv_resid(X, U(W), K, c.resid, M, gamma, c.ws.h, c.ws.ssq, c.s);
+    return;
+  }
   SkinnyArgs a{};
   a.X = X;
   a.W = U(W);
-  a.out = c.ws.part;
-  a.M = c.B * c.T;
+  a.M = M;
   a.N = C;
   a.K = K;
   a.ldo = C;
-  a.resid = c.resid;
   a.gamma = gamma;
   a.hg = c.ws.h;
   a.ssq_out = c.ws.ssq;
+  a.ssq_n = nsq_for(M);
+  a.out = c.ws.part;
+  a.resid = c.resid;
   a.counters = c.ws.tick;
   launch_gemm_skinny(a, n_split, EPI_PARTIAL, c.s);
 }
@@ -148,18 +162,20 @@ void run_head(const q3_model* m, const Ws& ws, int B, int T, float* logits, int3
               int seq_mode, int seq_val, hipStream_t s) {
   const uint16_t* X;
   const float* ssq;
-  int ldx, ssq_ld;
+  int ldx, ssq_ld, ssq_n;
   if (skinny_rows(B * T)) {
+    ssq_n = nsq_for(B * T);
     X = ws.h + (size_t)(T - 1) * C;
     ldx = T * C;
-    ssq = ws.ssq + (size_t)(T - 1) * 64;
-    ssq_ld = T * 64;
+    ssq = ws.ssq + (size_t)(T - 1) * ssq_n;
+    ssq_ld = T * ssq_n;
   } else {
-    launch_norm_operand(ws.resid, B, T, T - 1, U(m->final_norm), ws.fh, ws.ssq, nullptr, 0, s);
+    ssq_n = NSQ_BLK;
+    launch_norm_operand(ws.resid, B, T, T - 1, U(m->final_norm), ws.fh, ws.ssq, ssq_n, nullptr, 0, s);
     X = ws.fh;
     ldx = C;
     ssq = ws.ssq;
-    ssq_ld = 64;
+    ssq_ld = ssq_n;
   }
   // logits plus each 16-row weight block's (max, argmax) per sequence
   constexpr int n_part = V / 16;
@@ -177,6 +193,7 @@ void run_head(const q3_model* m, const Ws& ws, int B, int T, float* logits, int3
     a.amax_part = static_cast<char*>(ws.amax) + (size_t)r0 * n_part * 8;
     a.ssq = ssq + (size_t)r0 * ssq_ld;
     a.ssq_ld = ssq_ld;
+    a.ssq_n = ssq_n;
     launch_gemm_skinny(a, 1, EPI_LOGITS, s);
   }
   launch_argmax_partials(ws.amax, B, n_part, next_ids, seq_lens, seq_mode, seq_val, s);
@@ -248,8 +265,8 @@ int q3_layer_forward(const q3_layer_weights* w, const float* rope_cos, const flo
   c.s = s;
   const int M = batch * n_tokens;
   // the skinny path starts from the norm-folded operand; both paths start with zeroed tickets
-  launch_norm_operand(residual, skinny_rows(M) ? M : 0, 1, 0, U(w->input_norm), c.ws.h, c.ws.ssq, c.ws.tick,
-                      c.ws.n_tick, s);
+  launch_norm_operand(residual, skinny_rows(M) ? M : 0, 1, 0, U(w->input_norm), c.ws.h, c.ws.ssq, nsq_for(M),
+                      c.ws.tick, c.ws.n_tick, s);
   run_layer(c);
   return launch_status();
 }
@@ -263,8 +280,8 @@ int q3_prefill(const q3_model* m, const q3_kv* kv, int32_t batch, int32_t prompt
   const Ws wsp = carve(ws, batch, prompt_len);
   const int M = batch * prompt_len;
   const bool sk = skinny_rows(M);
-  launch_embed(ids, U(m->embed), wsp.resid, M, sk ? U(m->layer[0].input_norm) : nullptr, wsp.h, wsp.ssq, wsp.tick,
-               wsp.n_tick, s);
+  launch_embed(ids, U(m->embed), wsp.resid, M, sk ? U(m->layer[0].input_norm) : nullptr, wsp.h, wsp.ssq, nsq_for(M),
+               wsp.tick, wsp.n_tick, s);
   LayerCtx c;
   c.cos = m->rope_cos;
   c.sin = m->rope_sin;
@@ -297,7 +314,7 @@ int q3_decode_step(const q3_model* m, const q3_kv* kv, int32_t batch, const int3
   const Ws wsp = carve(ws, batch, 1);
   const bool sk = skinny_rows(batch);
   launch_embed(in_ids, U(m->embed), wsp.resid, batch, sk ? U(m->layer[0].input_norm) : nullptr, wsp.h, wsp.ssq,
-               wsp.tick, wsp.n_tick, s);
+               nsq_for(batch), wsp.tick, wsp.n_tick, s);
   LayerCtx c;
   c.cos = m->rope_cos;
   c.sin = m->rope_sin;

@@ -7,26 +7,32 @@
 // per-head q/k RMSNorm and NeoX RoPE ("手写Qwen3-0.6B推理" §Attention and
 // §Rope) and the cache write of the new K/V happen here as well:
 //   q' = rope_p(gamma_q * q / sqrt(mean(q^2) + eps)), likewise k'; v as is.
-// A 16-lane DPP row holds one 128-dim head row, lane j dims 8j..8j+7, so the
-// head's sum of squares is a row sum and RoPE's partner dims (i, i+64) sit
-// in lanes j and j^8 (a row rotate by 8).
+// For that step a 16-lane DPP row holds one 128-dim head row (lane j dims
+// 8j..8j+7): the head's sum of squares is a row sum and RoPE's partner
+// dims (i, i+64) sit in lanes j and j^8 (a row rotate by 8).
 //
-// Grid (split, KV head g, sequence b).  A workgroup reads its key range of
-// K and V exactly once and serves both query heads 2g, 2g+1 that share g.
-// Keys are processed in sub-chunks of up to 512: pass 1 computes scores
-// into LDS (16 lanes per key row, 16 B per lane, row sums over the 16
-// lanes with DPP), the sub-chunk's softmax statistics are merged into a
-// running (max, sum), and pass 2 accumulates p * V over the blocked V
-// cache (8 positions x 128 dims per 2 KB block): lane l owns dims 2l and
-// 2l+1 and reads their 8 positions as two 16 B loads.  The workgroup whose
-// range holds p takes the new key and value from registers / LDS rather
-// than from the cache it is writing.
+// Grid (split, KV head g, sequence b); each workgroup reads its key range of
+// K and V once for both query heads 2g, 2g+1.  Its 4 waves take 32-key
+// tiles round-robin and each keeps its own online softmax, on
+// v_mfma_f32_16x16x32_bf16 (lane l: A row l%16, B column l%16, k-slot
+// (l/16, j); C column l%16, rows 4(l/16)+i):
+//   scores  S^T[key][head] = K q^T, two MFMA chains of 16 keys whose A rows
+//           are ordered so that lane l ends up holding keys 8(l/16)+0..7 of
+//           head l%16;
+//   values  O^T[dim][head] += V^T P^T, where P^T is exactly those registers
+//           (exp2, packed to bf16) and the A operand, 8 consecutive
+//           positions of one dim, is one 16 B chunk of the blocked V cache.
+// Only columns 0 and 1 (the two query heads) are used.  The running max is
+// raised only when a score exceeds it by more than 8 (log2 units), so most
+// tiles need no cross-lane exchange.  The next tile's loads are in flight
+// while a tile is computed.  The split that owns position p writes the new
+// K/V into the cache and takes them from LDS rather than from the cache.
 //
-// Each split writes unnormalised (o, m, l) in the log2 domain; the last
-// split to finish for a (b, g) (atomic ticket) combines them with the usual
-// log-sum-exp rescaling and writes the two heads' bf16 outputs.  The key
-// range of a split follows from the sequence's own device length, so the
-// result is exact whatever split count the host picked.
+// The 4 waves combine in LDS; each split writes unnormalised (o, m, l) in
+// the log2 domain; the last split to finish for a (b, g) (atomic ticket)
+// merges them with log-sum-exp rescaling and writes the two heads' bf16
+// outputs.  The key range of a split follows from the sequence's own device
+// length, so the result is exact whatever split count the host picked.
 #include <math.h>
 
 #include "common.hpp"
@@ -34,9 +40,10 @@
 
 namespace q3 {
 
-constexpr int DEC_SUB = 512;  // keys per LDS sub-chunk
+constexpr int DT = 32;  // keys per wave tile
 constexpr int PART_STRIDE = D + 2;
 constexpr int DEC_SPLIT_CAP = 64;
+constexpr float DEC_RESCALE_SLACK = 8.0f;
 
 __device__ __forceinline__ void load_row8(const uint16_t* src, float (&f)[8]) {
   const u32x4 w = *reinterpret_cast<const u32x4*>(src);
@@ -78,218 +85,228 @@ __device__ __forceinline__ void norm_rope8(float (&f)[8], const uint16_t* __rest
   for (int e = 0; e < 8; ++e) f[e] = f[e] * cs[e] + sgn * o[e] * sn[e];
 }
 
-__global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict__ qkv,
-                                                     const uint16_t* __restrict__ q_norm,
-                                                     const uint16_t* __restrict__ k_norm,
-                                                     const float* __restrict__ rope_cos,
-                                                     const float* __restrict__ rope_sin,
-                                                     uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
-                                                     float* __restrict__ part, int* __restrict__ counters,
-                                                     uint16_t* __restrict__ out, int max_seq,
-                                                     const int32_t* __restrict__ pos_dev, int start, int n_split) {
-  __shared__ __attribute__((aligned(16))) float sc[2][DEC_SUB];
-  __shared__ float red[4][2][D];
-  __shared__ float stat[2][8];
-  __shared__ float vnew[D];
+__global__ __launch_bounds__(256, 2) void k_attn_decode(const uint16_t* __restrict__ qkv,
+                                                        const uint16_t* __restrict__ q_norm,
+                                                        const uint16_t* __restrict__ k_norm,
+                                                        const float* __restrict__ rope_cos,
+                                                        const float* __restrict__ rope_sin,
+                                                        uint16_t* __restrict__ k_cache,
+                                                        uint16_t* __restrict__ v_cache, float* __restrict__ part,
+                                                        int* __restrict__ counters, uint16_t* __restrict__ out,
+                                                        int max_seq, const int32_t* __restrict__ pos_dev, int start,
+                                                        int n_split) {
+  __shared__ __attribute__((aligned(16))) uint16_t qs[4][2][D];  // per wave: rotated q of heads 2g, 2g+1
+  __shared__ __attribute__((aligned(16))) uint16_t knew[4][D];   // per wave: the new key (rotated)
+  __shared__ __attribute__((aligned(16))) uint16_t vnew[4][D];   // per wave: the new value
+  __shared__ float wo[4][2][D];
+  __shared__ float wml[4][2][2];
   __shared__ float mls[2][DEC_SPLIT_CAP][2];
   __shared__ int last_ticket;
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, col = l & 15, grp = l >> 4;
   const int p = pos_dev ? pos_dev[b] : start;
   int n = p + 1;
   n = n < max_seq ? n : max_seq;
   n = n > 0 ? n : 0;
-  const int cs = (((n + n_split - 1) / n_split) + 15) & ~15;
+  const int cs = (((n + n_split - 1) / n_split) + DT - 1) & ~(DT - 1);
   const int k0 = s * cs;
   const int k1 = (k0 + cs) < n ? (k0 + cs) : n;
   const bool own = p >= k0 && p < k1;  // this split holds the new token (then p < n <= max_seq)
-  const int p_own = own ? p : -1;
-  const int kc_end = own ? p : k1;     // keys read from the cache: k0 .. kc_end-1
+  const int n_tile = k1 > k0 ? (k1 - k0 + DT - 1) / DT : 0;
+  const int last_key = k1 - 1, last_blk = (k1 - 1) & ~7;
 
-  // ---- q (and, for the owner, k and v) of the new token
-  const int j = l & 15, d0 = 8 * j, krow = l >> 4;
-  const int pc = p < 0 ? 0 : (p >= MAXPOS ? MAXPOS - 1 : p);
-  const float* cos_row = rope_cos + (size_t)pc * ROPE_HALF;
-  const float* sin_row = rope_sin + (size_t)pc * ROPE_HALF;
-  const uint16_t* qrow = qkv + (size_t)b * QKV_N;
-  float qf0[8], qf1[8];
-  load_row8(qrow + (2 * g) * D + d0, qf0);
-  load_row8(qrow + (2 * g + 1) * D + d0, qf1);
-  norm_rope8(qf0, q_norm, cos_row, sin_row, j);
-  norm_rope8(qf1, q_norm, cos_row, sin_row, j);
-  const float sl2 = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
-  float s_new0 = 0.f, s_new1 = 0.f;
-  if (own) {
-    float kf[8], vf[8];
-    load_row8(qrow + QDIM + g * D + d0, kf);
-    load_row8(qrow + QDIM + HKV * D + g * D + d0, vf);
-    norm_rope8(kf, k_norm, cos_row, sin_row, j);
-    u32x4 kb;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) kb[e] = pack_bf2(kf[2 * e], kf[2 * e + 1]);
-    // the score uses the key exactly as the cache will hold it
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      kf[2 * e] = bf_lo(kb[e]);
-      kf[2 * e + 1] = bf_hi(kb[e]);
-    }
-    float d0s = 0.f, d1s = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      d0s += qf0[e] * kf[e];
-      d1s += qf1[e] * kf[e];
-    }
-    s_new0 = row16_sum(d0s) * sl2;
-    s_new1 = row16_sum(d1s) * sl2;
-    if (w == 0 && l < 16) {
-      const size_t head_base = ((size_t)b * HKV + g) * max_seq * D;
-      *reinterpret_cast<u32x4*>(k_cache + head_base + (size_t)p * D + d0) = kb;
-      const u32x4 vb = *reinterpret_cast<const u32x4*>(qrow + QDIM + HKV * D + g * D + d0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v_cache[head_base + vblk_index(p, d0 + 2 * e)] = (uint16_t)(vb[e] & 0xffffu);
-        v_cache[head_base + vblk_index(p, d0 + 2 * e + 1)] = (uint16_t)(vb[e] >> 16);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vnew[d0 + e] = vf[e];
-    }
+  const size_t head_base = ((size_t)b * HKV + g) * max_seq * D;
+  const uint16_t* kbase = k_cache + head_base;
+  const uint16_t* vbase = v_cache + head_base;
+
+  // key of A row `col` in score chain `set`: 8*(col/4) + 4*set + col%4 (see the header)
+  const int krel0 = 8 * (col >> 2) + (col & 3);
+  u32x4 ka[8], va[8], kn[8], vn[8];
+#define Q3_DEC_LOAD_TILE(T, KR, VR)                                                        \
+  {                                                                                        \
+    const int tb_ = k0 + (T) * DT;                                                         \
+    _Pragma("unroll") for (int set = 0; set < 2; ++set) {                                  \
+      int key = tb_ + krel0 + 4 * set;                                                     \
+      key = key < last_key ? key : last_key;                                               \
+      const uint16_t* kp = kbase + (size_t)key * D + 8 * grp;                              \
+      _Pragma("unroll") for (int st = 0; st < 4; ++st) KR[4 * set + st] =                  \
+          *reinterpret_cast<const u32x4*>(kp + 32 * st);                                   \
+    }                                                                                      \
+    int pb_ = tb_ + 8 * grp;                                                               \
+    pb_ = pb_ < last_blk ? pb_ : last_blk;                                                 \
+    const uint16_t* vp = vbase + (size_t)pb_ * D + col * VBLK;                             \
+    _Pragma("unroll") for (int db = 0; db < 8; ++db) VR[db] =                              \
+        *reinterpret_cast<const u32x4*>(vp + 16 * db * VBLK);                              \
   }
 
-  const uint16_t* kbase = k_cache + ((size_t)b * HKV + g) * max_seq * D + d0;
-  const uint16_t* vbase = v_cache + ((size_t)b * HKV + g) * max_seq * D + 2 * l * VBLK;
+  int t = w;
+  if (n_tile > 0) {
+    const int t0 = t < n_tile ? t : n_tile - 1;
+    Q3_DEC_LOAD_TILE(t0, ka, va);
+  }
 
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-  // acc[h][e]: head 2g+h, dim 2l+e
-  float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-  float vn[2] = {0.f, 0.f};
-  bool vn_loaded = false;
-
-  for (int c0 = k0; c0 < k1; c0 += DEC_SUB) {
-    const int c1 = (c0 + DEC_SUB) < k1 ? (c0 + DEC_SUB) : k1;
-    const int c1c = c1 < kc_end ? c1 : kc_end;  // cache keys of this sub-chunk end here
-    // ---- pass 1: scores for keys c0..c1c-1 from the cache, the new key from registers
-    for (int base = c0; base < c1c; base += 64) {
-      u32x4 kv[4];
+  // ---- the new token: rows of the wave hold q(2g), q(2g+1), k(g), v(g); lane j dims 8j..8j+7
+  {
+    const int pc = p < 0 ? 0 : (p >= MAXPOS ? MAXPOS - 1 : p);
+    const uint16_t* row = qkv + (size_t)b * QKV_N +
+                          (grp < 2 ? (2 * g + grp) * D : (grp == 2 ? QDIM + g * D : QDIM + HKV * D + g * D));
+    float f[8];
+    load_row8(row + 8 * col, f);
+    float r[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        int key = base + 16 * u + 4 * w + krow;
-        key = key < c1c ? key : c1c - 1;
-        kv[u] = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * D);
-      }
+    for (int e = 0; e < 8; ++e) r[e] = f[e];
+    norm_rope8(r, grp < 2 ? q_norm : k_norm, rope_cos + (size_t)pc * ROPE_HALF, rope_sin + (size_t)pc * ROPE_HALF,
+               col);
+    u32x4 pk;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float d0s = 0.f, d1s = 0.f;
+    for (int e = 0; e < 4; ++e)
+      pk[e] = grp < 3 ? pack_bf2(r[2 * e], r[2 * e + 1]) : pack_bf2(f[2 * e], f[2 * e + 1]);
+    uint16_t* dst = grp < 2 ? &qs[w][grp][0] : (grp == 2 ? &knew[w][0] : &vnew[w][0]);
+    *reinterpret_cast<u32x4*>(dst + 8 * col) = pk;
+    if (own && w == 0) {
+      if (grp == 2) *reinterpret_cast<u32x4*>(k_cache + head_base + (size_t)p * D + 8 * col) = pk;
+      if (grp == 3) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float x0 = bf_lo(kv[u][e]), x1 = bf_hi(kv[u][e]);
-          d0s += x0 * qf0[2 * e] + x1 * qf0[2 * e + 1];
-          d1s += x0 * qf1[2 * e] + x1 * qf1[2 * e + 1];
-        }
-        d0s = row16_sum(d0s);
-        d1s = row16_sum(d1s);
-        const int key = base + 16 * u + 4 * w + krow;
-        if (key < c1c) {
-          if (j == 0) sc[0][key - c0] = d0s * sl2;
-          if (j == 1) sc[1][key - c0] = d1s * sl2;
+          v_cache[head_base + vblk_index(p, 8 * col + 2 * e)] = (uint16_t)(pk[e] & 0xffffu);
+          v_cache[head_base + vblk_index(p, 8 * col + 2 * e + 1)] = (uint16_t)(pk[e] >> 16);
         }
       }
     }
-    if (p_own >= c0 && p_own < c1 && tid == 0) {
-      sc[0][p_own - c0] = s_new0;
-      sc[1][p_own - c0] = s_new1;
-    }
-    __syncthreads();
-    if (!vn_loaded) {  // vnew is visible after the first barrier
-      vn[0] = vnew[2 * l];
-      vn[1] = vnew[2 * l + 1];
-      vn_loaded = true;
-    }
-    // ---- sub-chunk max per head (threads 0..127 head 0, 128..255 head 1)
-    const int hh = tid >> 7, ti = tid & 127;
-    const int cnt = c1 - c0;
-    float mx = -INFINITY;
-    for (int i = ti; i < cnt; i += 128) mx = fmaxf(mx, sc[hh][i]);
-    mx = wave_max(mx);
-    if (l == 0) stat[hh][w & 1] = mx;
-    __syncthreads();
-    float m_new[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) m_new[h] = fmaxf(m_run[h], fmaxf(stat[h][0], stat[h][1]));
-    float ls = 0.f;
-    for (int i = ti; i < cnt; i += 128) {
-      const float pv = __builtin_amdgcn_exp2f(sc[hh][i] - m_new[hh]);
-      sc[hh][i] = pv;
-      ls += pv;
-    }
-    ls = wave_sum(ls);
-    if (l == 0) stat[hh][2 + (w & 1)] = ls;
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_new[h]);
-      l_run[h] = l_run[h] * alpha + stat[h][2] + stat[h][3];
-      m_run[h] = m_new[h];
-      acc[h][0] *= alpha;
-      acc[h][1] *= alpha;
-    }
-    // ---- pass 2: acc += p * V, one 8-position block per wave step
-    for (int blk0 = c0 + 8 * w; blk0 < c1; blk0 += 64) {
-      u32x4 vv[2][2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int pb = blk0 + 32 * u;
-        if (pb < c1) {
-          const uint16_t* src = vbase + (size_t)pb * D;
-          vv[u][0] = *reinterpret_cast<const u32x4*>(src);
-          vv[u][1] = *reinterpret_cast<const u32x4*>(src + VBLK);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int pb = blk0 + 32 * u;
-        if (pb >= c1) continue;
-        const int valid = c1 - pb;  // positions beyond the range get p = 0 and a zeroed value
-        float pr[2][8];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const f32x4 a = *reinterpret_cast<const f32x4*>(&sc[h][pb - c0]);
-          const f32x4 bq = *reinterpret_cast<const f32x4*>(&sc[h][pb - c0 + 4]);
-          pr[h][0] = a.x; pr[h][1] = a.y; pr[h][2] = a.z; pr[h][3] = a.w;
-          pr[h][4] = bq.x; pr[h][5] = bq.y; pr[h][6] = bq.z; pr[h][7] = bq.w;
-        }
-        const int knew = p_own - pb;  // slot of the new token in this block, if any
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const uint32_t word = vv[u][e][k >> 1];
-            float x = (k & 1) ? bf_hi(word) : bf_lo(word);
-            x = k == knew ? vn[e] : x;
-            x = k < valid ? x : 0.f;
-            acc[0][e] += (k < valid ? pr[0][k] : 0.f) * x;
-            acc[1][e] += (k < valid ? pr[1][k] : 0.f) * x;
-          }
-      }
-    }
-    __syncthreads();  // sc is rewritten by the next sub-chunk
   }
-
-  // ---- reduce acc over the 4 waves, store this split's (o, m, l)
+  // q as the B operand: column col (heads 0, 1 only), dims 32*st + 8*grp .. +7
+  u32x4 qop[4];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    red[w][h][2 * l] = acc[h][0];
-    red[w][h][2 * l + 1] = acc[h][1];
+  for (int st = 0; st < 4; ++st)
+    qop[st] = col < 2 ? *reinterpret_cast<const u32x4*>(&qs[w][col & 1][32 * st + 8 * grp]) : u32x4{0u, 0u, 0u, 0u};
+
+  const float sl2 = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 oacc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (; t < n_tile; t += 4) {
+    {  // prefetch the wave's next tile (clamped, so the load count per iteration is fixed)
+      int tn = t + 4;
+      tn = tn < n_tile ? tn : n_tile - 1;
+      Q3_DEC_LOAD_TILE(tn, kn, vn);
+    }
+    const int tb = k0 + t * DT;
+    if (own && p - tb < DT) {  // the tile holding the new token: take it from LDS (wave-uniform branch)
+#pragma unroll
+      for (int set = 0; set < 2; ++set)
+        if (tb + krel0 + 4 * set == p)
+#pragma unroll
+          for (int st = 0; st < 4; ++st) ka[4 * set + st] = *reinterpret_cast<const u32x4*>(&knew[w][32 * st + 8 * grp]);
+      const int slot = p - tb - 8 * grp;
+      if (slot >= 0 && slot < 8) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const uint32_t vbits = vnew[w][16 * db + col];
+          const int e = slot >> 1;
+          const uint32_t keep = (slot & 1) ? 0x0000ffffu : 0xffff0000u;
+          const uint32_t put = (slot & 1) ? (vbits << 16) : vbits;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (q == e) va[db][q] = (va[db][q] & keep) | put;
+        }
+      }
+    }
+    const bool tail = tb + DT > k1;
+    if (tail) {  // positions at or past the range end: zero V (the cache may hold anything there)
+      const int valid = k1 - tb - 8 * grp;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t keep = (2 * e + 1 < valid) ? 0xffffffffu : ((2 * e < valid) ? 0x0000ffffu : 0u);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) va[db][e] &= keep;
+      }
+    }
+    // ---- scores of keys tb + 8*grp + j, j = 0..7, head col
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[st]), as_bf16x8(qop[st]), sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[4 + st]), as_bf16x8(qop[st]), sb, 0, 0, 0);
+    }
+    float sv[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float x = sv[j] * sl2;
+      if (tail && tb + 8 * grp + j >= k1) x = -INFINITY;
+      sv[j] = x;
+      mx = fmaxf(mx, x);
+    }
+    // ---- lazy online softmax: raise the running max only past the slack
+    if (__ballot(col < 2 && mx > m_run + DEC_RESCALE_SLACK)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    u32x4 pb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = __builtin_amdgcn_exp2f(sv[2 * e] - m_run);
+      const float p1 = __builtin_amdgcn_exp2f(sv[2 * e + 1] - m_run);
+      l_run += p0 + p1;
+      pb[e] = pack_bf2(p0, p1);
+    }
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[db]), as_bf16x8(pb), oacc[db], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ka[i] = kn[i];
+      va[i] = vn[i];
+    }
+  }
+#undef Q3_DEC_LOAD_TILE
+
+  // ---- combine the 4 waves: lane (grp, col < 2) holds dims 16*db + 4*grp + i of head col
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (col < 2) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wo[w][col][16 * db + 4 * grp + i] = oacc[db][i];
+    if (grp == 0) {
+      wml[w][col][0] = m_run;
+      wml[w][col][1] = l_run;
+    }
   }
   __syncthreads();
   const int hh = tid >> 7, d = tid & 127;
   {
-    const float o = red[0][hh][d] + red[1][hh][d] + red[2][hh][d] + red[3][hh][d];
+    float mm = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) mm = fmaxf(mm, wml[ww][hh][0]);
+    float o = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float mw = wml[ww][hh][0];
+      const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - mm);
+      o += f * wo[ww][hh][d];
+      lsum += f * wml[ww][hh][1];
+    }
+    if (n_split == 1) {  // a single split is already the whole softmax
+      out[(size_t)b * QDIM + (2 * g + hh) * D + d] = (uint16_t)f2bf(o / lsum);
+      return;
+    }
     float* dst = part + (((size_t)b * HQ + 2 * g + hh) * n_split + s) * PART_STRIDE;
     st_dev(dst + d, o);
     if (d == 0) {
-      st_dev(dst + D, m_run[hh]);
-      st_dev(dst + D + 1, l_run[hh]);
+      st_dev(dst + D, mm);
+      st_dev(dst + D + 1, lsum);
     }
   }
 

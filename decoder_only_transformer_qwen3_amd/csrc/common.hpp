@@ -19,6 +19,12 @@ constexpr int QKV_N = (HQ + 2 * HKV) * D;  // 4096
 constexpr int QDIM = HQ * D;               // 2048
 constexpr int ROPE_HALF = D / 2;           // 64 table columns
 constexpr float EPS = 1e-6f;
+// The norm folded into a projection gets, per residual row, partial sums of
+// squares: NSQ (one per 4 columns) when at most 8 rows are in flight (the
+// VALU GEMV writes one per 4-column workgroup), NSQ_BLK (one per 16
+// columns) otherwise (fewer for the consumers to read).
+constexpr int NSQ = C / 4;
+constexpr int NSQ_BLK = C / 16;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -31,6 +37,11 @@ __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w <<
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// a.lo * b.lo + a.hi * b.hi + c on packed bf16 pairs (v_dot2c_f32_bf16)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
 
 // float32 -> bfloat16 (round to nearest even, NaN stays NaN); gfx950 does
 // this in hardware (v_cvt_pk_bf16_f32).

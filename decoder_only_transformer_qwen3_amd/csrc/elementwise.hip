@@ -10,26 +10,30 @@ namespace q3 {
 // ---------------------------------------------------------------- embedding
 // x = E[id] with no scaling ("手写Qwen3-0.6B推理" §Qwen3Model), plus, when a
 // gain is given, the operand of the first layer's norm-folded projection:
-// hg = bf16(gamma * x) and the per-16-column sums of squares ssq[m][64]
-// (the GEMM applies 1 / rms(x) itself).  One wave per token; lane l owns
-// columns 16l .. 16l+15, i.e. column block l.  Block 0 also clears the
-// call's workgroup tickets.
+// hg = bf16(gamma * x) and the sums of squares per 4 columns (ssq[m][256])
+// or per 16 columns (ssq[m][64]) (the GEMM applies 1 / rms(x) itself).  One
+// wave per token; lane l owns columns 16l .. 16l+15.  Block 0 also clears
+// the call's workgroup tickets.
 __device__ __forceinline__ void norm_operand_row(const float (&x)[16], int lane, const uint16_t* __restrict__ gamma,
-                                                 uint16_t* __restrict__ hg_row, float* __restrict__ ssq_row) {
+                                                 uint16_t* __restrict__ hg_row, float* __restrict__ ssq_row,
+                                                 int nsq) {
   const u32x4* gp = reinterpret_cast<const u32x4*>(gamma + 16 * lane);
   const u32x4 g0 = gp[0], g1 = gp[1];
   const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
   u32x4 o[2];
-  float ss = 0.f;
+  f32x4 ss = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     o[e >> 2][e & 3] = pack_bf2(x[2 * e] * bf_lo(gw[e]), x[2 * e + 1] * bf_hi(gw[e]));
-    ss += x[2 * e] * x[2 * e] + x[2 * e + 1] * x[2 * e + 1];
+    ss[e >> 1] += x[2 * e] * x[2 * e] + x[2 * e + 1] * x[2 * e + 1];
   }
   u32x4* dst = reinterpret_cast<u32x4*>(hg_row + 16 * lane);
   dst[0] = o[0];
   dst[1] = o[1];
-  ssq_row[lane] = ss;
+  if (nsq == NSQ)
+    *reinterpret_cast<f32x4*>(ssq_row + 4 * lane) = ss;
+  else
+    ssq_row[lane] = (ss.x + ss.y) + (ss.z + ss.w);
 }
 
 __device__ __forceinline__ void clear_tickets(int* counters, int n) {
@@ -39,7 +43,7 @@ __device__ __forceinline__ void clear_tickets(int* counters, int n) {
 
 __global__ __launch_bounds__(256) void k_embed(const int32_t* __restrict__ ids, const uint16_t* __restrict__ E,
                                                float* __restrict__ resid, int M, const uint16_t* __restrict__ gamma,
-                                               uint16_t* __restrict__ hg, float* __restrict__ ssq,
+                                               uint16_t* __restrict__ hg, float* __restrict__ ssq, int nsq,
                                                int* __restrict__ counters, int n_counters) {
   clear_tickets(counters, n_counters);
   const int lane = threadIdx.x & 63;
@@ -59,20 +63,20 @@ __global__ __launch_bounds__(256) void k_embed(const int32_t* __restrict__ ids, 
   f32x4* dst = reinterpret_cast<f32x4*>(resid + (size_t)m * C + 16 * lane);
 #pragma unroll
   for (int i = 0; i < 4; ++i) dst[i] = f32x4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
-  if (gamma) norm_operand_row(x, lane, gamma, hg + (size_t)m * C, ssq + (size_t)m * 64);
+  if (gamma) norm_operand_row(x, lane, gamma, hg + (size_t)m * C, ssq + (size_t)m * nsq, nsq);
 }
 
 void launch_embed(const int32_t* ids, const uint16_t* E, float* resid, int M, const uint16_t* gamma, uint16_t* hg,
-                  float* ssq, int* counters, int n_counters, hipStream_t s) {
-  hipLaunchKernelGGL(k_embed, dim3((M + 3) / 4), dim3(256), 0, s, ids, E, resid, M, gamma, hg, ssq, counters,
+                  float* ssq, int nsq, int* counters, int n_counters, hipStream_t s) {
+  hipLaunchKernelGGL(k_embed, dim3((M + 3) / 4), dim3(256), 0, s, ids, E, resid, M, gamma, hg, ssq, nsq, counters,
                      n_counters);
 }
 
 // Norm-folded operand of n_rows residual rows (row r of the output reads
-// resid row r*row_step + row_off): hg[r] = bf16(gamma * x), ssq[r][64].
+// resid row r*row_step + row_off): hg[r] = bf16(gamma * x), ssq[r][nsq].
 __global__ __launch_bounds__(256) void k_norm_operand(const float* __restrict__ resid, int n_rows, int row_step,
                                                       int row_off, const uint16_t* __restrict__ gamma,
-                                                      uint16_t* __restrict__ hg, float* __restrict__ ssq,
+                                                      uint16_t* __restrict__ hg, float* __restrict__ ssq, int nsq,
                                                       int* __restrict__ counters, int n_counters) {
   clear_tickets(counters, n_counters);
   const int lane = threadIdx.x & 63;
@@ -88,14 +92,14 @@ __global__ __launch_bounds__(256) void k_norm_operand(const float* __restrict__ 
     x[4 * i + 2] = v.z;
     x[4 * i + 3] = v.w;
   }
-  norm_operand_row(x, lane, gamma, hg + (size_t)r * C, ssq + (size_t)r * 64);
+  norm_operand_row(x, lane, gamma, hg + (size_t)r * C, ssq + (size_t)r * nsq, nsq);
 }
 
 void launch_norm_operand(const float* resid, int n_rows, int row_step, int row_off, const uint16_t* gamma,
-                         uint16_t* hg, float* ssq, int* counters, int n_counters, hipStream_t s) {
+                         uint16_t* hg, float* ssq, int nsq, int* counters, int n_counters, hipStream_t s) {
   const int blocks = n_rows > 0 ? (n_rows + 3) / 4 : 1;  // one block still clears the tickets
   hipLaunchKernelGGL(k_norm_operand, dim3(blocks), dim3(256), 0, s, resid, n_rows, row_step, row_off,
-                     gamma, hg, ssq, counters, n_counters);
+                     gamma, hg, ssq, nsq, counters, n_counters);
 }
 
 // ---------------------------------------------------------------- RMSNorm

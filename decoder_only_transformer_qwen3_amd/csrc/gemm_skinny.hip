@@ -19,8 +19,8 @@
 //
 // Input RMSNorm folded into the GEMM ("手写Qwen3-0.6B推理" §Qwen3RMSNorm):
 // with h = gamma * r / rms(r), h W^T = (1 / rms(r)) * ((gamma * r) W^T), so
-// the producer of r stores X = bf16(gamma * r) and, per 16-column block j,
-// ssq[m][j] = sum of r^2 over the block; this kernel multiplies each output
+// the producer of r stores X = bf16(gamma * r) and, per 4-column group j,
+// ssq[m][j] = sum of r^2 over the group; this kernel multiplies each output
 // row by 1 / sqrt(sum_j ssq[m][j] / 1024 + eps) in the epilogue.
 //
 // Split-K with an in-kernel finish (EPI_PARTIAL with a residual): every
@@ -40,9 +40,9 @@ __device__ __forceinline__ bool am_better2(float a, int ia, float b, int ib) {
   return a > b || (a == b && ia < ib);
 }
 
-template <int NB, int EPI, int U>
-__global__ __launch_bounds__(256) void k_gemm_skinny(SkinnyArgs a) {
-  __shared__ float red[4][NB * 16][17];
+template <int NB, int EPI, int U, int WV>
+__global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
+  __shared__ float red[WV][NB * 16][17];
   __shared__ float rsc[NB * 16];
   __shared__ int last_ticket;
   const uint16_t* __restrict__ X = a.X;
@@ -59,14 +59,23 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkinnyArgs a) {
   } else {
     wrow = rb * 16 + r;
   }
-  // norm statistics are loaded first so their latency hides behind the weight stream
-  const int sm = t >> 2;  // row whose 16 of 64 block sums this thread reads
-  f32x4 sq[4] = {};
-  const bool scaled = a.ssq != nullptr;
-  if (scaled && sm < M) {
-    const f32x4* sp = reinterpret_cast<const f32x4*>(a.ssq + (size_t)sm * a.ssq_ld + 16 * (t & 3));
+  // norm statistics are loaded first so their latency hides behind the
+  // weight stream: SG threads share a row, each reading NSQ / SG partials
+  // (a.ssq_n is NSQ only for up to 8 rows, so SQV below covers both layouts)
+  constexpr int SG = NB == 1 ? 16 : (NB == 2 ? 8 : 4);
+  constexpr int SQV = NB == 1 ? NSQ / SG / 4 : NSQ_BLK / SG / 4;
+  const int sqv = a.ssq_n / (SG * 4);
+  const int sm = t / SG;
+  f32x4 sq[SQV];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sq[i] = sp[i];
+  for (int i = 0; i < SQV; ++i) sq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool scaled = a.ssq != nullptr;
+  if (scaled && t < 256 && sm < M) {
+    // a fixed number of loads (no per-load branch, so the compiler keeps the
+    // weight loads in flight); slots past sqv reload slot 0 and are ignored
+    const f32x4* sp = reinterpret_cast<const f32x4*>(a.ssq + (size_t)sm * a.ssq_ld + (t % SG) * (4 * sqv));
+#pragma unroll
+    for (int i = 0; i < SQV; ++i) sq[i] = sp[i < sqv ? i : 0];
   }
   const size_t k_base = (size_t)split * kspan + qd * 8;
   const uint16_t* wp = W + (size_t)wrow * K + k_base;
@@ -82,15 +91,16 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkinnyArgs a) {
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = kspan >> 5;  // 32-wide k-steps in this workgroup's range
-  for (int s0 = w; s0 < nsteps; s0 += 4 * U) {
+  for (int s0 = w; s0 < nsteps; s0 += WV * U) {
     u32x4 wa[U];
     u32x4 bx[U][NB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) wa[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + (size_t)(s0 + 4 * u) * 32));
+    for (int u = 0; u < U; ++u) wa[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + (size_t)(s0 + WV * u) * 32));
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) bx[u][nb] = *reinterpret_cast<const u32x4*>(xp[nb] + (size_t)(s0 + 4 * u) * 32);
+      for (int nb = 0; nb < NB; ++nb) bx[u][nb] = *reinterpret_cast<const u32x4*>(xp[nb] + (size_t)(s0 + WV * u) * 32);
+    __builtin_amdgcn_sched_barrier(0);  // every load of the step is in flight before the first MFMA waits
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -104,10 +114,10 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkinnyArgs a) {
   if (scaled) {
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ss += (sq[i].x + sq[i].y) + (sq[i].z + sq[i].w);
-    ss += __shfl_xor(ss, 1, 64);
-    ss += __shfl_xor(ss, 2, 64);
-    if ((t & 3) == 0 && sm < NB * 16) rsc[sm] = 1.0f / sqrtf(ss * (1.0f / C) + EPS);
+    for (int i = 0; i < SQV; ++i) ss += i < sqv ? (sq[i].x + sq[i].y) + (sq[i].z + sq[i].w) : 0.f;
+#pragma unroll
+    for (int o = 1; o < SG; o <<= 1) ss += __shfl_xor(ss, o, 64);
+    if (t < 256 && (t % SG) == 0 && sm < NB * 16) rsc[sm] = 1.0f / sqrtf(ss * (1.0f / C) + EPS);
   }
   __syncthreads();
   if constexpr (EPI == EPI_SILU) {
@@ -116,8 +126,14 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkinnyArgs a) {
       const int m = e >> 3, j = e & 7;
       if (m >= M) continue;
       const float rs = scaled ? rsc[m] : 1.0f;
-      const float gsum = (red[0][m][j] + red[1][m][j] + red[2][m][j] + red[3][m][j]) * rs;
-      const float usum = (red[0][m][8 + j] + red[1][m][8 + j] + red[2][m][8 + j] + red[3][m][8 + j]) * rs;
+      float gsum = 0.f, usum = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < WV; ++ww) {
+        gsum += red[ww][m][j];
+        usum += red[ww][m][8 + j];
+      }
+      gsum *= rs;
+      usum *= rs;
       const float sg = gsum / (1.0f + __expf(-gsum));
       reinterpret_cast<uint16_t*>(a.out)[(size_t)m * a.ldo + rb * 8 + j] = (uint16_t)f2bf(sg * usum);
     }
@@ -125,9 +141,11 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkinnyArgs a) {
     if (t < NB * 16 * 4) {
       const int m = t >> 2, ng = t & 3;
       if (m < M) {  // whole groups of 4 lanes share m, so the shuffles below stay inside active groups
-        f32x4 v;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = red[0][m][4 * ng + i] + red[1][m][4 * ng + i] + red[2][m][4 * ng + i] + red[3][m][4 * ng + i];
+        for (int ww = 0; ww < WV; ++ww)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] += red[ww][m][4 * ng + i];
         if (scaled) v *= rsc[m];
         const int n = rb * 16 + 4 * ng;
         void* const out = a.out;
@@ -165,7 +183,23 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkinnyArgs a) {
           }
         } else if constexpr (EPI == EPI_ADD_F32) {
           f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)m * ldo + n);
-          *dst = *dst + v;
+          v = *dst + v;
+          *dst = v;
+          if (a.gamma) {  // the next norm's operand for this residual row (N == ldo == 1024)
+            const u32x2 g = *reinterpret_cast<const u32x2*>(a.gamma + n);
+            u32x2 o;
+            o.x = pack_bf2(v.x * bf_lo(g.x), v.y * bf_hi(g.x));
+            o.y = pack_bf2(v.z * bf_lo(g.y), v.w * bf_hi(g.y));
+            *reinterpret_cast<u32x2*>(a.hg + (size_t)m * N + n) = o;
+            float ss = (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+            if (a.ssq_n == NSQ) {
+              a.ssq_out[(size_t)m * NSQ + 4 * rb + ng] = ss;
+            } else {
+              ss += __shfl_xor(ss, 1, 64);  // the 4 lanes of row m are whole and active
+              ss += __shfl_xor(ss, 2, 64);
+              if (ng == 0) a.ssq_out[(size_t)m * NSQ_BLK + rb] = ss;
+            }
+          }
         } else {  // EPI_PARTIAL (device-coherent stores: the last workgroup of the block reads them)
           float* pp = reinterpret_cast<float*>(out) + ((size_t)split * M + m) * N + n;
 #pragma unroll
@@ -204,23 +238,120 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkinnyArgs a) {
           ss = (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
         }
       }
-      // groups of 4 lanes share m and are whole inside the wave
-      ss += __shfl_xor(ss, 1, 64);
-      ss += __shfl_xor(ss, 2, 64);
-      if (a.gamma && m < M && ng == 0) a.ssq_out[(size_t)m * 64 + rb] = ss;
+      if (a.gamma) {
+        if (a.ssq_n == NSQ) {
+          if (m < M) a.ssq_out[(size_t)m * NSQ + 4 * rb + ng] = ss;
+        } else {
+          ss += __shfl_xor(ss, 1, 64);  // groups of 4 lanes share m and are whole inside the wave
+          ss += __shfl_xor(ss, 2, 64);
+          if (m < M && ng == 0) a.ssq_out[(size_t)m * NSQ_BLK + rb] = ss;
+        }
+      }
     }
     if (t == 0) a.counters[rb] = 0;  // ready for the next call
   }
 }
 
+// ---------------------------------------------------------------------------
+// Residual projection for up to 8 rows: r[m][n] += sum_k X[m][k] W[n][k].
+// One wave per output column n (4 per workgroup, N / 4 workgroups, so every
+// CU streams weights); lane l reads 16 B of the weight row per 512-wide
+// chunk, fully coalesced, and forms bf16 dot products with v_dot2c.  No K
+// split, so the workgroup finishes its columns itself: the residual update
+// and, with a gain, hg = bf16(gamma * r) and the 4-column sum of squares.
+template <int MR, int NCH>
+__global__ __launch_bounds__(256) void k_gemv_resid(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+                                                    float* __restrict__ resid, int M,
+                                                    const uint16_t* __restrict__ gamma, uint16_t* __restrict__ hg,
+                                                    float* __restrict__ ssq_out) {
+  constexpr int K = NCH * 512;
+  __shared__ float rsq[4][MR];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + w;
+  const uint16_t* wr = W + (size_t)n * K + 8 * l;
+  u32x4 wv[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) wv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr + 512 * i));
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = 0.f;
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    if (m < M) {
+      const uint16_t* xr = X + (size_t)m * K + 8 * l;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + 512 * i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[m] = dot2_bf16(wv[i][e], xv[e], acc[m]);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = wave_sum(acc[m]);
+  if (l == 0) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      if (m < M) {
+        float* rp = resid + (size_t)m * C + n;
+        const float r = *rp + acc[m];
+        *rp = r;
+        if (gamma) {
+          hg[(size_t)m * C + n] = (uint16_t)f2bf(r * bf2f(gamma[n]));
+          rsq[w][m] = r * r;
+        }
+      }
+    }
+  }
+  if (gamma) {
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < MR && t < M) ssq_out[(size_t)t * NSQ + blockIdx.x] = (rsq[0][t] + rsq[1][t]) + (rsq[2][t] + rsq[3][t]);
+  }
+}
+
+template <int MR>
+static void launch_gemv_mr(const uint16_t* X, const uint16_t* W, int K, float* resid, int M, const uint16_t* gamma,
+                           uint16_t* hg, float* ssq_out, hipStream_t s) {
+  const dim3 grid(C / 4), block(256);
+  switch (K) {
+    case 1024: hipLaunchKernelGGL((k_gemv_resid<MR, 2>), grid, block, 0, s, X, W, resid, M, gamma, hg, ssq_out); break;
+    case 2048: hipLaunchKernelGGL((k_gemv_resid<MR, 4>), grid, block, 0, s, X, W, resid, M, gamma, hg, ssq_out); break;
+    default: hipLaunchKernelGGL((k_gemv_resid<MR, 6>), grid, block, 0, s, X, W, resid, M, gamma, hg, ssq_out); break;
+  }
+}
+
+void launch_gemv_resid(const uint16_t* X, const uint16_t* W, int K, float* resid, int M, const uint16_t* gamma,
+                       uint16_t* hg, float* ssq_out, hipStream_t s) {
+  if (M <= 1) launch_gemv_mr<1>(X, W, K, resid, M, gamma, hg, ssq_out, s);
+  else if (M <= 2) launch_gemv_mr<2>(X, W, K, resid, M, gamma, hg, ssq_out, s);
+  else if (M <= 4) launch_gemv_mr<4>(X, W, K, resid, M, gamma, hg, ssq_out, s);
+  else launch_gemv_mr<8>(X, W, K, resid, M, gamma, hg, ssq_out, s);
+}
+
+template <int NB, int EPI, int WV>
+static void launch_wv(const SkinnyArgs& a, int gx, int n_split, hipStream_t s) {
+  const int nsteps = a.kspan >> 5;  // 32-wide k-steps per workgroup
+  if (NB <= 2 && nsteps % (WV * 12) == 0)
+    hipLaunchKernelGGL((k_gemm_skinny<NB, EPI, (NB <= 2 ? 12 : 4), WV>), dim3(gx, n_split), dim3(64 * WV), 0, s, a);
+  else if (nsteps % (WV * 8) == 0)
+    hipLaunchKernelGGL((k_gemm_skinny<NB, EPI, 8, WV>), dim3(gx, n_split), dim3(64 * WV), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_gemm_skinny<NB, EPI, 4, WV>), dim3(gx, n_split), dim3(64 * WV), 0, s, a);
+}
+
 template <int NB, int EPI>
 static void launch_nb(const SkinnyArgs& a, int n_split, hipStream_t s) {
   const int gx = (EPI == EPI_SILU) ? (a.N / 2) / 8 : a.N / 16;
-  // Each wave takes kspan/128 steps; unroll by 8 when that divides evenly.
-  if (((a.kspan >> 5) % 32) == 0)
-    hipLaunchKernelGGL((k_gemm_skinny<NB, EPI, 8>), dim3(gx, n_split), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_gemm_skinny<NB, EPI, 4>), dim3(gx, n_split), dim3(256), 0, s, a);
+  // The residual-add projections run one K range per 16 columns, so they use
+  // 8 waves per workgroup to keep enough weight bytes in flight.
+  if constexpr (EPI == EPI_ADD_F32) {
+    if (((a.kspan >> 5) % 32) == 0) {
+      launch_wv<NB, EPI, 8>(a, gx, n_split, s);
+      return;
+    }
+  }
+  launch_wv<NB, EPI, 4>(a, gx, n_split, s);
 }
 
 template <int EPI>

@@ -19,14 +19,15 @@ enum Epi : int {
 
 // x[m] = E[ids[m]] widened to f32 (one row of 1024 per token); with a gain
 // also hg[m] = bf16(gamma * x[m]) and ssq[m][j] = sum of x^2 over columns
-// 16j..16j+15.  The first n_counters ints of `counters` are set to zero.
+// group j (nsq = NSQ: 4 columns, NSQ_BLK: 16 columns).  The first
+// n_counters ints of `counters` are set to zero.
 void launch_embed(const int32_t* ids, const uint16_t* E, float* resid, int M, const uint16_t* gamma, uint16_t* hg,
-                  float* ssq, int* counters, int n_counters, hipStream_t s);
+                  float* ssq, int nsq, int* counters, int n_counters, hipStream_t s);
 
-// hg[r] = bf16(gamma * resid[r*row_step + row_off]) and ssq[r][64] for r < n_rows;
+// hg[r] = bf16(gamma * resid[r*row_step + row_off]) and ssq[r][nsq] for r < n_rows;
 // clears n_counters tickets.
 void launch_norm_operand(const float* resid, int n_rows, int row_step, int row_off, const uint16_t* gamma,
-                         uint16_t* hg, float* ssq, int* counters, int n_counters, hipStream_t s);
+                         uint16_t* hg, float* ssq, int nsq, int* counters, int n_counters, hipStream_t s);
 
 // For r < n_rows, row = r*row_step + row_off:
 //   resid[row] += sum_{j < n_part} part[j][row]      (written back when n_part > 0)
@@ -56,13 +57,16 @@ struct SkinnyArgs {
   int M, N, K, ldo, ldx, kspan;
   void* amax_part;    // EPI_LOGITS: per-16-column (max, argmax) of each row
   // Optional input-norm scale: X holds bf16(gamma * r); output row m is
-  // multiplied by 1 / sqrt(sum_{j<64} ssq[m * ssq_ld + j] / 1024 + eps).
+  // multiplied by 1 / sqrt(sum_{j<ssq_n} ssq[m * ssq_ld + j] / 1024 + eps).
+  // ssq_n (also the layout of ssq_out below) is NSQ for up to 8 rows, else NSQ_BLK.
   const float* ssq;
-  int ssq_ld;
+  int ssq_ld, ssq_n;
   // EPI_PARTIAL finish (N == 1024, resid != null): the last workgroup of
   // each 16-column block adds all K splits to resid [M][1024]; with a gain
-  // it also writes hg = bf16(gamma * r) [M][1024] and ssq_out [M][64].
+  // it also writes hg = bf16(gamma * r) [M][1024] and ssq_out [M][ssq_n].
   // counters: 64 ints, zero on entry and left zero on exit.
+  // EPI_ADD_F32 with a gain (N == ldo == 1024): after out += X W^T, the same
+  // hg and ssq_out of the updated rows.
   float* resid;
   const uint16_t* gamma;
   uint16_t* hg;
@@ -70,6 +74,11 @@ struct SkinnyArgs {
   int* counters;
 };
 void launch_gemm_skinny(SkinnyArgs a, int n_split, Epi epi, hipStream_t s);
+
+// resid[M][1024] += X[M][K] W[1024][K]^T for M <= 8, K in {1024, 2048, 3072};
+// with a gain also hg = bf16(gamma * r) and ssq_out [M][256].
+void launch_gemv_resid(const uint16_t* X, const uint16_t* W, int K, float* resid, int M, const uint16_t* gamma,
+                       uint16_t* hg, float* ssq_out, hipStream_t s);
 void launch_gemm_skinny(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo,
                         int n_split, Epi epi, hipStream_t s, void* amax_part = nullptr);
 

@@ -30,17 +30,19 @@ WsLayout ws_layout(int32_t batch, int32_t n_tokens) {
   L.logits = take((size_t)batch * Q3_VOCAB * 4);
   L.amax = take((size_t)batch * (Q3_VOCAB / 16) * 8);
   L.fh = take((size_t)batch * Q3_HIDDEN * 2);
-  L.ssq = take(M * 64 * 4);
+  L.ssq = take(M * (Q3_HIDDEN / 4) * 4);
   L.tick = take((size_t)ticket_count(batch) * 4);
   L.total = off;
   return L;
 }
 
 int decode_splits(int32_t batch, int32_t ctx) {
-  const int target_workgroups = 2048;
+  // about two workgroups per CU in one wave of launches, at least 256 keys
+  // (two 32-key tiles per wave) per split
+  const int target_workgroups = 512;
   const int pairs = batch * Q3_N_KV_HEADS;
   int s = (target_workgroups + pairs - 1) / pairs;
-  const int cap = (ctx + 63) / 64;
+  const int cap = (ctx + 255) / 256;
   if (s > cap) s = cap;
   if (s > DEC_SPLIT_MAX) s = DEC_SPLIT_MAX;
   if (s < 1) s = 1;

@@ -47,10 +47,11 @@ int main() {
   EXPECT_EQ(L1.resid % 256, 0); EXPECT_EQ(L1.h % 256, 0); EXPECT_EQ(L1.fh % 256, 0);
   EXPECT_EQ(L3.total >= (size_t)8 * 4096 * (1024 * 4 + 1024 * 2 + 4096 * 2 + 2048 * 4 + 3072 * 2), 1);
   // ---- decode splits
-  EXPECT_EQ(decode_splits(32, 2176), 8);
-  EXPECT_EQ(decode_splits(4, 32832), 64);
+  EXPECT_EQ(decode_splits(32, 2176), 2);
+  EXPECT_EQ(decode_splits(4, 32832), 16);
   EXPECT_EQ(decode_splits(1, 1), 1);
-  EXPECT_EQ(decode_splits(1, 192), 3);
+  EXPECT_EQ(decode_splits(1, 192), 1);
+  EXPECT_EQ(decode_splits(1, 40960), 64);
   for (int b = 1; b <= 64; ++b)
     for (int c = 1; c < 40961; c += 997) {
       const int s = decode_splits(b, c);
