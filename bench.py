@@ -12,10 +12,11 @@ positions, 128 steps), prefill-bound (8 x 4096) and long-context (batch 4,
 32768 cached positions, 64 steps) shapes; their setup prefill is untimed.
 
 Besides the JSON line's headline value, the script times the dominant
-kernel in isolation with HIP events on the stream it runs on (through the
-library's q3_linear entry point, same kernel and shape as inside the step)
-for the roofline object, and times the float64 CPU oracle on a bounded
-sample of the same workload for the cpu_baseline object.
+kernel alone with HIP events on the stream it runs on (through the
+library's helper entry points, same kernel, shape and launch configuration
+as inside the step) for the roofline object, reports the whole timed phase
+against the roofline (step_roofline), and times the float64 CPU oracle on a
+bounded sample of the same workload for the cpu_baseline object.
 """
 from __future__ import annotations
 
@@ -112,49 +113,118 @@ def capture(torch, fn):
     return g
 
 
-def dominant_kernel(torch, B, dev, dm, workload, iters):
-    """Time the dominant kernel alone with HIP events on the current stream.
+# Matmul parameters of one layer (merged q|k|v, o, merged gate|up, down) and
+# of the tied lm_head; the norm gains are negligible next to them.
+LAYER_MATMUL_PARAMS = 4096 * 1024 + 1024 * 2048 + 6144 * 1024 + 1024 * 3072
+LMHEAD_PARAMS = 151936 * 1024
+KV_BYTES_PER_POS = 28 * 8 * 128 * 2 * 2  # K and V rows of one position, all layers and KV heads
 
-    Decode workloads: the tied lm_head weight stream at the workload's batch
-    (skinny MFMA GEMM, HBM-bound); prefill: the gate/up projection with the
-    SiLU epilogue at M = batch * prompt_len (tiled MFMA GEMM, MFMA-bound)."""
-    batch, T, steps, _ = WORKLOADS[workload]
+
+def _time_launches(torch, fn, iters, reps=10):
+    """Average duration (s) of one fn() launch: `reps` back-to-back launches
+    are captured as one HIP graph, which is replayed between HIP events on
+    the current stream (the stream the kernels run on), so host launch
+    overhead does not enter short kernels' figures.  Falls back to eager
+    launches bracketed by events if capture is not possible."""
     stream = torch.cuda.current_stream()
-    if workload == "prefill_8x4096":
-        M, N, K = batch * T, 2 * B.INTER, B.HIDDEN
-        x = torch.randn((M, K), device="cuda").to(torch.bfloat16)
-        out = torch.empty((M, N // 2), dtype=torch.bfloat16, device="cuda")
-        w = dm.layers[0].w_gate_up
-        fn = lambda: B.q3_linear(x, w, out, M, N, K, N // 2, B.Q3_EPI_SILU_GATE)
-        flops = 2.0 * M * N * K
-        name, bound = "k_gemm_tiled<EPI_SILU> (gate_up, M=%d N=%d K=%d)" % (M, N, K), "mfma"
-        algo = flops
-    else:
-        M, N, K = batch, B.VOCAB, B.HIDDEN
-        x = torch.randn((M, K), device="cuda").to(torch.bfloat16)
-        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
-        w = dm.embed
-        fn = lambda: B.q3_linear(x, w, out, M, N, K, N, B.Q3_EPI_STORE_F32)
-        algo = float(N * K * 2 + M * K * 2 + M * N * 4)  # weights once + activations + logits
-        name, bound = "k_gemm_skinny<EPI_F32> (lm_head, M=%d N=%d K=%d)" % (M, N, K), "hbm"
-    for _ in range(5):
+    for _ in range(3):
         fn()
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * iters)]
-    for i in range(iters):
+    n_rep = max(1, iters // reps)
+    try:
+        g = capture(torch, lambda: [fn() for _ in range(reps)])
+        per_replay = reps
+        run = g.replay
+    except Exception:  # pragma: no cover
+        per_replay, run = 1, fn
+        n_rep = iters
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_rep)]
+    for i in range(n_rep):
         ev[2 * i].record(stream)
-        fn()
+        run()
         ev[2 * i + 1].record(stream)
     torch.cuda.synchronize()
-    durs = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(iters)]) * 1e-3  # s
-    t = float(np.mean(durs))
+    return float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n_rep)])) * 1e-3 / per_replay
+
+
+def dominant_kernel(torch, B, dev, dm, r, workload, iters):
+    """Roofline of the kernel that takes most of the workload's step time
+    (per the rocprofv3 kernel summaries), timed alone with HIP events on the
+    stream it runs on, at the workload's shape and launch configuration:
+
+    - batch-1 prefill + decode: the step is weight streaming; the largest
+      GEMV is the gate|up projection with its SiLU epilogue (M = 1);
+    - decode-bound and long-context decode: the decode attention kernel at
+      the middle position of the timed steps (KV streaming);
+    - 8 x 4096 prefill: the causal flash-attention kernel.
+    """
+    batch, T, steps, _ = WORKLOADS[workload]
+    if workload == "prefill128_decode64":
+        # one launch per layer's weights in turn (28 x 12.6 MB, more than the
+        # 256 MB last-level cache), so the weights stream from HBM as in the step
+        M, N, K = 1, 2 * B.INTER, B.HIDDEN
+        x = torch.randn((M, K), device="cuda").to(torch.bfloat16)
+        out = torch.empty((M, N // 2), dtype=torch.bfloat16, device="cuda")
+        ws_all = [lw.w_gate_up for lw in dm.layers]
+        cursor = [0]
+
+        def fn():
+            w = ws_all[cursor[0] % len(ws_all)]
+            cursor[0] += 1
+            B.q3_linear(x, w, out, M, N, K, N // 2, B.Q3_EPI_SILU_GATE)
+        algo = float(N * K * 2 + M * K * 2 + M * (N // 2) * 2)
+        name, bound, per = f"k_gemm_skinny<EPI_SILU> (gate|up, M={M} N={N} K={K})", "hbm", \
+            "weight bytes + activation bytes per launch"
+        iters = max(iters, 280)
+        reps = 28
+    elif workload in ("decode_b32_ctx2048", "decode_b4_ctx32768"):
+        reps = 10
+        p = T + steps // 2  # middle of the timed decode steps
+        qkv = torch.randn((batch, B.QKV_ROWS), device="cuda").to(torch.bfloat16)
+        pos = torch.full((batch,), p, dtype=torch.int32, device="cuda")
+        out = torch.empty((batch, B.N_HEADS * B.HEAD_DIM), dtype=torch.bfloat16, device="cuda")
+        lw = dm.layers[0]
+        kl, vl = r.kv.k[0], r.kv.v[0]
+        fn = lambda: B.q3_attention_decode(qkv, lw.q_norm, lw.k_norm, dm.rope_cos, dm.rope_sin, kl, vl, batch,
+                                           r.max_seq, pos, r.T + r.steps, out, r.ws_d, r.nb_d)
+        algo = float(batch * (p + 1) * 8 * 128 * 2 * 2 + batch * (B.QKV_ROWS + 2048) * 2)
+        name, bound, per = f"k_attn_decode (batch {batch}, position {p}, one layer)", "hbm", \
+            "K and V bytes of positions 0..p for every (sequence, KV head) + q|k|v in + out"
+    else:
+        reps = 10
+        q = torch.randn((batch, T, B.N_HEADS * B.HEAD_DIM), device="cuda").to(torch.bfloat16)
+        out = torch.empty_like(q)
+        kl, vl = r.kv.k[0], r.kv.v[0]
+        fn = lambda: B.q3_attention_prefill(q, kl, vl, batch, T, 0, r.max_seq, out)
+        algo = float(batch * (T * (T + 1) // 2) * 4 * B.HEAD_DIM * B.N_HEADS)
+        name, bound, per = f"k_attn_prefill ({batch} x {T}, one layer)", "mfma", \
+            "causal flops: 4 * 128 * 16 per (query, key <= query) pair"
+    t = _time_launches(torch, fn, iters, reps)
     if bound == "hbm":
         achieved, peak, unit = algo / t / 1e9, HBM_PEAK_GBS, "GB/s"
     else:
         achieved, peak, unit = algo / t / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
     return {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": None, "kernel": name,
-            "avg_launch_us": round(t * 1e6, 2), "algorithmic_per_launch": algo}
+            "avg_launch_us": round(t * 1e6, 2), "algorithmic_per_launch": algo, "algorithmic_unit": per}
+
+
+def step_roofline(workload, pre_ms, dec_ms):
+    """Whole-phase figure for context: algorithmic bytes (decode) or flops
+    (prefill-bound workload) of the timed phase over its measured time."""
+    batch, T, steps, prefill_timed = WORKLOADS[workload]
+    if workload == "prefill_8x4096":
+        flops = batch * T * 2 * LAYER_MATMUL_PARAMS * 28 + batch * (T * (T + 1) // 2) * 8192 * 28 \
+            + batch * 2 * LMHEAD_PARAMS
+        a = flops / (pre_ms * 1e-3) / 1e12
+        return {"phase": "prefill", "bound": "mfma", "achieved": round(a, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(a / BF16_PEAK_TFLOPS, 4)}
+    weights = 2 * (28 * LAYER_MATMUL_PARAMS + LMHEAD_PARAMS)
+    mean_ctx = T + (steps + 1) / 2.0
+    per_step = weights + batch * mean_ctx * KV_BYTES_PER_POS
+    a = per_step * steps / (dec_ms * 1e-3) / 1e9
+    return {"phase": "decode", "bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(a / HBM_PEAK_GBS, 4), "bytes_per_step": round(per_step)}
 
 
 def cpu_baseline(workload, bits):
@@ -297,10 +367,11 @@ def main():
         "decode_tok_s": round(tokens_decode / (dec_ms * 1e-3), 1) if steps > 0 else None,
     }
     try:
-        out["roofline"] = dominant_kernel(torch, B, dev, dm, args.workload, args.kernel_iters)
+        out["roofline"] = dominant_kernel(torch, B, dev, dm, r, args.workload, args.kernel_iters)
     except Exception as e:  # pragma: no cover
         log(f"[bench] kernel timing failed: {e}")
         out["roofline"] = None
+    out["step_roofline"] = step_roofline(args.workload, pre_ms, dec_ms)
     if not args.no_cpu_baseline:
         log("[bench] timing the float64 oracle on the host")
         out["cpu_baseline"] = cpu_baseline(args.workload, bits)

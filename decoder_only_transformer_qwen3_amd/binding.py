@@ -62,11 +62,15 @@ _decode = _sig("q3_decode_step", ctypes.c_int, ctypes.POINTER(q3_model), ctypes.
                _vp, _i32, _vp, _vp, _vp, _sz, _vp)
 _argmax = _sig("q3_argmax", ctypes.c_int, _vp, _i32, _i32, _i64, _vp, _vp)
 _linear = _sig("q3_linear", ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp)
+_attn_prefill = _sig("q3_attention_prefill", ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp)
+_attn_decode = _sig("q3_attention_decode", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
+                    _i32, _vp, _vp, _sz, _vp)
 
 Q3_EPI_STORE_BF16, Q3_EPI_STORE_F32, Q3_EPI_ADD_F32, Q3_EPI_SILU_GATE = 0, 1, 2, 3
 
 EXPORTS = ("q3_status_str", "q3_rope_table_host", "q3_workspace_bytes", "q3_layer_forward",
-           "q3_prefill", "q3_decode_step", "q3_argmax", "q3_linear")
+           "q3_prefill", "q3_decode_step", "q3_argmax", "q3_linear", "q3_attention_prefill",
+           "q3_attention_decode")
 
 
 class Q3Error(RuntimeError):
@@ -156,4 +160,23 @@ def q3_linear(x, w, out, m, n, k, ldo, epilogue, stream=None, check=True) -> int
     st = _linear(_ptr(x), _ptr(w), _ptr(out), m, n, k, ldo, epilogue, _stream(stream))
     if check:
         _check(st, "q3_linear")
+    return st
+
+
+def q3_attention_prefill(q, k_layer, v_layer, batch, n_tokens, start_pos, max_seq, out, stream=None,
+                         check=True) -> int:
+    st = _attn_prefill(_ptr(q), _ptr(k_layer), _ptr(v_layer), batch, n_tokens, start_pos, max_seq, _ptr(out),
+                       _stream(stream))
+    if check:
+        _check(st, "q3_attention_prefill")
+    return st
+
+
+def q3_attention_decode(qkv, q_norm, k_norm, rope_cos, rope_sin, k_layer, v_layer, batch, max_seq, positions,
+                        max_len_hint, out, ws, ws_bytes, stream=None, check=True) -> int:
+    st = _attn_decode(_ptr(qkv), _ptr(q_norm), _ptr(k_norm), _ptr(rope_cos), _ptr(rope_sin), _ptr(k_layer),
+                      _ptr(v_layer), batch, max_seq, _ptr(positions), max_len_hint, _ptr(out), _ptr(ws), ws_bytes,
+                      _stream(stream))
+    if check:
+        _check(st, "q3_attention_decode")
     return st

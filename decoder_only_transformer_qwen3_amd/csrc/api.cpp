@@ -351,6 +351,31 @@ int q3_linear(const void* x, const void* w, void* out, int32_t m, int32_t n, int
   return launch_status();
 }
 
+int q3_attention_prefill(const void* q, const void* k_layer, const void* v_layer, int32_t batch, int32_t n_tokens,
+                         int32_t start_pos, int32_t max_seq, void* out, void* stream) {
+  const int st = q3v::check_attn_prefill_call(q, k_layer, v_layer, batch, n_tokens, start_pos, max_seq, out);
+  if (st != Q3_OK) return st;
+  launch_attn_prefill(U(q), U(k_layer), U(v_layer), static_cast<uint16_t*>(out), batch, n_tokens, start_pos, max_seq,
+                      static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int q3_attention_decode(const void* qkv, const void* q_norm, const void* k_norm, const float* rope_cos,
+                        const float* rope_sin, void* k_layer, void* v_layer, int32_t batch, int32_t max_seq,
+                        const int32_t* positions, int32_t max_len_hint, void* out, void* ws, size_t ws_bytes,
+                        void* stream) {
+  const int st = q3v::check_attn_decode_call(qkv, q_norm, k_norm, rope_cos, rope_sin, k_layer, v_layer, batch,
+                                             max_seq, positions, max_len_hint, out, ws, ws_bytes);
+  if (st != Q3_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const Ws w = carve(ws, batch, 1);
+  launch_norm_operand(nullptr, 0, 1, 0, nullptr, nullptr, nullptr, NSQ, w.tick, w.n_tick, s);  // zero the tickets
+  launch_attn_decode(U(qkv), U(q_norm), U(k_norm), rope_cos, rope_sin, static_cast<uint16_t*>(k_layer),
+                     static_cast<uint16_t*>(v_layer), w.apart, w.tick + 64, static_cast<uint16_t*>(out), batch,
+                     max_seq, positions, 0, q3v::decode_splits(batch, max_len_hint), s);
+  return launch_status();
+}
+
 int q3_argmax(const float* logits, int32_t rows, int32_t vocab, int64_t row_stride, int32_t* out_idx, void* stream) {
   const int st = q3v::check_argmax_call(logits, rows, vocab, row_stride, out_idx);
   if (st != Q3_OK) return st;

@@ -128,6 +128,33 @@ int check_linear_call(const void* x, const void* w, const void* out, int32_t m, 
   return Q3_OK;
 }
 
+static bool cache_shape_ok(int32_t max_seq) { return max_seq >= 8 && max_seq <= Q3_MAX_POS && (max_seq % 8) == 0; }
+
+int check_attn_prefill_call(const void* q, const void* k_layer, const void* v_layer, int32_t batch, int32_t n_tokens,
+                            int32_t start_pos, int32_t max_seq, const void* out) {
+  if (!q || !k_layer || !v_layer || !out) return Q3_ERR_NULL;
+  if (batch < 1 || n_tokens < 1 || !cache_shape_ok(max_seq)) return Q3_ERR_SHAPE;
+  if ((int64_t)batch * n_tokens > MAX_TOKENS) return Q3_ERR_SHAPE;
+  if (start_pos < 0 || (int64_t)start_pos + n_tokens > max_seq) return Q3_ERR_POSITION;
+  if (!al16(q) || !al16(k_layer) || !al16(v_layer) || !al16(out)) return Q3_ERR_ALIGN;
+  return Q3_OK;
+}
+
+int check_attn_decode_call(const void* qkv, const void* q_norm, const void* k_norm, const float* rope_cos,
+                           const float* rope_sin, const void* k_layer, const void* v_layer, int32_t batch,
+                           int32_t max_seq, const int32_t* positions, int32_t max_len_hint, const void* out,
+                           const void* ws, size_t ws_bytes) {
+  if (!qkv || !q_norm || !k_norm || !rope_cos || !rope_sin || !k_layer || !v_layer || !positions || !out || !ws)
+    return Q3_ERR_NULL;
+  if (batch < 1 || batch > (int32_t)(MAX_TOKENS / 8) || !cache_shape_ok(max_seq)) return Q3_ERR_SHAPE;
+  if (max_len_hint < 1 || max_len_hint > max_seq) return Q3_ERR_POSITION;
+  if (!al16(qkv) || !al16(q_norm) || !al16(k_norm) || !al16(rope_cos) || !al16(rope_sin) || !al16(k_layer) ||
+      !al16(v_layer) || !al4(positions) || !al16(out) || !al16(ws))
+    return Q3_ERR_ALIGN;
+  if (ws_bytes < ws_layout(batch, 1).total) return Q3_ERR_WORKSPACE;
+  return Q3_OK;
+}
+
 int check_argmax_call(const float* logits, int32_t rows, int32_t vocab, int64_t row_stride, const int32_t* out_idx) {
   if (!logits || !out_idx) return Q3_ERR_NULL;
   if (rows < 1 || vocab < 1 || row_stride < vocab) return Q3_ERR_SHAPE;

@@ -44,6 +44,14 @@ int check_decode_call(const q3_model* m, const q3_kv* kv, int32_t batch, const i
 int check_linear_call(const void* x, const void* w, const void* out, int32_t m, int32_t n, int32_t k, int32_t ldo,
                       int32_t epilogue);
 
+int check_attn_prefill_call(const void* q, const void* k_layer, const void* v_layer, int32_t batch, int32_t n_tokens,
+                            int32_t start_pos, int32_t max_seq, const void* out);
+
+int check_attn_decode_call(const void* qkv, const void* q_norm, const void* k_norm, const float* rope_cos,
+                           const float* rope_sin, const void* k_layer, const void* v_layer, int32_t batch,
+                           int32_t max_seq, const int32_t* positions, int32_t max_len_hint, const void* out,
+                           const void* ws, size_t ws_bytes);
+
 int check_argmax_call(const float* logits, int32_t rows, int32_t vocab, int64_t row_stride, const int32_t* out_idx);
 
 }  // namespace q3v

@@ -229,6 +229,42 @@ enum {
 int q3_linear(const void *x, const void *w, void *out, int32_t m, int32_t n, int32_t k, int32_t ldo,
               int32_t epilogue, void *stream);
 
+/* Helper: causal GQA attention of a chunk of n_tokens queries over one
+ * layer's filled KV cache ("手写Qwen3-0.6B推理" §Attention; "第 3 章" §3.3).
+ * For sequence b, query head h (KV head h/2) and chunk row t at position
+ * p = start_pos + t:
+ *   out[b, t, h, :] = sum_{j <= p} softmax_j(q[b, t, h, :] . K[b, h/2, j, :] / sqrt(128)) V[b, h/2, j, :]
+ *   q        bf16 [batch, n_tokens, 16, 128], already normed and rotated;
+ *   k_layer, v_layer  one layer of a KV cache of capacity max_seq (layouts
+ *            as in q3_kv); rows 0 .. start_pos + n_tokens - 1 are read;
+ *   out      bf16 [batch, n_tokens, 2048].
+ * Errors: Q3_ERR_NULL, Q3_ERR_SHAPE (batch or n_tokens < 1, max_seq not a
+ * multiple of 8 in 8..40960), Q3_ERR_POSITION (start_pos < 0 or
+ * start_pos + n_tokens > max_seq), Q3_ERR_ALIGN (16 B), Q3_ERR_HIP. */
+int q3_attention_prefill(const void *q, const void *k_layer, const void *v_layer, int32_t batch,
+                         int32_t n_tokens, int32_t start_pos, int32_t max_seq, void *out, void *stream);
+
+/* Helper: the attention half of one decode step for one new token per
+ * sequence, as q3_decode_step runs it ("古法手撕简易LLM推理器"
+ * §prefill与predict): from the raw projection rows of the new tokens it
+ * applies the per-head q/k RMSNorm and RoPE at each token's position p,
+ * writes the rotated K and the raw V into cache row p, and attends over
+ * rows 0..p.
+ *   qkv        bf16 [batch, 4096] raw q|k|v rows (as q3_layer_weights.w_qkv orders them);
+ *   q_norm, k_norm  bf16 [128] gains; rope_cos, rope_sin as in q3_model;
+ *   k_layer, v_layer  one layer of a KV cache of capacity max_seq;
+ *   positions  device int32 [batch]: p of each new token (p < max_seq);
+ *   max_len_hint  host bound with max(positions) < max_len_hint <= max_seq
+ *              (it sets only the number of key-range splits);
+ *   out        bf16 [batch, 2048];
+ *   ws         >= q3_workspace_bytes(batch, 1) bytes (split partials, tickets).
+ * Errors: Q3_ERR_NULL, Q3_ERR_SHAPE, Q3_ERR_POSITION (max_len_hint outside
+ * 1..max_seq), Q3_ERR_ALIGN, Q3_ERR_WORKSPACE, Q3_ERR_HIP. */
+int q3_attention_decode(const void *qkv, const void *q_norm, const void *k_norm, const float *rope_cos,
+                        const float *rope_sin, void *k_layer, void *v_layer, int32_t batch, int32_t max_seq,
+                        const int32_t *positions, int32_t max_len_hint, void *out, void *ws, size_t ws_bytes,
+                        void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -58,6 +58,23 @@ int main() {
       EXPECT_EQ(s >= 1 && s <= DEC_SPLIT_MAX, 1);
     }
 
+  // ---- attention helpers
+  {
+    const void* p = A(0x1000);
+    EXPECT_EQ(check_attn_prefill_call(p, p, p, 2, 16, 0, 64, p), Q3_OK);
+    EXPECT_EQ(check_attn_prefill_call(nullptr, p, p, 2, 16, 0, 64, p), Q3_ERR_NULL);
+    EXPECT_EQ(check_attn_prefill_call(p, p, p, 2, 16, 48, 64, p), Q3_OK);
+    EXPECT_EQ(check_attn_prefill_call(p, p, p, 2, 16, 49, 64, p), Q3_ERR_POSITION);
+    EXPECT_EQ(check_attn_prefill_call(p, p, p, 2, 16, 0, 68, p), Q3_ERR_SHAPE);
+    const float* f = static_cast<const float*>(p);
+    const int32_t* pos = static_cast<const int32_t*>(p);
+    const size_t need = ws_layout(3, 1).total;
+    EXPECT_EQ(check_attn_decode_call(p, p, p, f, f, p, p, 3, 64, pos, 64, p, p, need), Q3_OK);
+    EXPECT_EQ(check_attn_decode_call(p, p, p, f, f, p, p, 3, 64, pos, 65, p, p, need), Q3_ERR_POSITION);
+    EXPECT_EQ(check_attn_decode_call(p, p, p, f, f, p, p, 3, 64, nullptr, 64, p, p, need), Q3_ERR_NULL);
+    EXPECT_EQ(check_attn_decode_call(p, p, p, f, f, p, p, 3, 64, pos, 64, p, p, need - 1), Q3_ERR_WORKSPACE);
+  }
+
   // ---- q3_layer_forward
   q3_layer_weights w = good_layer();
   const float* cs = static_cast<const float*>(A(0x50000));

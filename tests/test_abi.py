@@ -132,6 +132,31 @@ def test_prefill_decode_argmax_reject_bad_arguments(B):
     assert B.q3_argmax(None, 2, 10, 10, 0x900000, stream=0, check=False) == B.Q3_ERR_NULL
 
 
+def test_attention_helpers_reject_bad_arguments(B):
+    pf = lambda *a: B.q3_attention_prefill(*a, stream=0, check=False)
+    assert pf(None, 0x2000, 0x3000, 2, 16, 0, 64, 0x4000) == B.Q3_ERR_NULL
+    assert pf(0x1000, 0x2000, 0x3000, 0, 16, 0, 64, 0x4000) == B.Q3_ERR_SHAPE
+    assert pf(0x1000, 0x2000, 0x3000, 2, 16, 0, 60, 0x4000) == B.Q3_ERR_SHAPE
+    assert pf(0x1000, 0x2000, 0x3000, 2, 16, 49, 64, 0x4000) == B.Q3_ERR_POSITION
+    assert pf(0x1000, 0x2000, 0x3000, 2, 16, -1, 64, 0x4000) == B.Q3_ERR_POSITION
+    assert pf(0x1000, 0x2008, 0x3000, 2, 16, 0, 64, 0x4000) == B.Q3_ERR_ALIGN
+    need = B.q3_workspace_bytes(3, 1)
+    base = [0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000, 3, 64, 0x8000, 64, 0x9000, 0xA000, need]
+
+    def dec(i, value):
+        a = list(base)
+        a[i] = value
+        return B.q3_attention_decode(*a, stream=0, check=False)
+
+    assert dec(9, None) == B.Q3_ERR_NULL
+    assert dec(7, 0) == B.Q3_ERR_SHAPE
+    assert dec(8, 20) == B.Q3_ERR_SHAPE
+    assert dec(10, 65) == B.Q3_ERR_POSITION
+    assert dec(10, 0) == B.Q3_ERR_POSITION
+    assert dec(9, 0x8002) == B.Q3_ERR_ALIGN
+    assert dec(13, need - 1) == B.Q3_ERR_WORKSPACE
+
+
 def test_rope_table_matches_oracle_angles(B):
     import oracle as O
     cos = np.empty((B.MAX_POS, 64), dtype=np.float32)

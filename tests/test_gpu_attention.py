@@ -1,0 +1,157 @@
+"""GPU parity of the attention kernels on their own, through the helper
+entry points q3_attention_prefill and q3_attention_decode, against the
+float64 oracle's attention (plus its RMSNorm and RoPE for the decode helper,
+which starts from the raw projection rows).
+
+Covers ragged query tiles, a chunk at an offset, single keys, the cache
+capacity edge, and the full benchmark sizes (8 x 4096 prefill; batch 32
+over 2048 positions; batch 4 over 32768 positions) on sampled outputs.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from decoder_only_transformer_qwen3_amd import inputs as I
+
+from gpu_common import REL_TOL, bf16_tensor_to_f64, cache_fill_bits, log, rel_err, v_blocked_to_dense, \
+    v_dense_to_blocked
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decoder_only_transformer_qwen3_amd import binding, device
+    return binding, device
+
+
+@pytest.fixture(scope="module")
+def rope(lib):
+    B, dev = lib
+    return dev.rope_tables()
+
+
+def _caches(B, dev, batch, max_seq, filled, seed):
+    """K/V caches with `filled` rows of N(0, 1) bf16 per (sequence, head)."""
+    shape = (batch, B.N_KV_HEADS, max_seq, B.HEAD_DIM)
+    kb = np.zeros(shape, dtype=np.uint16)
+    vb = np.zeros(shape, dtype=np.uint16)
+    if filled:
+        kb[:, :, :filled] = cache_fill_bits(seed, (batch, B.N_KV_HEADS, filled, B.HEAD_DIM))
+        vb[:, :, :filled] = cache_fill_bits(seed + 1, (batch, B.N_KV_HEADS, filled, B.HEAD_DIM))
+    return kb, vb, dev.to_device_bf16(kb), dev.to_device_bf16(v_dense_to_blocked(vb))
+
+
+@pytest.mark.parametrize("batch,T,start,max_seq", [
+    (1, 16, 0, 16),      # one-layer workload shape
+    (2, 100, 50, 160),   # ragged 128-query tile at an offset
+    (1, 1, 0, 8),        # a single key
+    (2, 200, 0, 200),    # two query tiles, ragged
+    (3, 13, 3, 16),      # chunk ending at the capacity edge
+])
+def test_attention_prefill_parity(lib, batch, T, start, max_seq):
+    B, dev = lib
+    log(f"[attn-prefill] batch={batch} T={T} start={start} max_seq={max_seq}")
+    kb, vb, kc, vc = _caches(B, dev, batch, max_seq, start + T, seed=31)
+    qb = I.normal_bf16(32, "attn_q", (batch, T, B.N_HEADS, B.HEAD_DIM), std=1.0)
+    out = torch.empty((batch, T, B.N_HEADS * B.HEAD_DIM), dtype=torch.bfloat16, device="cuda")
+    B.q3_attention_prefill(dev.to_device_bf16(qb), kc, vc, batch, T, start, max_seq, out)
+    torch.cuda.synchronize()
+    got = bf16_tensor_to_f64(out).reshape(batch, T, B.N_HEADS, B.HEAD_DIM)
+    pos = np.arange(start, start + T)
+    for b in range(batch):
+        q = O.widen_bf16(qb[b]).transpose(1, 0, 2)                       # [H, T, D]
+        k = O.widen_bf16(kb[b, :, :start + T])
+        v = O.widen_bf16(vb[b, :, :start + T])
+        ref = O.attention(q, k, v, pos).transpose(1, 0, 2)               # [T, H, D]
+        e = rel_err(got[b], ref)
+        log(f"   seq {b}: rel={e:.3e}")
+        assert e <= REL_TOL
+
+
+def test_attention_prefill_8x4096_sampled(lib):
+    """Benchmark size: 8 x 4096 from position 0; rows sampled across tiles
+    (first, tile edges, last) of two sequences, every head."""
+    B, dev = lib
+    batch, T = 8, 4096
+    log("[attn-prefill] 8 x 4096 (sampled rows)")
+    kb, vb, kc, vc = _caches(B, dev, batch, T, T, seed=41)
+    qb = I.normal_bf16(42, "attn_q", (batch, T, B.N_HEADS, B.HEAD_DIM), std=1.0)
+    out = torch.empty((batch, T, B.N_HEADS * B.HEAD_DIM), dtype=torch.bfloat16, device="cuda")
+    B.q3_attention_prefill(dev.to_device_bf16(qb), kc, vc, batch, T, 0, T, out)
+    torch.cuda.synchronize()
+    got = bf16_tensor_to_f64(out).reshape(batch, T, B.N_HEADS, B.HEAD_DIM)
+    rows = np.array([0, 1, 63, 64, 127, 128, 1000, 2047, 2048, 4094, 4095])
+    for b in (0, 7):
+        q = O.widen_bf16(qb[b, rows]).transpose(1, 0, 2)
+        ref = O.attention(q, O.widen_bf16(kb[b]), O.widen_bf16(vb[b]), rows).transpose(1, 0, 2)
+        e = rel_err(got[b, rows], ref)
+        log(f"   seq {b}: rel={e:.3e}")
+        assert e <= REL_TOL
+
+
+def _decode_case(lib, rope, batch, max_seq, positions, check_seqs=None, seed=51):
+    B, dev = lib
+    positions = np.asarray(positions, dtype=np.int32)
+    log(f"[attn-decode] batch={batch} max_seq={max_seq} positions={positions.tolist()[:6]}")
+    filled = int(positions.max())
+    kb, vb, kc, vc = _caches(B, dev, batch, max_seq, filled, seed)
+    # rows past each sequence's own position are garbage the kernel must not read
+    for b in range(batch):
+        p = int(positions[b])
+        if p < filled:
+            kb[b, :, p:filled] = 0x7FC0  # NaN bits: any read of them would poison the output
+            vb[b, :, p:filled] = 0x7FC0
+    kc = dev.to_device_bf16(kb)
+    vc = dev.to_device_bf16(v_dense_to_blocked(vb))
+    qkv = I.normal_bf16(seed + 2, "attn_qkv", (batch, B.QKV_ROWS), std=1.0)
+    qn = I.normal_bf16(seed + 3, "attn_qn", (B.HEAD_DIM,), std=0.02, mean=1.0)
+    kn = I.normal_bf16(seed + 4, "attn_kn", (B.HEAD_DIM,), std=0.02, mean=1.0)
+    pos_d = torch.from_numpy(positions).cuda()
+    out = torch.empty((batch, B.N_HEADS * B.HEAD_DIM), dtype=torch.bfloat16, device="cuda")
+    ws, nb = dev.workspace(batch, 1)
+    B.q3_attention_decode(dev.to_device_bf16(qkv), dev.to_device_bf16(qn), dev.to_device_bf16(kn), rope[0], rope[1],
+                          kc, vc, batch, max_seq, pos_d, int(positions.max()) + 1, out, ws, nb)
+    torch.cuda.synchronize()
+    got = bf16_tensor_to_f64(out).reshape(batch, B.N_HEADS, B.HEAD_DIM)
+    kg = bf16_tensor_to_f64(kc)
+    vg = v_blocked_to_dense(bf16_tensor_to_f64(vc))
+    qkv64 = O.widen_bf16(qkv)
+    for b in (range(batch) if check_seqs is None else check_seqs):
+        p = int(positions[b])
+        x = qkv64[b]
+        q = x[:2048].reshape(1, B.N_HEADS, B.HEAD_DIM)
+        k = x[2048:3072].reshape(1, B.N_KV_HEADS, B.HEAD_DIM)
+        v = x[3072:].reshape(1, B.N_KV_HEADS, B.HEAD_DIM)
+        q = O.rope(O.rmsnorm(q, O.widen_bf16(qn)), [p], 1e6)
+        k = O.rope(O.rmsnorm(k, O.widen_bf16(kn)), [p], 1e6)
+        kk = np.concatenate([O.widen_bf16(kb[b, :, :p]), k.transpose(1, 0, 2)], axis=1)
+        vv = np.concatenate([O.widen_bf16(vb[b, :, :p]), v.transpose(1, 0, 2)], axis=1)
+        ref = O.attention(q.transpose(1, 0, 2), kk, vv, [p])[:, 0]
+        e = rel_err(got[b], ref)
+        ek = rel_err(kg[b, :, p], k[0])
+        np.testing.assert_array_equal(vg[b, :, p], v[0])  # raw V is stored exactly
+        log(f"   seq {b} p={p}: out rel={e:.3e} K row rel={ek:.3e}")
+        assert e <= REL_TOL and ek <= REL_TOL
+
+
+def test_attention_decode_parity_mixed_positions(lib, rope):
+    """Different positions per sequence, incl. position 0 and the last cache row."""
+    _decode_case(lib, rope, 5, 4096, [0, 1, 700, 2049, 4095])
+
+
+def test_attention_decode_unaligned_positions(lib, rope):
+    """Positions on either side of 8-position V blocks and 32-key tiles."""
+    _decode_case(lib, rope, 6, 160, [7, 8, 31, 32, 33, 159])
+
+
+def test_attention_decode_batch32_ctx2048(lib, rope):
+    _decode_case(lib, rope, 32, 2176, [2048 + (i % 7) for i in range(32)], check_seqs=[0, 13, 31])
+
+
+def test_attention_decode_batch4_ctx32768(lib, rope):
+    _decode_case(lib, rope, 4, 32832, [32768, 32800, 20000, 32831], check_seqs=[0, 3])
