@@ -2,23 +2,32 @@
 // chunk at an offset):  o_h[t] = sum_{j <= p(t)} softmax_j(q_h[t].k_g[j] / sqrt(128)) v_g[j]
 // with g = h / 2 ("手写Qwen3-0.6B推理" §Attention; "第 3 章" §3.3).
 //
-// One workgroup = one KV head g of one sequence and 128 query positions, for
-// BOTH query heads 2g and 2g+1, so each K/V tile staged in LDS feeds 256
-// query rows.  8 waves: wave w takes head 2g + w/4 and 32 positions.
+// One workgroup = one KV head g of one sequence and 64 query positions, for
+// both query heads 2g and 2g+1 that share g, so each K/V tile staged in LDS
+// feeds 128 query rows.  4 waves: wave w takes head 2g + w/2 and 32
+// positions.  Two workgroups share a CU, so each SIMD runs two waves whose
+// MFMA and softmax phases overlap.
 //
-// Per 64-key tile a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
-// (A = K rows from LDS, B = the wave's Q held in registers).  The
-// accumulator gives each lane one query (column l%32) and 32 of the 64 key
-// scores, so the online-softmax max and sum are lane-local up to one
-// exchange with lane l^32.  O^T = V^T P^T then takes the score registers,
-// rounded to bf16, directly as the B operand; the A operand (8 consecutive
-// positions of one dim) comes straight from the blocked V cache layout,
-// which is staged into LDS as a plain copy.
+// K/V tiles of 64 keys are copied into LDS with direct-to-LDS loads
+// (global_load_lds_dwordx4) into a 2-stage ring, one tile ahead of the
+// compute, with one barrier per tile.
 //
-// The running max is only raised when a new score exceeds it by more than
-// 8 (log2 units), so most tiles skip the O rescale; p = 2^(s - m) then stays
-// below 256, well inside float and bfloat16 range, and the final O / l is
-// unchanged.
+// Per tile a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
+// (A = K rows from LDS, B = the wave's Q held in registers).  The K rows of
+// a 32-key block are fed to the A operand in the order
+//   A row 8a + 4h + b  <-  key 16(a/2) + 8h + 4(a%2) + b,
+// so that the accumulator gives lane l (h = l/32) the scores of keys
+// 16s + 8h + 0..7 for s = 0, 1: exactly the keys whose values one 16 B
+// chunk of the blocked V cache holds for one dim.  O^T += V^T P^T then takes
+// those registers, rounded to bf16, directly as the B operand, and each A
+// operand (8 positions of one dim) is a single 16 B LDS read.
+// K rows are XOR-swizzled in LDS (16 B chunk c of row r at c ^ swz(r)) so
+// the operand reads are free of bank conflicts.
+//
+// Softmax works in the log2 domain with the hardware exp2; the running max
+// is raised only when a score exceeds it by more than 8, so most tiles skip
+// the O rescale (p = 2^(s - m) stays below 256).  The causal mask is applied
+// only on tiles that reach past a wave's first query.
 //
 // MFMA lane layouts (32x32x16): A row l%32, B column l%32, k-slot (l/32, j);
 // C column l%32, rows 8*(i/4) + 4*(l/32) + (i%4).
@@ -29,82 +38,71 @@
 
 namespace q3 {
 
-constexpr int FA_BQ = 128;        // query positions per workgroup (per head)
-constexpr int FA_BK = 64;         // keys per tile
-constexpr int FA_THREADS = 512;   // 8 waves
-constexpr int KS_STRIDE = D + 8;  // K tile row (bf16), 272 B
-constexpr int VS_ELEMS = FA_BK * D;  // blocked V tile: 8 blocks x 128 dims x 8 positions
-constexpr float RESCALE_SLACK = 8.0f;
+constexpr int FA_BQ = 64;                  // query positions per workgroup (per head)
+constexpr int FA_BK = 64;                  // keys per tile
+constexpr int FA_NS = 2;                   // LDS stages
+constexpr int FA_TILE = FA_BK * D;         // bf16 elements of one K or V tile (16 KB)
+constexpr float FA_RESCALE_SLACK = 8.0f;
 
-__global__ __launch_bounds__(FA_THREADS) void k_attn_prefill(const uint16_t* __restrict__ q,
-                                                             const uint16_t* __restrict__ k_cache,
-                                                             const uint16_t* __restrict__ v_cache,
-                                                             uint16_t* __restrict__ out, int T, int start,
-                                                             int max_seq) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][FA_BK * KS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][VS_ELEMS];
+// 16 B-chunk swizzle of K row r in LDS
+__device__ __forceinline__ int fa_kswz(int r) { return (r & 3) | ((r >> 1) & 4); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_prefill(const uint16_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ k_cache,
+                                                         const uint16_t* __restrict__ v_cache,
+                                                         uint16_t* __restrict__ out, int T, int start,
+                                                         int max_seq) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[FA_NS][2][FA_TILE];
 
   const int qt = gridDim.x - 1 - blockIdx.x;  // longest (latest) tiles first
   const int g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lq = l & 31, lh = l >> 5;
-  const int hq = 2 * g + (w >> 2);
-  const int t0 = qt * FA_BQ + 32 * (w & 3);  // first query of this wave
-  const int tq = t0 + lq;                    // this lane's query
-  const int tq_c = tq < T ? tq : T - 1;      // rows past the end are computed, not stored
-  const int pq = start + tq_c;               // its absolute position
+  const int tid = threadIdx.x, l = tid & 63, lq = l & 31, lh = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
+  const int hq = 2 * g + (w >> 1);
+  const int t0 = qt * FA_BQ + 32 * (w & 1);  // first query row of this wave
   const int kv_len = start + T;
-  const int wave_pmin = start + (t0 < T ? t0 : T - 1);
-  const int wave_pmax = start + ((t0 + 31) < T ? (t0 + 31) : T - 1);
   const int wg_last = (qt * FA_BQ + FA_BQ - 1) < T ? (qt * FA_BQ + FA_BQ - 1) : T - 1;
-  const int n_kt = (start + wg_last) / FA_BK + 1;
+  const int n_kt = (start + wg_last) / FA_BK + 1;  // key tiles of the workgroup
+  const int wave_last = (t0 + 31) < T ? (t0 + 31) : T - 1;
+  const int wave_kt = t0 < T ? (start + wave_last) / FA_BK + 1 : 0;  // tiles this wave computes
+  const int wave_pmin = start + (t0 < T ? t0 : T - 1);
 
-  // Q operand: lane holds dims 16 s + 8 lh + j of its query, s = 0..7
+  // ---- Q operand: qreg[s] = dims 16 s + 8 lh .. +7 of query row t0 + lq
   u32x4 qreg[8];
   {
-    const uint16_t* qrow = q + ((size_t)b * T + tq_c) * QDIM + hq * D + 8 * lh;
+    int tq = t0 + lq;
+    tq = tq < T ? tq : T - 1;
+    const uint16_t* qrow = q + ((size_t)b * T + tq) * QDIM + hq * D + 8 * lh;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qreg[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s);
   }
 
   const uint16_t* kbase = k_cache + ((size_t)b * HKV + g) * max_seq * D;
   const uint16_t* vbase = v_cache + ((size_t)b * HKV + g) * max_seq * D;
-  u32x4 kreg[2], vreg[2];
+  const int last_key = kv_len - 1, last_blk = (kv_len - 1) & ~7;
 
-  // K: chunk c = tid + 512 i -> key c/16, dims 8*(c%16).  V: the tile's 8
-  // position blocks are 16 KB of contiguous cache; chunk c covers dim c%128
-  // of block c/128 (8 positions).  Loads only read in-range blocks (clamped
-  // to the last real block); positions at or past kv_len are zeroed when the
-  // registers are written to LDS, so prefetching never waits on a mask.
-  const int last_blk = ((kv_len - 1) >> 3) << 3;
-  auto load_tile = [&](int j) {
+  // DMA of key tile j into its stage: 8 instructions per thread (4 for K, 4 for V)
+  auto issue = [&](int j) {
+    uint16_t* ks = lds[j % FA_NS][0];
+    uint16_t* vs = lds[j % FA_NS][1];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + FA_THREADS * i;
-      int key = j * FA_BK + (c >> 4);
-      key = key < kv_len ? key : kv_len - 1;
-      kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * D + (c & 15) * 8);
+    for (int rq = 0; rq < 4; ++rq) {  // K rows 16 rq + 4 w .. +3, one row per 16 lanes
+      const int r = 16 * rq + 4 * w + (l >> 4);
+      const int c = (l & 15) ^ fa_kswz(r);
+      int key = j * FA_BK + r;
+      key = key < last_key ? key : last_key;
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + (size_t)key * D + 8 * c),
+                                       (lds_ptr_t)(ks + (16 * rq + 4 * w) * D), 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + FA_THREADS * i;
-      int p0 = j * FA_BK + (c >> 7) * VBLK;
-      p0 = p0 < last_blk ? p0 : last_blk;
-      vreg[i] = *reinterpret_cast<const u32x4*>(vbase + (size_t)p0 * D + (size_t)(c & 127) * VBLK);
-    }
-  };
-  auto store_tile = [&](int buf, int j) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + FA_THREADS * i;
-      *reinterpret_cast<u32x4*>(&Ks[buf][(c >> 4) * KS_STRIDE + (c & 15) * 8]) = kreg[i];
-      const int valid = kv_len - (j * FA_BK + (c >> 7) * VBLK);  // real positions in this chunk
-      u32x4 v = vreg[i];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t keep = (2 * e + 1 < valid) ? 0xffffffffu : ((2 * e < valid) ? 0x0000ffffu : 0u);
-        v[e] &= keep;
-      }
-      *reinterpret_cast<u32x4*>(&Vs[buf][c * VBLK]) = v;
+    for (int rq = 0; rq < 4; ++rq) {  // V: the tile's 8 blocks are 16 KB of contiguous cache
+      const int ch = 4 * rq + w;      // 1 KB chunk: block ch/2, half ch%2
+      int pb = j * FA_BK + 8 * (ch >> 1);
+      pb = pb < last_blk ? pb : last_blk;
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + (size_t)pb * D + (ch & 1) * 512 + 8 * l),
+                                       (lds_ptr_t)(vs + ch * 512), 16, 0, 0);
     }
   };
 
@@ -115,47 +113,74 @@ __global__ __launch_bounds__(FA_THREADS) void k_attn_prefill(const uint16_t* __r
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
+  // K row read by this lane's A operand within a 32-key block
+  const int krow = 16 * (lq >> 4) + 8 * ((lq >> 2) & 1) + 4 * ((lq >> 3) & 1) + (lq & 3);
 
-  load_tile(0);
-  store_tile(0, 0);
-  __syncthreads();
+  issue(0);
 
   for (int j = 0; j < n_kt; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_kt) load_tile(j + 1);
-    if (j * FA_BK <= wave_pmax) {
-      const uint16_t* ks = Ks[buf];
-      const uint16_t* vs = Vs[buf];
-      // ---- S^T = K Q^T for keys j*64 .. j*64+63 (two 32-key blocks)
-      f32x16 sacc[2];
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's part of tile j landed
+    __builtin_amdgcn_s_barrier();        // all of tile j is in LDS; stage (j+1)%2 is free
+    if (j + 1 < n_kt) issue(j + 1);
+    if (j >= wave_kt) continue;          // past this wave's causal range (wave-uniform)
+
+    const uint16_t* ks = lds[j % FA_NS][0];
+    const uint16_t* vs = lds[j % FA_NS][1];
+    // ---- S^T = K Q^T: sacc[kb] for keys j*64 + 32 kb + (row order above)
+    f32x16 sacc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+    {
+      // 16 K operand reads (2 key blocks x 8 dim steps) in a ring four reads
+      // ahead of the MFMAs
+      const uint16_t* kr0 = ks + krow * D;
+      const uint16_t* kr1 = ks + (32 + krow) * D;
+      const int sw = fa_kswz(krow);  // equal for rows krow and 32 + krow
+      auto kread = [&](int x) {
+        return *reinterpret_cast<const u32x4*>(((x >> 3) ? kr1 : kr0) + 8 * ((2 * (x & 7) + lh) ^ sw));
+      };
+      u32x4 ka[4];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(&ks[(kb * 32 + lq) * KS_STRIDE + 16 * s + 8 * lh]);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[s]), sacc[kb], 0, 0, 0);
-        }
+      for (int x = 0; x < 4; ++x) ka[x] = kread(x);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        sacc[x >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[x & 3]), as_bf16x8(qreg[x & 7]),
+                                                               sacc[x >> 3], 0, 0, 0);
+        if (x + 4 < 16) ka[x & 3] = kread(x + 4);
+        __builtin_amdgcn_sched_barrier(0);  // keep each read four steps ahead of its MFMA
       }
-      // ---- scale (log2 domain) and causal mask
-      const bool need_mask = (j * FA_BK + FA_BK - 1) > wave_pmin;
-      float mx = -INFINITY;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- causal mask, lazy online softmax, P packed to bf16.  Lane keys
+    // relative to the tile: 32 kb + 16 (i / 8) + 8 lh + i % 8.
+    const bool v_tail = (j + 1) * FA_BK > kv_len;  // the tile runs past the cache range
+    const bool need_mask = (j * FA_BK + FA_BK - 1) > wave_pmin || v_tail;
+    u32x4 pb[4];  // per key step of 16
+    {
+      float sv[32];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float sv = sacc[kb][i] * sl2;
-          if (need_mask) {
-            const int key = j * FA_BK + kb * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-            if (key > pq) sv = -INFINITY;
-          }
-          sacc[kb][i] = sv;
-          mx = fmaxf(mx, sv);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // ---- lazy rescale: raise the running max only when it is exceeded by more than the slack
-      const bool raise = mx > m_run + RESCALE_SLACK;
+        for (int i = 0; i < 16; ++i) sv[16 * kb + i] = sacc[kb][i];
+      if (need_mask) {
+        // keys above min(query position, kv_len - 1) are excluded
+        int lim = start + t0 + lq;
+        lim = lim < kv_len - 1 ? lim : kv_len - 1;
+        lim -= j * FA_BK + 8 * lh;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            sv[16 * kb + i] = (32 * kb + 16 * (i >> 3) + (i & 7)) > lim ? -INFINITY : sv[16 * kb + i];
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int i = 1; i < 32; ++i) mx = fmaxf(mx, sv[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+      const bool raise = mx > m_run + FA_RESCALE_SLACK;
       if (__ballot(raise)) {
         const float m_new = raise ? mx : m_run;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -166,60 +191,73 @@ __global__ __launch_bounds__(FA_THREADS) void k_attn_prefill(const uint16_t* __r
           for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
         m_run = m_new;
       }
-      float lsum = 0.f;
+      const float mneg = -m_run;
+      float ls = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int k = 0; k < 4; ++k)  // key step of 16: sv[8k .. 8k+7]
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(sacc[kb][i] - m_run);
-          sacc[kb][i] = p;
-          lsum += p;
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[8 * k + 2 * e], sl2, mneg));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[8 * k + 2 * e + 1], sl2, mneg));
+          ls += p0 + p1;
+          pb[k][e] = pack_bf2(p0, p1);
         }
-      l_run += lsum;
-      // ---- O^T += V^T P^T, 16 keys per MFMA step
+      l_run += ls;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- O^T += V^T P^T, 16 keys per MFMA step; A = 8 positions of one dim
+    {
+      // 16 V operand reads (4 key steps x 4 dim blocks) in a ring four reads ahead
+      const uint16_t* vb0 = vs + lh * (D * VBLK) + lq * VBLK;
+      auto vread = [&](int x) {
+        return *reinterpret_cast<const u32x4*>(vb0 + 2 * (x >> 2) * (D * VBLK) + 32 * (x & 3) * VBLK);
+      };
+      const int vvalid = kv_len - (j * FA_BK + 8 * lh);  // valid positions of this lane's first chunk
+      u32x4 va[4];
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int kb = st >> 1, c = st & 1;
-        u32x4 pb;
+      for (int x = 0; x < 4; ++x) va[x] = vread(x);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) pb[jj] = pack_bf2(sacc[kb][8 * c + 2 * jj], sacc[kb][8 * c + 2 * jj + 1]);
-        // this lane's keys: block (4 kb + 2 c) positions 4 lh..4 lh+3, block (4 kb + 2 c + 1) same positions
-        const int blk = 4 * kb + 2 * c;
+      for (int x = 0; x < 16; ++x) {
+        const int st = x >> 2, db = x & 3;
+        u32x4 a = va[x & 3];
+        if (v_tail) {  // positions at or past kv_len may hold anything: zero them
+          const int valid = vvalid - 16 * st;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int d = db * 32 + lq;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(&vs[(blk * D + d) * VBLK + 4 * lh]);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(&vs[((blk + 1) * D + d) * VBLK + 4 * lh]);
-          const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pb), oacc[db], 0, 0, 0);
+          for (int e = 0; e < 4; ++e)
+            a[e] &= (2 * e + 1 < valid) ? 0xffffffffu : ((2 * e < valid) ? 0x0000ffffu : 0u);
         }
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pb[st]), oacc[db], 0, 0, 0);
+        if (x + 4 < 16) va[x & 3] = vread(x + 4);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (j + 1 < n_kt) store_tile(buf ^ 1, j + 1);
-    __syncthreads();
   }
 
-  // ---- normalise and store: lane holds dims db*32 + 8*(i/4) + 4*lh + (i%4)
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (tq < T) {
-    const float inv = 1.0f / l_tot;
-    uint16_t* orow = out + ((size_t)b * T + tq) * QDIM + hq * D;
+  // ---- normalise and store: lane holds dims db*32 + 8*(i/4) + 4*lh + (i%4) of its query
+  {
+    const int tq = t0 + lq;
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (tq < T) {
+      const float inv = 1.0f / l_tot;
+      uint16_t* orow = out + ((size_t)b * T + tq) * QDIM + hq * D;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        u32x2 o;
-        o.x = pack_bf2(oacc[db][4 * gq] * inv, oacc[db][4 * gq + 1] * inv);
-        o.y = pack_bf2(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * gq + 4 * lh) = o;
-      }
+        for (int gq = 0; gq < 4; ++gq) {
+          u32x2 o;
+          o.x = pack_bf2(oacc[db][4 * gq] * inv, oacc[db][4 * gq + 1] * inv);
+          o.y = pack_bf2(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * gq + 4 * lh) = o;
+        }
+    }
   }
 }
 
 void launch_attn_prefill(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out, int B,
                          int T, int start, int max_seq, hipStream_t s) {
   const dim3 grid((T + FA_BQ - 1) / FA_BQ, HKV, B);
-  hipLaunchKernelGGL(k_attn_prefill, grid, dim3(FA_THREADS), 0, s, q, k_cache, v_cache, out, T, start, max_seq);
+  hipLaunchKernelGGL(k_attn_prefill, grid, dim3(256), 0, s, q, k_cache, v_cache, out, T, start, max_seq);
 }
 
 }  // namespace q3
