@@ -17,9 +17,9 @@ static_assert(Q3_EPI_STORE_BF16 == EPI_BF16 && Q3_EPI_STORE_F32 == EPI_F32 && Q3
 
 namespace {
 
-// Skinny-GEMM K splits: o_proj K = 2048 -> 4 x 512, down K = 3072 -> 6 x 512.
+// Skinny-GEMM K splits: o_proj K = 2048 -> 4 x 512, down K = 3072 -> 3 x 1024.
 constexpr int SPLIT_O = 4;
-constexpr int SPLIT_DOWN = 6;
+constexpr int SPLIT_DOWN = 3;
 // Row counts up to this run o_proj / down as a VALU GEMV without a K split.
 constexpr int GEMV_MAX_ROWS = 8;
 
@@ -60,6 +60,7 @@ struct LayerCtx {
   int B, T, max_seq, start;
   const int32_t* pos_dev;  // per-sequence start positions on the device (decode), or null
   int dec_splits;          // decode-attention splits (T == 1 only)
+  int dec_len;             // bound on the sequences' lengths after the step (T == 1 only)
   float* resid;
   const uint16_t* gamma_next;  // gain of the norm that follows this layer, or null
   Ws ws;
@@ -135,7 +136,7 @@ void run_layer(const LayerCtx& c) {
   // q/k RMSNorm + RoPE, K/V into the cache, causal GQA attention
   if (c.T == 1) {
     launch_attn_decode(c.ws.qkv, U(w->q_norm), U(w->k_norm), c.cos, c.sin, c.kl, c.vl, c.ws.apart, c.ws.tick + 64,
-                       c.ws.ao, c.B, c.max_seq, c.pos_dev, c.start, c.dec_splits, c.s);
+                       c.ws.ao, c.B, c.max_seq, c.pos_dev, c.start, c.dec_splits, c.dec_len, c.s);
   } else {
     launch_qknorm_rope(c.ws.qkv, U(w->q_norm), U(w->k_norm), c.cos, c.sin, c.ws.qr, c.kl, c.vl, c.B, c.T,
                        c.max_seq, c.pos_dev, c.start, c.s);
@@ -259,6 +260,7 @@ int q3_layer_forward(const q3_layer_weights* w, const float* rope_cos, const flo
   c.start = start_pos;
   c.pos_dev = nullptr;
   c.dec_splits = q3v::decode_splits(batch, start_pos + 1);
+  c.dec_len = start_pos + 1;
   c.resid = residual;
   c.gamma_next = nullptr;
   c.ws = carve(ws, batch, n_tokens);
@@ -291,6 +293,7 @@ int q3_prefill(const q3_model* m, const q3_kv* kv, int32_t batch, int32_t prompt
   c.start = 0;
   c.pos_dev = nullptr;
   c.dec_splits = q3v::decode_splits(batch, 1);
+  c.dec_len = 1;
   c.resid = wsp.resid;
   c.ws = wsp;
   c.s = s;
@@ -324,6 +327,7 @@ int q3_decode_step(const q3_model* m, const q3_kv* kv, int32_t batch, const int3
   c.start = 0;
   c.pos_dev = seq_lens;
   c.dec_splits = q3v::decode_splits(batch, max_len_hint);
+  c.dec_len = max_len_hint;
   c.resid = wsp.resid;
   c.ws = wsp;
   c.s = s;
@@ -372,7 +376,7 @@ int q3_attention_decode(const void* qkv, const void* q_norm, const void* k_norm,
   launch_norm_operand(nullptr, 0, 1, 0, nullptr, nullptr, nullptr, NSQ, w.tick, w.n_tick, s);  // zero the tickets
   launch_attn_decode(U(qkv), U(q_norm), U(k_norm), rope_cos, rope_sin, static_cast<uint16_t*>(k_layer),
                      static_cast<uint16_t*>(v_layer), w.apart, w.tick + 64, static_cast<uint16_t*>(out), batch,
-                     max_seq, positions, 0, q3v::decode_splits(batch, max_len_hint), s);
+                     max_seq, positions, 0, q3v::decode_splits(batch, max_len_hint), max_len_hint, s);
   return launch_status();
 }
 

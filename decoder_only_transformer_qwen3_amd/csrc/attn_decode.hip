@@ -85,6 +85,17 @@ __device__ __forceinline__ void norm_rope8(float (&f)[8], const uint16_t* __rest
   for (int e = 0; e < 8; ++e) f[e] = f[e] * cs[e] + sgn * o[e] * sn[e];
 }
 
+// K/V loads: nontemporal ones stream from HBM faster when the cache is far
+// larger than the last-level cache; ordinary ones hit there when it is not.
+template <bool NT>
+__device__ __forceinline__ u32x4 ld_kv(const uint16_t* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <bool NT>
 __global__ __launch_bounds__(256, 2) void k_attn_decode(const uint16_t* __restrict__ qkv,
                                                         const uint16_t* __restrict__ q_norm,
                                                         const uint16_t* __restrict__ k_norm,
@@ -122,7 +133,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(const uint16_t* __restri
 
   // key of A row `col` in score chain `set`: 8*(col/4) + 4*set + col%4 (see the header)
   const int krel0 = 8 * (col >> 2) + (col & 3);
-  u32x4 ka[8], va[8], kn[8], vn[8];
+  // two tiles' registers per wave: while one tile is computed, the next is in flight
+  u32x4 kA[8], vA[8], kB[8], vB[8];
 #define Q3_DEC_LOAD_TILE(T, KR, VR)                                                        \
   {                                                                                        \
     const int tb_ = k0 + (T) * DT;                                                         \
@@ -131,20 +143,19 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(const uint16_t* __restri
       key = key < last_key ? key : last_key;                                               \
       const uint16_t* kp = kbase + (size_t)key * D + 8 * grp;                              \
       _Pragma("unroll") for (int st = 0; st < 4; ++st) KR[4 * set + st] =                  \
-          *reinterpret_cast<const u32x4*>(kp + 32 * st);                                   \
+          ld_kv<NT>(kp + 32 * st);                                                         \
     }                                                                                      \
     int pb_ = tb_ + 8 * grp;                                                               \
     pb_ = pb_ < last_blk ? pb_ : last_blk;                                                 \
     const uint16_t* vp = vbase + (size_t)pb_ * D + col * VBLK;                             \
     _Pragma("unroll") for (int db = 0; db < 8; ++db) VR[db] =                              \
-        *reinterpret_cast<const u32x4*>(vp + 16 * db * VBLK);                              \
+        ld_kv<NT>(vp + 16 * db * VBLK);                                                    \
   }
 
-  int t = w;
-  if (n_tile > 0) {
-    const int t0 = t < n_tile ? t : n_tile - 1;
-    Q3_DEC_LOAD_TILE(t0, ka, va);
-  }
+  // a wave's tiles are w, w + 4, w + 8, ...; loads past the last tile re-load
+  // it (clamped), so every iteration issues the same number of loads
+  auto clamp_tile = [&](int tt) { return tt < n_tile ? tt : n_tile - 1; };
+  if (n_tile > 0) Q3_DEC_LOAD_TILE(clamp_tile(w), kA, vA);
 
   // ---- the new token: rows of the wave hold q(2g), q(2g+1), k(g), v(g); lane j dims 8j..8j+7
   {
@@ -175,11 +186,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(const uint16_t* __restri
       }
     }
   }
-  // q as the B operand: column col (heads 0, 1 only), dims 32*st + 8*grp .. +7
-  u32x4 qop[4];
-#pragma unroll
-  for (int st = 0; st < 4; ++st)
-    qop[st] = col < 2 ? *reinterpret_cast<const u32x4*>(&qs[w][col & 1][32 * st + 8 * grp]) : u32x4{0u, 0u, 0u, 0u};
+  // q as the B operand (column col, heads 0 and 1 only; dims 32*st + 8*grp .. +7)
+  // is re-read from LDS for every tile, which keeps registers for the K/V buffers
+  const uint16_t* qsrc = &qs[w][col & 1][8 * grp];
+  const bool qcol = col < 2;
 
   const float sl2 = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
   float m_run = -INFINITY, l_run = 0.f;
@@ -187,12 +197,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(const uint16_t* __restri
 #pragma unroll
   for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (; t < n_tile; t += 4) {
-    {  // prefetch the wave's next tile (clamped, so the load count per iteration is fixed)
-      int tn = t + 4;
-      tn = tn < n_tile ? tn : n_tile - 1;
-      Q3_DEC_LOAD_TILE(tn, kn, vn);
-    }
+  auto process = [&](int t, u32x4(&ka)[8], u32x4(&va)[8]) __attribute__((always_inline)) {
     const int tb = k0 + t * DT;
     if (own && p - tb < DT) {  // the tile holding the new token: take it from LDS (wave-uniform branch)
 #pragma unroll
@@ -228,8 +233,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(const uint16_t* __restri
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[st]), as_bf16x8(qop[st]), sa, 0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[4 + st]), as_bf16x8(qop[st]), sb, 0, 0, 0);
+      const u32x4 qop = qcol ? *reinterpret_cast<const u32x4*>(qsrc + 32 * st) : u32x4{0u, 0u, 0u, 0u};
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[st]), as_bf16x8(qop), sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[4 + st]), as_bf16x8(qop), sb, 0, 0, 0);
     }
     float sv[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
     float mx = -INFINITY;
@@ -263,11 +269,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(const uint16_t* __restri
 #pragma unroll
     for (int db = 0; db < 8; ++db)
       oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[db]), as_bf16x8(pb), oacc[db], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ka[i] = kn[i];
-      va[i] = vn[i];
-    }
+  };
+  // the two buffers alternate; each is refilled with the tile two steps ahead
+  // as soon as it has been consumed (no register copies between iterations)
+  for (int t = w; t < n_tile; t += 8) {
+    Q3_DEC_LOAD_TILE(clamp_tile(t + 4), kB, vB);
+    process(t, kA, vA);
+    if (t + 4 >= n_tile) break;
+    Q3_DEC_LOAD_TILE(clamp_tile(t + 8), kA, vA);
+    process(t + 4, kB, vB);
   }
 #undef Q3_DEC_LOAD_TILE
 
@@ -341,9 +351,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(const uint16_t* __restri
 void launch_attn_decode(const uint16_t* qkv, const uint16_t* q_norm, const uint16_t* k_norm, const float* rope_cos,
                         const float* rope_sin, uint16_t* k_cache, uint16_t* v_cache, float* part, int* counters,
                         uint16_t* out, int B, int max_seq, const int32_t* pos_dev, int start, int n_split,
-                        hipStream_t s) {
-  hipLaunchKernelGGL(k_attn_decode, dim3(n_split, HKV, B), dim3(256), 0, s, qkv, q_norm, k_norm, rope_cos, rope_sin,
-                     k_cache, v_cache, part, counters, out, max_seq, pos_dev, start, n_split);
+                        int max_len, hipStream_t s) {
+  // nontemporal loads once the layers' caches together (about max_len * 4 KB
+  // per sequence and layer) outgrow the 256 MB last-level cache
+  const bool nt = (double)B * max_len * HKV * D * 2 * 2 * NL > 128.0 * (1 << 20);
+  if (nt)
+    hipLaunchKernelGGL(k_attn_decode<true>, dim3(n_split, HKV, B), dim3(256), 0, s, qkv, q_norm, k_norm, rope_cos,
+                       rope_sin, k_cache, v_cache, part, counters, out, max_seq, pos_dev, start, n_split);
+  else
+    hipLaunchKernelGGL(k_attn_decode<false>, dim3(n_split, HKV, B), dim3(256), 0, s, qkv, q_norm, k_norm, rope_cos,
+                       rope_sin, k_cache, v_cache, part, counters, out, max_seq, pos_dev, start, n_split);
 }
 
 }  // namespace q3

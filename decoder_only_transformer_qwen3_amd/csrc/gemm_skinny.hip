@@ -40,25 +40,17 @@ __device__ __forceinline__ bool am_better2(float a, int ia, float b, int ib) {
   return a > b || (a == b && ia < ib);
 }
 
-template <int NB, int EPI, int U, int WV>
+template <int NB, int RB, int EPI, int U, int WV>
 __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
-  __shared__ float red[WV][NB * 16][17];
+  __shared__ float red[WV][RB][NB * 16][17];
   __shared__ float rsc[NB * 16];
   __shared__ int last_ticket;
   const uint16_t* __restrict__ X = a.X;
   const uint16_t* __restrict__ W = a.W;
   const int M = a.M, N = a.N, K = a.K, kspan = a.kspan;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, qd = l >> 4;
-  const int rb = blockIdx.x, split = blockIdx.y;
+  const int split = blockIdx.y;
   const int t = threadIdx.x;
-  int wrow;
-  if constexpr (EPI == EPI_SILU) {
-    // rows 0..7 of the block are gate rows, 8..15 the matching up rows
-    const int half = N >> 1;
-    wrow = (r < 8) ? rb * 8 + r : half + rb * 8 + (r - 8);
-  } else {
-    wrow = rb * 16 + r;
-  }
   // norm statistics are loaded first so their latency hides behind the
   // weight stream: SG threads share a row, each reading NSQ / SG partials
   // (a.ssq_n is NSQ only for up to 8 rows, so SQV below covers both layouts)
@@ -78,7 +70,20 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
     for (int i = 0; i < SQV; ++i) sq[i] = sp[i < sqv ? i : 0];
   }
   const size_t k_base = (size_t)split * kspan + qd * 8;
-  const uint16_t* wp = W + (size_t)wrow * K + k_base;
+  const uint16_t* wp[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int blk = blockIdx.x * RB + rb;  // 16-row weight block
+    int wrow;
+    if constexpr (EPI == EPI_SILU) {
+      // rows 0..7 of a block are gate rows, 8..15 the matching up rows
+      const int half = N >> 1;
+      wrow = (r < 8) ? blk * 8 + r : half + blk * 8 + (r - 8);
+    } else {
+      wrow = blk * 16 + r;
+    }
+    wp[rb] = W + (size_t)wrow * K + k_base;
+  }
   const uint16_t* xp[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -86,16 +91,21 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
     m = m < M ? m : M - 1;
     xp[nb] = X + (size_t)m * a.ldx + k_base;
   }
-  f32x4 acc[NB];
+  f32x4 acc[RB][NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = kspan >> 5;  // 32-wide k-steps in this workgroup's range
   for (int s0 = w; s0 < nsteps; s0 += WV * U) {
-    u32x4 wa[U];
+    u32x4 wa[U][RB];
     u32x4 bx[U][NB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) wa[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + (size_t)(s0 + WV * u) * 32));
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        wa[u][rb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp[rb] + (size_t)(s0 + WV * u) * 32));
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -104,13 +114,18 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u]), as_bf16x8(bx[u][nb]), acc[nb], 0, 0, 0);
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[rb][nb] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u][rb]), as_bf16x8(bx[u][nb]), acc[rb][nb], 0, 0, 0);
   }
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[w][nb * 16 + r][4 * qd + i] = acc[nb][i];
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[w][rb][nb * 16 + r][4 * qd + i] = acc[rb][nb][i];
   if (scaled) {
     float ss = 0.f;
 #pragma unroll
@@ -121,33 +136,35 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
   }
   __syncthreads();
   if constexpr (EPI == EPI_SILU) {
-    // out[m][rb*8 + j] = silu(gate) * up
-    for (int e = t; e < NB * 16 * 8; e += 256) {
-      const int m = e >> 3, j = e & 7;
+    // out[m][blk*8 + j] = silu(gate) * up
+    for (int e = t; e < RB * NB * 16 * 8; e += 64 * WV) {
+      const int rb = e / (NB * 16 * 8), m = (e >> 3) % (NB * 16), j = e & 7;
       if (m >= M) continue;
       const float rs = scaled ? rsc[m] : 1.0f;
       float gsum = 0.f, usum = 0.f;
 #pragma unroll
       for (int ww = 0; ww < WV; ++ww) {
-        gsum += red[ww][m][j];
-        usum += red[ww][m][8 + j];
+        gsum += red[ww][rb][m][j];
+        usum += red[ww][rb][m][8 + j];
       }
       gsum *= rs;
       usum *= rs;
       const float sg = gsum / (1.0f + __expf(-gsum));
-      reinterpret_cast<uint16_t*>(a.out)[(size_t)m * a.ldo + rb * 8 + j] = (uint16_t)f2bf(sg * usum);
+      reinterpret_cast<uint16_t*>(a.out)[(size_t)m * a.ldo + (blockIdx.x * RB + rb) * 8 + j] = (uint16_t)f2bf(sg * usum);
     }
   } else {
-    if (t < NB * 16 * 4) {
-      const int m = t >> 2, ng = t & 3;
-      if (m < M) {  // whole groups of 4 lanes share m, so the shuffles below stay inside active groups
+    for (int e = t; e < RB * NB * 16 * 4; e += 64 * WV) {
+      const int rb = e / (NB * 16 * 4), m = (e >> 2) % (NB * 16), ng = e & 3;
+      const int blk = blockIdx.x * RB + rb;
+      // whole groups of 4 lanes share (rb, m), so the shuffles below stay inside active groups
+      if (m < M) {
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ww = 0; ww < WV; ++ww)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] += red[ww][m][4 * ng + i];
+          for (int i = 0; i < 4; ++i) v[i] += red[ww][rb][m][4 * ng + i];
         if (scaled) v *= rsc[m];
-        const int n = rb * 16 + 4 * ng;
+        const int n = blk * 16 + 4 * ng;
         void* const out = a.out;
         const int ldo = a.ldo;
         if constexpr (EPI == EPI_BF16) {
@@ -178,7 +195,7 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
             }
           }
           if (ng == 0) {
-            float2* ap = reinterpret_cast<float2*>(a.amax_part) + (size_t)m * gridDim.x + rb;
+            float2* ap = reinterpret_cast<float2*>(a.amax_part) + (size_t)m * (N >> 4) + blk;
             *ap = make_float2(bv, __int_as_float(bi));
           }
         } else if constexpr (EPI == EPI_ADD_F32) {
@@ -193,11 +210,11 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
             *reinterpret_cast<u32x2*>(a.hg + (size_t)m * N + n) = o;
             float ss = (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
             if (a.ssq_n == NSQ) {
-              a.ssq_out[(size_t)m * NSQ + 4 * rb + ng] = ss;
+              a.ssq_out[(size_t)m * NSQ + 4 * blk + ng] = ss;
             } else {
               ss += __shfl_xor(ss, 1, 64);  // the 4 lanes of row m are whole and active
               ss += __shfl_xor(ss, 2, 64);
-              if (ng == 0) a.ssq_out[(size_t)m * NSQ_BLK + rb] = ss;
+              if (ng == 0) a.ssq_out[(size_t)m * NSQ_BLK + blk] = ss;
             }
           }
         } else {  // EPI_PARTIAL (device-coherent stores: the last workgroup of the block reads them)
@@ -210,15 +227,16 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
   }
   if constexpr (EPI == EPI_PARTIAL) {
     if (a.resid == nullptr) return;
-    // ticket: the last workgroup of this column block finishes it
+    // ticket: the last workgroup of this column range finishes it
     vm_drain();
     __syncthreads();
-    if (t == 0) last_ticket = atomicAdd(a.counters + rb, 1) == (int)gridDim.y - 1;
+    if (t == 0) last_ticket = atomicAdd(a.counters + blockIdx.x, 1) == (int)gridDim.y - 1;
     __syncthreads();
     if (!last_ticket) return;
-    if (t < NB * 16 * 4) {
-      const int m = t >> 2, ng = t & 3;
-      const int n = rb * 16 + 4 * ng;
+    for (int e = t; e < RB * NB * 16 * 4; e += 64 * WV) {
+      const int rb = e / (NB * 16 * 4), m = (e >> 2) % (NB * 16), ng = e & 3;
+      const int blk = blockIdx.x * RB + rb;
+      const int n = blk * 16 + 4 * ng;
       float ss = 0.f;
       if (m < M) {
         f32x4* rp = reinterpret_cast<f32x4*>(a.resid + (size_t)m * N + n);
@@ -240,15 +258,15 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
       }
       if (a.gamma) {
         if (a.ssq_n == NSQ) {
-          if (m < M) a.ssq_out[(size_t)m * NSQ + 4 * rb + ng] = ss;
+          if (m < M) a.ssq_out[(size_t)m * NSQ + 4 * blk + ng] = ss;
         } else {
           ss += __shfl_xor(ss, 1, 64);  // groups of 4 lanes share m and are whole inside the wave
           ss += __shfl_xor(ss, 2, 64);
-          if (m < M && ng == 0) a.ssq_out[(size_t)m * NSQ_BLK + rb] = ss;
+          if (m < M && ng == 0) a.ssq_out[(size_t)m * NSQ_BLK + blk] = ss;
         }
       }
     }
-    if (t == 0) a.counters[rb] = 0;  // ready for the next call
+    if (t == 0) a.counters[blockIdx.x] = 0;  // ready for the next call
   }
 }
 
@@ -329,29 +347,69 @@ void launch_gemv_resid(const uint16_t* X, const uint16_t* W, int K, float* resid
   else launch_gemv_mr<8>(X, W, K, resid, M, gamma, hg, ssq_out, s);
 }
 
-template <int NB, int EPI, int WV>
+#ifndef Q3_PARTIAL_RB
+#define Q3_PARTIAL_RB(epi) 1
+#endif
+
+template <int NB, int RB, int EPI, int WV, int U>
+static void launch_k(const SkinnyArgs& a, int gx, int n_split, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm_skinny<NB, RB, EPI, U, WV>), dim3(gx, n_split), dim3(64 * WV), 0, s, a);
+}
+
+// Unroll U: as many 32-wide k-steps per wave and iteration as divide the
+// workgroup's range, with at most 24 (RB > 1) or 36 (RB == 1, NB <= 2)
+// 16-byte loads per lane in flight.  Every caller keeps the K range a
+// multiple of 32 * WV (q3_linear: K % 512 == 0; the residual projections'
+// splits: 512-wide ranges), so the U = 1 kernel always fits.
+template <int NB, int RB, int EPI, int WV>
 static void launch_wv(const SkinnyArgs& a, int gx, int n_split, hipStream_t s) {
   const int nsteps = a.kspan >> 5;  // 32-wide k-steps per workgroup
-  if (NB <= 2 && nsteps % (WV * 12) == 0)
-    hipLaunchKernelGGL((k_gemm_skinny<NB, EPI, (NB <= 2 ? 12 : 4), WV>), dim3(gx, n_split), dim3(64 * WV), 0, s, a);
-  else if (nsteps % (WV * 8) == 0)
-    hipLaunchKernelGGL((k_gemm_skinny<NB, EPI, 8, WV>), dim3(gx, n_split), dim3(64 * WV), 0, s, a);
+  constexpr int LOADS = (RB == 1 && NB <= 2) ? 36 : 24;
+  if (12 * (RB + NB) <= LOADS && nsteps % (WV * 12) == 0)
+    launch_k<NB, RB, EPI, WV, (12 * (RB + NB) <= LOADS ? 12 : 1)>(a, gx, n_split, s);
+  else if (8 * (RB + NB) <= LOADS && nsteps % (WV * 8) == 0)
+    launch_k<NB, RB, EPI, WV, (8 * (RB + NB) <= LOADS ? 8 : 1)>(a, gx, n_split, s);
+  else if (4 * (RB + NB) <= LOADS && nsteps % (WV * 4) == 0)
+    launch_k<NB, RB, EPI, WV, (4 * (RB + NB) <= LOADS ? 4 : 1)>(a, gx, n_split, s);
+  else if (nsteps % (WV * 2) == 0)
+    launch_k<NB, RB, EPI, WV, 2>(a, gx, n_split, s);
   else
-    hipLaunchKernelGGL((k_gemm_skinny<NB, EPI, 4, WV>), dim3(gx, n_split), dim3(64 * WV), 0, s, a);
+    launch_k<NB, RB, EPI, WV, 1>(a, gx, n_split, s);
+}
+
+template <int NB, int RB, int EPI>
+static void launch_rb(const SkinnyArgs& a, int n_split, hipStream_t s) {
+  const int gx = ((EPI == EPI_SILU) ? (a.N / 2) / 8 : a.N / 16) / RB;
+  // The residual-add projections run one K range per 16 columns, so they use
+  // 8 waves per workgroup to keep enough weight bytes in flight.
+  if constexpr (EPI == EPI_ADD_F32 && RB == 1) {
+    if (((a.kspan >> 5) % 32) == 0) {
+      launch_wv<NB, RB, EPI, 8>(a, gx, n_split, s);
+      return;
+    }
+  }
+  launch_wv<NB, RB, EPI, 4>(a, gx, n_split, s);
+}
+
+// 16-row weight blocks per workgroup.  Every workgroup reads the
+// activation rows of its K range once, so from 16 rows on (where that read
+// costs as much as the weights) more weight rows per workgroup pay off, as
+// long as enough workgroups remain to keep every CU streaming: the gate|up
+// projection (384 blocks) takes 2, the vocabulary projection (9496) takes 4.
+static int rows_blocks(const SkinnyArgs& a, Epi epi) {
+  if (a.M < 16) return 1;
+  if (epi == EPI_SILU) return 2;
+  if (a.N >= 16384) return 4;
+  return Q3_PARTIAL_RB(epi);
 }
 
 template <int NB, int EPI>
 static void launch_nb(const SkinnyArgs& a, int n_split, hipStream_t s) {
-  const int gx = (EPI == EPI_SILU) ? (a.N / 2) / 8 : a.N / 16;
-  // The residual-add projections run one K range per 16 columns, so they use
-  // 8 waves per workgroup to keep enough weight bytes in flight.
-  if constexpr (EPI == EPI_ADD_F32) {
-    if (((a.kspan >> 5) % 32) == 0) {
-      launch_wv<NB, EPI, 8>(a, gx, n_split, s);
-      return;
-    }
+  switch (rows_blocks(a, static_cast<Epi>(EPI))) {
+    case 4: launch_rb<NB, 4, EPI>(a, n_split, s); break;
+    case 2: launch_rb<NB, 2, EPI>(a, n_split, s); break;
+    default: launch_rb<NB, 1, EPI>(a, n_split, s); break;
   }
-  launch_wv<NB, EPI, 4>(a, gx, n_split, s);
 }
 
 template <int EPI>
