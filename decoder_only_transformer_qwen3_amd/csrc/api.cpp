@@ -60,7 +60,7 @@ struct LayerCtx {
   int B, T, max_seq, start;
   const int32_t* pos_dev;  // per-sequence start positions on the device (decode), or null
   int dec_splits;          // decode-attention splits (T == 1 only)
-  int dec_len;             // bound on the sequences' lengths after the step (T == 1 only)
+  bool dec_stream;         // decode attention in its streaming configuration (T == 1 only)
   float* resid;
   const uint16_t* gamma_next;  // gain of the norm that follows this layer, or null
   Ws ws;
@@ -136,7 +136,7 @@ void run_layer(const LayerCtx& c) {
   // q/k RMSNorm + RoPE, K/V into the cache, causal GQA attention
   if (c.T == 1) {
     launch_attn_decode(c.ws.qkv, U(w->q_norm), U(w->k_norm), c.cos, c.sin, c.kl, c.vl, c.ws.apart, c.ws.tick + 64,
-                       c.ws.ao, c.B, c.max_seq, c.pos_dev, c.start, c.dec_splits, c.dec_len, c.s);
+                       c.ws.ao, c.B, c.max_seq, c.pos_dev, c.start, c.dec_splits, c.dec_stream, c.s);
   } else {
     launch_qknorm_rope(c.ws.qkv, U(w->q_norm), U(w->k_norm), c.cos, c.sin, c.ws.qr, c.kl, c.vl, c.B, c.T,
                        c.max_seq, c.pos_dev, c.start, c.s);
@@ -260,7 +260,7 @@ int q3_layer_forward(const q3_layer_weights* w, const float* rope_cos, const flo
   c.start = start_pos;
   c.pos_dev = nullptr;
   c.dec_splits = q3v::decode_splits(batch, start_pos + 1);
-  c.dec_len = start_pos + 1;
+  c.dec_stream = q3v::decode_streaming(batch, start_pos + 1);
   c.resid = residual;
   c.gamma_next = nullptr;
   c.ws = carve(ws, batch, n_tokens);
@@ -293,7 +293,7 @@ int q3_prefill(const q3_model* m, const q3_kv* kv, int32_t batch, int32_t prompt
   c.start = 0;
   c.pos_dev = nullptr;
   c.dec_splits = q3v::decode_splits(batch, 1);
-  c.dec_len = 1;
+  c.dec_stream = false;
   c.resid = wsp.resid;
   c.ws = wsp;
   c.s = s;
@@ -327,7 +327,7 @@ int q3_decode_step(const q3_model* m, const q3_kv* kv, int32_t batch, const int3
   c.start = 0;
   c.pos_dev = seq_lens;
   c.dec_splits = q3v::decode_splits(batch, max_len_hint);
-  c.dec_len = max_len_hint;
+  c.dec_stream = q3v::decode_streaming(batch, max_len_hint);
   c.resid = wsp.resid;
   c.ws = wsp;
   c.s = s;
@@ -376,7 +376,8 @@ int q3_attention_decode(const void* qkv, const void* q_norm, const void* k_norm,
   launch_norm_operand(nullptr, 0, 1, 0, nullptr, nullptr, nullptr, NSQ, w.tick, w.n_tick, s);  // zero the tickets
   launch_attn_decode(U(qkv), U(q_norm), U(k_norm), rope_cos, rope_sin, static_cast<uint16_t*>(k_layer),
                      static_cast<uint16_t*>(v_layer), w.apart, w.tick + 64, static_cast<uint16_t*>(out), batch,
-                     max_seq, positions, 0, q3v::decode_splits(batch, max_len_hint), max_len_hint, s);
+                     max_seq, positions, 0, q3v::decode_splits(batch, max_len_hint),
+                     q3v::decode_streaming(batch, max_len_hint), s);
   return launch_status();
 }
 

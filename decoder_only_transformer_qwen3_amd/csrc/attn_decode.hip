@@ -12,7 +12,8 @@
 // dims (i, i+64) sit in lanes j and j^8 (a row rotate by 8).
 //
 // Grid (split, KV head g, sequence b); each workgroup reads its key range of
-// K and V once for both query heads 2g, 2g+1.  Its 4 waves take 32-key
+// K and V once for both query heads 2g, 2g+1.  Its waves (8 when the
+// caches are far larger than the last-level cache, else 4) take 32-key
 // tiles round-robin and each keeps its own online softmax, on
 // v_mfma_f32_16x16x32_bf16 (lane l: A row l%16, B column l%16, k-slot
 // (l/16, j); C column l%16, rows 4(l/16)+i):
@@ -28,7 +29,7 @@
 // while a tile is computed.  The split that owns position p writes the new
 // K/V into the cache and takes them from LDS rather than from the cache.
 //
-// The 4 waves combine in LDS; each split writes unnormalised (o, m, l) in
+// The waves combine in LDS; each split writes unnormalised (o, m, l) in
 // the log2 domain; the last split to finish for a (b, g) (atomic ticket)
 // merges them with log-sum-exp rescaling and writes the two heads' bf16
 // outputs.  The key range of a split follows from the sequence's own device
@@ -95,8 +96,8 @@ __device__ __forceinline__ u32x4 ld_kv(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
-template <bool NT>
-__global__ __launch_bounds__(256, 2) void k_attn_decode(const uint16_t* __restrict__ qkv,
+template <bool NT, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_decode(const uint16_t* __restrict__ qkv,
                                                         const uint16_t* __restrict__ q_norm,
                                                         const uint16_t* __restrict__ k_norm,
                                                         const float* __restrict__ rope_cos,
@@ -106,11 +107,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(const uint16_t* __restri
                                                         int* __restrict__ counters, uint16_t* __restrict__ out,
                                                         int max_seq, const int32_t* __restrict__ pos_dev, int start,
                                                         int n_split) {
-  __shared__ __attribute__((aligned(16))) uint16_t qs[4][2][D];  // per wave: rotated q of heads 2g, 2g+1
-  __shared__ __attribute__((aligned(16))) uint16_t knew[4][D];   // per wave: the new key (rotated)
-  __shared__ __attribute__((aligned(16))) uint16_t vnew[4][D];   // per wave: the new value
-  __shared__ float wo[4][2][D];
-  __shared__ float wml[4][2][2];
+  __shared__ __attribute__((aligned(16))) uint16_t qs[NW][2][D];  // per wave: rotated q of heads 2g, 2g+1
+  __shared__ __attribute__((aligned(16))) uint16_t knew[NW][D];   // per wave: the new key (rotated)
+  __shared__ __attribute__((aligned(16))) uint16_t vnew[NW][D];   // per wave: the new value
+  __shared__ float wo[NW][2][D];
+  __shared__ float wml[NW][2][2];
   __shared__ float mls[2][DEC_SPLIT_CAP][2];
   __shared__ int last_ticket;
 
@@ -272,12 +273,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(const uint16_t* __restri
   };
   // the two buffers alternate; each is refilled with the tile two steps ahead
   // as soon as it has been consumed (no register copies between iterations)
-  for (int t = w; t < n_tile; t += 8) {
-    Q3_DEC_LOAD_TILE(clamp_tile(t + 4), kB, vB);
+  for (int t = w; t < n_tile; t += 2 * NW) {
+    Q3_DEC_LOAD_TILE(clamp_tile(t + NW), kB, vB);
     process(t, kA, vA);
-    if (t + 4 >= n_tile) break;
-    Q3_DEC_LOAD_TILE(clamp_tile(t + 8), kA, vA);
-    process(t + 4, kB, vB);
+    if (t + NW >= n_tile) break;
+    Q3_DEC_LOAD_TILE(clamp_tile(t + 2 * NW), kA, vA);
+    process(t + NW, kB, vB);
   }
 #undef Q3_DEC_LOAD_TILE
 
@@ -295,28 +296,32 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(const uint16_t* __restri
     }
   }
   __syncthreads();
-  const int hh = tid >> 7, d = tid & 127;
+  // threads 0..255 finish (head hh, dim d); the others mirror them and store nothing
+  const int hh = (tid >> 7) & 1, d = tid & 127;
+  const bool fin = tid < 2 * D;
   {
     float mm = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) mm = fmaxf(mm, wml[ww][hh][0]);
+    for (int ww = 0; ww < NW; ++ww) mm = fmaxf(mm, wml[ww][hh][0]);
     float o = 0.f, lsum = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       const float mw = wml[ww][hh][0];
       const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - mm);
       o += f * wo[ww][hh][d];
       lsum += f * wml[ww][hh][1];
     }
     if (n_split == 1) {  // a single split is already the whole softmax
-      out[(size_t)b * QDIM + (2 * g + hh) * D + d] = (uint16_t)f2bf(o / lsum);
+      if (fin) out[(size_t)b * QDIM + (2 * g + hh) * D + d] = (uint16_t)f2bf(o / lsum);
       return;
     }
-    float* dst = part + (((size_t)b * HQ + 2 * g + hh) * n_split + s) * PART_STRIDE;
-    st_dev(dst + d, o);
-    if (d == 0) {
-      st_dev(dst + D, mm);
-      st_dev(dst + D + 1, lsum);
+    if (fin) {
+      float* dst = part + (((size_t)b * HQ + 2 * g + hh) * n_split + s) * PART_STRIDE;
+      st_dev(dst + d, o);
+      if (d == 0) {
+        st_dev(dst + D, mm);
+        st_dev(dst + D + 1, lsum);
+      }
     }
   }
 
@@ -333,6 +338,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(const uint16_t* __restri
     mls[h][sp][1] = ld_dev(src + D + 1);
   }
   __syncthreads();
+  if (!fin) return;
   float mm = -INFINITY;
   for (int sp = 0; sp < n_split; ++sp) mm = fmaxf(mm, mls[hh][sp][0]);
   const float* src = part + ((size_t)b * HQ + 2 * g + hh) * n_split * PART_STRIDE + d;
@@ -351,16 +357,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(const uint16_t* __restri
 void launch_attn_decode(const uint16_t* qkv, const uint16_t* q_norm, const uint16_t* k_norm, const float* rope_cos,
                         const float* rope_sin, uint16_t* k_cache, uint16_t* v_cache, float* part, int* counters,
                         uint16_t* out, int B, int max_seq, const int32_t* pos_dev, int start, int n_split,
-                        int max_len, hipStream_t s) {
-  // nontemporal loads once the layers' caches together (about max_len * 4 KB
-  // per sequence and layer) outgrow the 256 MB last-level cache
-  const bool nt = (double)B * max_len * HKV * D * 2 * 2 * NL > 128.0 * (1 << 20);
-  if (nt)
-    hipLaunchKernelGGL(k_attn_decode<true>, dim3(n_split, HKV, B), dim3(256), 0, s, qkv, q_norm, k_norm, rope_cos,
-                       rope_sin, k_cache, v_cache, part, counters, out, max_seq, pos_dev, start, n_split);
+                        bool streaming, hipStream_t s) {
+  // streaming: caches far larger than the last-level cache, 8-wave workgroups
+  // with nontemporal loads; otherwise 4-wave workgroups with ordinary loads
+  if (streaming)
+    hipLaunchKernelGGL((k_attn_decode<true, 8>), dim3(n_split, HKV, B), dim3(512), 0, s, qkv, q_norm, k_norm,
+                       rope_cos, rope_sin, k_cache, v_cache, part, counters, out, max_seq, pos_dev, start, n_split);
   else
-    hipLaunchKernelGGL(k_attn_decode<false>, dim3(n_split, HKV, B), dim3(256), 0, s, qkv, q_norm, k_norm, rope_cos,
-                       rope_sin, k_cache, v_cache, part, counters, out, max_seq, pos_dev, start, n_split);
+    hipLaunchKernelGGL((k_attn_decode<false, 4>), dim3(n_split, HKV, B), dim3(256), 0, s, qkv, q_norm, k_norm,
+                       rope_cos, rope_sin, k_cache, v_cache, part, counters, out, max_seq, pos_dev, start, n_split);
 }
 
 }  // namespace q3

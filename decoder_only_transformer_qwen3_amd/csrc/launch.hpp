@@ -95,7 +95,7 @@ void launch_attn_prefill(const uint16_t* q, const uint16_t* k_cache, const uint1
 void launch_attn_decode(const uint16_t* qkv, const uint16_t* q_norm, const uint16_t* k_norm, const float* rope_cos,
                         const float* rope_sin, uint16_t* k_cache, uint16_t* v_cache, float* part, int* counters,
                         uint16_t* out, int B, int max_seq, const int32_t* pos_dev, int start, int n_split,
-                        int max_len, hipStream_t s);
+                        bool streaming, hipStream_t s);
 
 // Final greedy choice from the lm_head's per-block (max, argmax) partials:
 // part is [rows][n_part] of (float value, int index).  seq_mode as below.

@@ -36,13 +36,22 @@ WsLayout ws_layout(int32_t batch, int32_t n_tokens) {
   return L;
 }
 
+bool decode_streaming(int32_t batch, int32_t ctx) {
+  // the layers' caches together (4 KB per position, sequence and layer)
+  // outgrow the 256 MB last-level cache
+  return (double)batch * ctx * 4096.0 * Q3_N_LAYERS > 128.0 * (1 << 20);
+}
+
 int decode_splits(int32_t batch, int32_t ctx) {
-  // about two workgroups per CU in one wave of launches, at least 256 keys
-  // (two 32-key tiles per wave) per split
-  const int target_workgroups = 512;
+  // one wave of launches: streaming, one 8-wave workgroup per CU with at
+  // least 512 keys (two 32-key tiles per wave) per split; otherwise two
+  // 4-wave workgroups per CU with at least 256 keys per split
+  const bool streaming = decode_streaming(batch, ctx);
+  const int target_workgroups = streaming ? 256 : 512;
+  const int min_keys = streaming ? 512 : 256;
   const int pairs = batch * Q3_N_KV_HEADS;
   int s = (target_workgroups + pairs - 1) / pairs;
-  const int cap = (ctx + 255) / 256;
+  const int cap = (ctx + min_keys - 1) / min_keys;
   if (s > cap) s = cap;
   if (s > DEC_SPLIT_MAX) s = DEC_SPLIT_MAX;
   if (s < 1) s = 1;

@@ -26,7 +26,10 @@ WsLayout ws_layout(int32_t batch, int32_t n_tokens);
 // Workgroup tickets in the workspace: 64 column blocks + 8 per sequence.
 inline int ticket_count(int32_t batch) { return 64 + 8 * batch; }
 
-// Number of decode-attention splits for `batch` sequences of at most `ctx` keys.
+// Decode attention over `batch` sequences of at most `ctx` keys: whether it
+// runs in its streaming configuration (caches far larger than the
+// last-level cache), and its number of splits.
+bool decode_streaming(int32_t batch, int32_t ctx);
 int decode_splits(int32_t batch, int32_t ctx);
 
 int check_layer_call(const q3_layer_weights* w, const float* rope_cos, const float* rope_sin, const void* k_layer,

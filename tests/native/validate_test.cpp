@@ -47,11 +47,15 @@ int main() {
   EXPECT_EQ(L1.resid % 256, 0); EXPECT_EQ(L1.h % 256, 0); EXPECT_EQ(L1.fh % 256, 0);
   EXPECT_EQ(L3.total >= (size_t)8 * 4096 * (1024 * 4 + 1024 * 2 + 4096 * 2 + 2048 * 4 + 3072 * 2), 1);
   // ---- decode splits
-  EXPECT_EQ(decode_splits(32, 2176), 2);
-  EXPECT_EQ(decode_splits(4, 32832), 16);
+  EXPECT_EQ(decode_streaming(1, 192), 0);     // 22 MB of caches: stays in the last-level cache
+  EXPECT_EQ(decode_streaming(32, 2176), 1);
+  EXPECT_EQ(decode_splits(32, 2176), 1);      // 256 (sequence, KV head) pairs fill the CUs
+  EXPECT_EQ(decode_splits(4, 32832), 8);
   EXPECT_EQ(decode_splits(1, 1), 1);
   EXPECT_EQ(decode_splits(1, 192), 1);
-  EXPECT_EQ(decode_splits(1, 40960), 64);
+  EXPECT_EQ(decode_streaming(2, 512), 0);
+  EXPECT_EQ(decode_splits(2, 512), 2);        // not streaming: at least 256 keys per split
+  EXPECT_EQ(decode_splits(1, 40960), 32);
   for (int b = 1; b <= 64; ++b)
     for (int c = 1; c < 40961; c += 997) {
       const int s = decode_splits(b, c);
