@@ -58,6 +58,10 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-iters", type=int, default=200)
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="time only the workload's dominant kernel (the run the counter passes profile)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="copy 1 GiB on the device three times (counter calibration) and exit")
     return ap.parse_args()
 
 
@@ -120,7 +124,7 @@ LMHEAD_PARAMS = 151936 * 1024
 KV_BYTES_PER_POS = 28 * 8 * 128 * 2 * 2  # K and V rows of one position, all layers and KV heads
 
 
-def _time_launches(torch, fn, iters, reps=10):
+def _time_launches(torch, fn, iters, reps=10, use_graph=True):
     """Average duration (s) of one fn() launch: `reps` back-to-back launches
     are captured as one HIP graph, which is replayed between HIP events on
     the current stream (the stream the kernels run on), so host launch
@@ -132,10 +136,12 @@ def _time_launches(torch, fn, iters, reps=10):
     torch.cuda.synchronize()
     n_rep = max(1, iters // reps)
     try:
+        if not use_graph:
+            raise RuntimeError("eager launches requested")
         g = capture(torch, lambda: [fn() for _ in range(reps)])
         per_replay = reps
         run = g.replay
-    except Exception:  # pragma: no cover
+    except Exception:
         per_replay, run = 1, fn
         n_rep = iters
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_rep)]
@@ -147,7 +153,7 @@ def _time_launches(torch, fn, iters, reps=10):
     return float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n_rep)])) * 1e-3 / per_replay
 
 
-def dominant_kernel(torch, B, dev, dm, r, workload, iters):
+def dominant_kernel(torch, B, dev, dm, r, workload, iters, use_graph=True):
     """Roofline of the kernel that takes most of the workload's step time
     (per the rocprofv3 kernel summaries), timed alone with HIP events on the
     stream it runs on, at the workload's shape and launch configuration:
@@ -199,14 +205,50 @@ def dominant_kernel(torch, B, dev, dm, r, workload, iters):
         algo = float(batch * (T * (T + 1) // 2) * 4 * B.HEAD_DIM * B.N_HEADS)
         name, bound, per = f"k_attn_prefill ({batch} x {T}, one layer)", "mfma", \
             "causal flops: 4 * 128 * 16 per (query, key <= query) pair"
-    t = _time_launches(torch, fn, iters, reps)
+    t = _time_launches(torch, fn, iters, reps, use_graph)
     if bound == "hbm":
         achieved, peak, unit = algo / t / 1e9, HBM_PEAK_GBS, "GB/s"
     else:
         achieved, peak, unit = algo / t / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+    traffic = measured_traffic(workload)
     return {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": None, "kernel": name,
+            "frac": round(achieved / peak, 4), "traffic": round(traffic) if traffic else None, "kernel": name,
             "avg_launch_us": round(t * 1e6, 2), "algorithmic_per_launch": algo, "algorithmic_unit": per}
+
+
+# Source files of each workload's dominant kernel.  The HBM traffic measured
+# by the counter passes (profiles/traffic.json) belongs to one version of the
+# kernel: it is reported only while these files hash to the recorded digest.
+KERNEL_SOURCES = {
+    "prefill128_decode64": ["gemm_skinny.hip", "common.hpp"],
+    "decode_b32_ctx2048": ["attn_decode.hip", "common.hpp"],
+    "decode_b4_ctx32768": ["attn_decode.hip", "common.hpp"],
+    "prefill_8x4096": ["attn_prefill.hip", "common.hpp"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_digest(workload):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[workload]:
+        with open(os.path.join(ROOT, "decoder_only_transformer_qwen3_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the dominant kernel (calibrated FETCH_SIZE +
+    WRITE_SIZE counters), or None when no counters were taken for the
+    current version of its source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != kernel_source_digest(workload):
+        return None
+    return float(rec["fetch_bytes_per_launch"]) + float(rec["write_bytes_per_launch"])
 
 
 def step_roofline(workload, pre_ms, dec_ms):
@@ -292,11 +334,25 @@ def main():
     from decoder_only_transformer_qwen3_amd import inputs as I
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        x = torch.empty(1 << 28, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": 4 << 28, "bytes_written": 4 << 28,
+                          "launches": 3}), flush=True)
+        return
     batch, T, steps, prefill_timed = WORKLOADS[args.workload]
     log(f"[bench] workload {args.workload}: batch {batch}, prompt {T}, decode steps {steps}")
     bits = I.model_weights(0)
     dm = dev.DeviceModel(bits)
     r = Runner(torch, B, dev, dm, batch, T, steps)
+    if args.kernel_only:  # (the cache is not prefilled: the kernels stream it all the same)
+        rl = dominant_kernel(torch, B, dev, dm, r, args.workload, args.kernel_iters, not args.no_graph)
+        rl["source_sha256"] = kernel_source_digest(args.workload)
+        print(json.dumps({"workload": args.workload, "roofline": rl}), flush=True)
+        return
 
     use_graph = not args.no_graph
     # setup prefill (untimed); decode-only workloads restart from this state each step
