@@ -65,12 +65,13 @@ _linear = _sig("q3_linear", ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
 _attn_prefill = _sig("q3_attention_prefill", ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp)
 _attn_decode = _sig("q3_attention_decode", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
                     _i32, _vp, _vp, _sz, _vp)
+_rope_conv = _sig("q3_rope_interleaved_to_half", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp)
 
 Q3_EPI_STORE_BF16, Q3_EPI_STORE_F32, Q3_EPI_ADD_F32, Q3_EPI_SILU_GATE = 0, 1, 2, 3
 
 EXPORTS = ("q3_status_str", "q3_rope_table_host", "q3_workspace_bytes", "q3_layer_forward",
            "q3_prefill", "q3_decode_step", "q3_argmax", "q3_linear", "q3_attention_prefill",
-           "q3_attention_decode")
+           "q3_attention_decode", "q3_rope_interleaved_to_half")
 
 
 class Q3Error(RuntimeError):
@@ -179,4 +180,13 @@ def q3_attention_decode(qkv, q_norm, k_norm, rope_cos, rope_sin, k_layer, v_laye
                       _stream(stream))
     if check:
         _check(st, "q3_attention_decode")
+    return st
+
+
+def q3_rope_interleaved_to_half(w_qkv, q_norm, k_norm, w_qkv_out, q_norm_out, k_norm_out, stream=None,
+                                check=True) -> int:
+    st = _rope_conv(_ptr(w_qkv), _ptr(q_norm), _ptr(k_norm), _ptr(w_qkv_out), _ptr(q_norm_out), _ptr(k_norm_out),
+                    _stream(stream))
+    if check:
+        _check(st, "q3_rope_interleaved_to_half")
     return st

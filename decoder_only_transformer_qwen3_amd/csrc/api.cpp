@@ -388,4 +388,14 @@ int q3_argmax(const float* logits, int32_t rows, int32_t vocab, int64_t row_stri
   return launch_status();
 }
 
+int q3_rope_interleaved_to_half(const void* w_qkv, const void* q_norm, const void* k_norm, void* w_qkv_out,
+                                void* q_norm_out, void* k_norm_out, void* stream) {
+  const int st = q3v::check_rope_convert_call(w_qkv, q_norm, k_norm, w_qkv_out, q_norm_out, k_norm_out);
+  if (st != Q3_OK) return st;
+  launch_rope_pair_permute(U(w_qkv), U(q_norm), U(k_norm), static_cast<uint16_t*>(w_qkv_out),
+                           static_cast<uint16_t*>(q_norm_out), static_cast<uint16_t*>(k_norm_out),
+                           static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
 }  // extern "C"

@@ -406,4 +406,35 @@ void launch_argmax_partials(const void* part, int rows, int n_part, int32_t* out
                      out_idx, seq_lens, seq_mode, seq_val);
 }
 
+// ---------------------------------------------------------------------------
+// Interleaved rotary pairs -> half-swap pairs: destination dim j of a q or k
+// head takes source dim P(j) = 2j (j < 64), 2(j - 64) + 1 (j >= 64), so the
+// half-swap pair (j, j + 64) is the interleaved pair (2j, 2j + 1).
+// Blocks 0..4095 copy one weight row each (128 threads x 16 B); block 4096
+// permutes the two gains.
+__device__ __forceinline__ int half_from_interleaved(int j) { return j < D / 2 ? 2 * j : 2 * (j - D / 2) + 1; }
+
+__global__ __launch_bounds__(128) void k_rope_pair_permute(const uint16_t* __restrict__ w_qkv,
+                                                           const uint16_t* __restrict__ q_norm,
+                                                           const uint16_t* __restrict__ k_norm,
+                                                           uint16_t* __restrict__ w_out, uint16_t* __restrict__ qn_out,
+                                                           uint16_t* __restrict__ kn_out) {
+  const int r = blockIdx.x, t = threadIdx.x;
+  if (r < QKV_N) {
+    // rows 0..3071 are q and k heads of 128 rows; v rows are copied as they are
+    const int src = r < QDIM + HKV * D ? (r / D) * D + half_from_interleaved(r % D) : r;
+    reinterpret_cast<u32x4*>(w_out + (size_t)r * C)[t] = reinterpret_cast<const u32x4*>(w_qkv + (size_t)src * C)[t];
+  } else {
+    qn_out[t] = q_norm[half_from_interleaved(t)];
+    kn_out[t] = k_norm[half_from_interleaved(t)];
+  }
+}
+
+void launch_rope_pair_permute(const uint16_t* w_qkv, const uint16_t* q_norm, const uint16_t* k_norm,
+                              uint16_t* w_out, uint16_t* qn_out, uint16_t* kn_out, hipStream_t s) {
+  static_assert(C / 8 == 128 && D == 128, "one 128-thread block per 1024-wide row, one thread per gain");
+  hipLaunchKernelGGL(k_rope_pair_permute, dim3(QKV_N + 1), dim3(128), 0, s, w_qkv, q_norm, k_norm, w_out, qn_out,
+                     kn_out);
+}
+
 }  // namespace q3

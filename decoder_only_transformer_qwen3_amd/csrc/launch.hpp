@@ -82,6 +82,11 @@ void launch_gemv_resid(const uint16_t* X, const uint16_t* W, int K, float* resid
 void launch_gemm_skinny(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo,
                         int n_split, Epi epi, hipStream_t s, void* amax_part = nullptr);
 
+// Copy of the merged q|k|v rows and the q/k gains with the q and k rows of
+// every head (and the gains) permuted by P(j) = 2j (j < 64), 2(j-64)+1.
+void launch_rope_pair_permute(const uint16_t* w_qkv, const uint16_t* q_norm, const uint16_t* k_norm,
+                              uint16_t* w_out, uint16_t* qn_out, uint16_t* kn_out, hipStream_t s);
+
 // Causal GQA flash attention over the cache for B x T queries at positions start..start+T-1.
 void launch_attn_prefill(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out,
                          int B, int T, int start, int max_seq, hipStream_t s);

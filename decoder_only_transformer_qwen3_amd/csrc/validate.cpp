@@ -125,6 +125,30 @@ int check_decode_call(const q3_model* m, const q3_kv* kv, int32_t batch, const i
   return Q3_OK;
 }
 
+static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+int check_rope_convert_call(const void* w_qkv, const void* q_norm, const void* k_norm, const void* w_qkv_out,
+                            const void* q_norm_out, const void* k_norm_out) {
+  if (!w_qkv || !q_norm || !k_norm || !w_qkv_out || !q_norm_out || !k_norm_out) return Q3_ERR_NULL;
+  const size_t wb = (size_t)Q3_QKV_ROWS * Q3_HIDDEN * 2, gb = (size_t)Q3_HEAD_DIM * 2;
+  const void* in[3] = {w_qkv, q_norm, k_norm};
+  const size_t in_n[3] = {wb, gb, gb};
+  const void* out[3] = {w_qkv_out, q_norm_out, k_norm_out};
+  const size_t out_n[3] = {wb, gb, gb};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (overlap(out[i], out_n[i], in[j], in_n[j])) return Q3_ERR_SHAPE;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(out[i], out_n[i], out[j], out_n[j])) return Q3_ERR_SHAPE;
+  }
+  if (!al16(w_qkv) || !al16(q_norm) || !al16(k_norm) || !al16(w_qkv_out) || !al16(q_norm_out) || !al16(k_norm_out))
+    return Q3_ERR_ALIGN;
+  return Q3_OK;
+}
+
 int check_linear_call(const void* x, const void* w, const void* out, int32_t m, int32_t n, int32_t k, int32_t ldo,
                       int32_t epilogue) {
   if (!x || !w || !out) return Q3_ERR_NULL;

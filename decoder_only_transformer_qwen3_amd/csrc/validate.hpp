@@ -44,6 +44,8 @@ int check_decode_call(const q3_model* m, const q3_kv* kv, int32_t batch, const i
                       const int32_t* seq_lens, int32_t max_len_hint, const float* logits, const int32_t* out_ids,
                       const void* ws, size_t ws_bytes);
 
+int check_rope_convert_call(const void* w_qkv, const void* q_norm, const void* k_norm, const void* w_qkv_out,
+                            const void* q_norm_out, const void* k_norm_out);
 int check_linear_call(const void* x, const void* w, const void* out, int32_t m, int32_t n, int32_t k, int32_t ldo,
                       int32_t epilogue);
 

@@ -265,6 +265,26 @@ int q3_attention_decode(const void *qkv, const void *q_norm, const void *k_norm,
                         const int32_t *positions, int32_t max_len_hint, void *out, void *ws, size_t ws_bytes,
                         void *stream);
 
+/* Rotary-pairing conversion for weights trained with interleaved rotary
+ * pairs (dims 2i, 2i+1 rotated by p * 1e6^(-2i/128); "从零开始写Qwen3（二）"
+ * §rope/原理 describes this pairing next to the half-swap one that Qwen3
+ * uses, "古法手撕简易LLM推理器" §RoPE的细节).  Such a layer equals a
+ * half-swap layer whose q and k projection rows and q/k norm gains are
+ * permuted within each head by P(j) = 2j (j < 64), 2(j - 64) + 1 (j >= 64):
+ * attention scores are q.k sums, unchanged by a common permutation of the
+ * q and k dims, and the per-head RMSNorm commutes with it.  This call
+ * writes that permuted copy; the layer then runs on every other entry
+ * point unchanged (its cache holds the keys in the permuted dim order).
+ *   w_qkv   bf16 [4096, 1024] merged rows as in q3_layer_weights;
+ *           w_qkv_out gets q rows (heads 0..15) and k rows (heads 0..7)
+ *           permuted, v rows copied.
+ *   q_norm, k_norm  bf16 [128] gains; *_out their permuted copies.
+ * Outputs must not overlap the inputs.
+ * Errors: Q3_ERR_NULL, Q3_ERR_SHAPE (an output overlaps an input),
+ * Q3_ERR_ALIGN (16 B), Q3_ERR_HIP. */
+int q3_rope_interleaved_to_half(const void *w_qkv, const void *q_norm, const void *k_norm, void *w_qkv_out,
+                                void *q_norm_out, void *k_norm_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,7 @@ from dataclasses import dataclass
 import numpy as np
 
 __all__ = [
-    "Cfg", "QWEN3", "widen_bf16", "rmsnorm", "silu", "rope_inv_freq", "rope",
+    "Cfg", "QWEN3", "widen_bf16", "rmsnorm", "silu", "rope_inv_freq", "rope", "rope_interleaved", "apply_rope",
     "attention", "LayerW", "Model", "KVCache", "embed", "layer_forward",
     "final_logits", "prefill", "decode_step", "argmax_lowest",
     "generate_nocache", "generate_cached",
@@ -54,6 +54,9 @@ class Cfg:
     eps: float = 1e-6
     theta: float = 1e6
     max_pos: int = 40960
+    # "neox": pairs (i, i + D/2), Qwen3's form; "interleaved": pairs (2i, 2i+1),
+    # the other pairing "从零开始写Qwen3（二）" §rope/原理 describes
+    rope_style: str = "neox"
 
 
 QWEN3 = Cfg()
@@ -112,6 +115,31 @@ def rope(x: np.ndarray, positions, theta: float) -> np.ndarray:
     s = np.sin(ang)[..., None, :]
     x1, x2 = x[..., :half], x[..., half:]
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def rope_interleaved(x: np.ndarray, positions, theta: float) -> np.ndarray:
+    """Interleaved ("GPT-J style") rotary embedding: dimension 2i is paired
+    with 2i+1 and the pair is rotated by p * theta^(-2i/D)
+    ("从零开始写Qwen3（二）" §rope/原理 rotates consecutive dimension pairs by
+    the pair's base angle; "古法手撕简易LLM推理器" §RoPE的细节 contrasts it
+    with the half-swap form).  Shapes as in ``rope``."""
+    d = x.shape[-1]
+    p = np.asarray(positions, dtype=np.float64)
+    ang = p[..., None] * rope_inv_freq(d, theta)          # [..., T, D/2]
+    c = np.cos(ang)[..., None, :]
+    s = np.sin(ang)[..., None, :]
+    xe, xo = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x, dtype=np.float64)
+    y[..., 0::2] = xe * c - xo * s
+    y[..., 1::2] = xo * c + xe * s
+    return y
+
+
+def apply_rope(x: np.ndarray, positions, cfg: "Cfg") -> np.ndarray:
+    """The configuration's rotary form (half-swap for Qwen3)."""
+    if cfg.rope_style == "interleaved":
+        return rope_interleaved(x, positions, cfg.theta)
+    return rope(x, positions, cfg.theta)
 
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos, block: int = 1024) -> np.ndarray:
@@ -220,8 +248,8 @@ def layer_forward(w: LayerW, x: np.ndarray, k_cache: np.ndarray, v_cache: np.nda
     v = (h @ w.wv.T).reshape(b_sz, t_len, hkv, d)
     q = rmsnorm(q, w.q_norm, cfg.eps)
     k = rmsnorm(k, w.k_norm, cfg.eps)
-    q = rope(q, pos, cfg.theta)
-    k = rope(k, pos, cfg.theta)
+    q = apply_rope(q, pos, cfg)
+    k = apply_rope(k, pos, cfg)
 
     o = np.empty((b_sz, t_len, hq * d))
     for b in range(b_sz):

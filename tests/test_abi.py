@@ -157,6 +157,24 @@ def test_attention_helpers_reject_bad_arguments(B):
     assert dec(13, need - 1) == B.Q3_ERR_WORKSPACE
 
 
+def test_rope_conversion_rejects_bad_arguments(B):
+    conv = lambda *a: B.q3_rope_interleaved_to_half(*a, stream=0, check=False)
+    W = 4096 * 1024 * 2
+    ok = [0x10000000, 0x20000000, 0x20001000, 0x30000000, 0x40000000, 0x40001000]
+    for i in range(6):
+        a = list(ok)
+        a[i] = None
+        assert conv(*a) == B.Q3_ERR_NULL
+    a = list(ok); a[3] = ok[0] + W - 16          # output rows overlap the input's tail
+    assert conv(*a) == B.Q3_ERR_SHAPE
+    a = list(ok); a[4] = ok[1] + 128             # output gain overlaps the input gain
+    assert conv(*a) == B.Q3_ERR_SHAPE
+    a = list(ok); a[5] = ok[4]                   # the two output gains overlap
+    assert conv(*a) == B.Q3_ERR_SHAPE
+    a = list(ok); a[4] = ok[4] + 8
+    assert conv(*a) == B.Q3_ERR_ALIGN
+
+
 def test_rope_table_matches_oracle_angles(B):
     import oracle as O
     cos = np.empty((B.MAX_POS, 64), dtype=np.float32)

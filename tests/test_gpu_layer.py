@@ -92,6 +92,8 @@ def run_layer_case(lib, layer0, rope, batch, T, start, max_seq, check_seqs=None,
     (2, 100, 0, 128),     # several tiles + ragged tail on every axis
     (2, 77, 50, 160),     # multi-token chunk at an offset into a filled cache
     (3, 1, 700, 1024),    # decode-shaped, host start position
+    (4, 2, 30, 64),       # 8 rows: the largest fused post-attention kernel
+    (1, 5, 3, 16),        # 5 rows at an offset
     (1, 1, 0, 8),         # single key
     (2, 1, 4095, 4096),   # decode into the last cache row
     (5, 3, 13, 16),       # tiny chunk, several sequences, cache full afterwards

@@ -195,6 +195,74 @@ def test_rope_neox_is_interleaved_under_half_interleave_permutation():
     np.testing.assert_allclose(y[..., perm], yi, atol=1e-10)
 
 
+def _rope_int1(x, p):
+    return O.rope_interleaved(x[None, None, :], np.array([p]), 1e6)[0, 0]
+
+
+def test_rope_interleaved_identity_norm_and_first_pair_angle():
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal(128)
+    np.testing.assert_array_equal(_rope_int1(x, 0), x)
+    for p in (1, 17, 4095, 40959):
+        y = _rope_int1(x, p)
+        assert abs(np.linalg.norm(y) - np.linalg.norm(x)) < 1e-12 * np.linalg.norm(x)
+        # adjacent pair (0, 1) has frequency theta^0 = 1: rotated by exactly p radians
+        assert abs(complex(y[0], y[1]) - complex(x[0], x[1]) * np.exp(1j * p)) < 1e-12
+        # the last pair (126, 127) turns by p * 1e6^(-126/128)
+        ang = p * 1e6 ** (-126 / 128)
+        assert abs(complex(y[126], y[127]) - complex(x[126], x[127]) * np.exp(1j * ang)) < 1e-12
+
+
+def test_rope_interleaved_relative_position_invariance():
+    rng = np.random.default_rng(32)
+    q, k = rng.standard_normal(128), rng.standard_normal(128)
+    for m, n, s in ((3, 1, 5), (100, 40, 1000), (0, 2047, 30000)):
+        a = np.dot(_rope_int1(q, m), _rope_int1(k, n))
+        b = np.dot(_rope_int1(q, m + s), _rope_int1(k, n + s))
+        assert abs(a - b) < 1e-10
+
+
+def test_rope_interleaved_is_neox_after_the_pair_permutation():
+    """Interleaved pairs (2i, 2i+1) are the half-swap pairs (i, i+64) under the
+    permutation P(j) = 2j (j < 64), 2(j-64)+1 (j >= 64): the two oracle forms
+    agree element for element, which is what lets a model with interleaved
+    rotary run on the half-swap kernels with permuted q/k rows and gains."""
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((4, 3, 128))
+    pos = np.array([0, 9, 300, 39000])
+    perm = np.concatenate([2 * np.arange(64), 2 * np.arange(64) + 1])
+    np.testing.assert_allclose(O.rope(x[..., perm], pos, 1e6), O.rope_interleaved(x, pos, 1e6)[..., perm],
+                               atol=1e-12)
+
+
+def test_interleaved_model_equals_half_swap_model_with_permuted_qk():
+    """Whole forward: a model whose rotary pairs are interleaved gives the
+    same logits as the half-swap model whose q and k projection rows and q/k
+    norm gains are permuted within each head by P (V, o_proj and the MLP
+    untouched): attention scores are q.k sums, invariant under a common
+    permutation of q and k dims, and the per-head norm commutes with it."""
+    dims = I.TINY
+    cfg_h = O.Cfg(hidden=dims.hidden, n_heads=dims.n_heads, n_kv_heads=dims.n_kv_heads, head_dim=dims.head_dim,
+                  inter=dims.inter, vocab=dims.vocab, n_layers=2)
+    cfg_i = O.Cfg(**{**cfg_h.__dict__, "rope_style": "interleaved"})
+    bits = I.model_weights(34, dims, n_layers=2, std=0.3)
+    d = dims.head_dim
+    perm = np.concatenate([2 * np.arange(d // 2), 2 * np.arange(d // 2) + 1])
+    pbits = {**bits, "layers": []}
+    for lw in bits["layers"]:
+        q = lw["wq"].reshape(dims.n_heads, d, -1)[:, perm].reshape(lw["wq"].shape)
+        k = lw["wk"].reshape(dims.n_kv_heads, d, -1)[:, perm].reshape(lw["wk"].shape)
+        pbits["layers"].append({**lw, "wq": q, "wk": k, "q_norm": lw["q_norm"][perm], "k_norm": lw["k_norm"][perm]})
+    ids = I.token_ids(35, (2, 9), vocab=dims.vocab)
+    li, ni, _, _ = O.prefill(O.Model(bits, cfg_i), ids)
+    lh, nh, _, _ = O.prefill(O.Model(pbits, cfg_h), ids)
+    assert rel(lh, li) < 1e-12
+    np.testing.assert_array_equal(ni, nh)
+    # and the interleaved model is a different model: the pairing matters
+    l0, _, _, _ = O.prefill(O.Model(bits, cfg_h), ids)
+    assert rel(l0, li) > 1e-3
+
+
 # ------------------------------------------------------------------ attention
 
 def _attn_brute(q, k, v, q_pos):
