@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--workload", default="prefill128_decode64", choices=sorted(WORKLOADS))
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eos-id", type=int, default=None,
+                    help="decode with q3_decode_step_eos (on-device done mask) and this end-of-sequence token")
     ap.add_argument("--kernel-iters", type=int, default=200)
     ap.add_argument("--kernel-only", action="store_true",
                     help="time only the workload's dominant kernel (the run the counter passes profile)")
@@ -68,8 +70,9 @@ def parse():
 class Runner:
     """Holds device state for one workload and runs prefill / decode phases."""
 
-    def __init__(self, torch, B, dev, dm, batch, prompt_len, steps):
+    def __init__(self, torch, B, dev, dm, batch, prompt_len, steps, eos_id=None):
         self.torch, self.B, self.dev, self.dm = torch, B, dev, dm
+        self.eos_id = eos_id
         self.batch, self.T, self.steps = batch, prompt_len, steps
         from decoder_only_transformer_qwen3_amd import inputs as I
         self.ids_np = I.token_ids(1000 + batch, (batch, prompt_len))
@@ -99,8 +102,12 @@ class Runner:
     def decode_loop(self):
         B = self.B
         for _ in range(self.steps):
-            B.q3_decode_step(self.dm.struct, self.kv.struct, self.batch, self.nxt, self.seq,
-                             self.T + self.steps, None, self.nxt, self.ws_d, self.nb_d)
+            if self.eos_id is None:
+                B.q3_decode_step(self.dm.struct, self.kv.struct, self.batch, self.nxt, self.seq,
+                                 self.T + self.steps, None, self.nxt, self.ws_d, self.nb_d)
+            else:
+                B.q3_decode_step_eos(self.dm.struct, self.kv.struct, self.batch, self.nxt, self.seq,
+                                     self.T + self.steps, self.eos_id, None, self.nxt, self.ws_d, self.nb_d)
 
 
 def capture(torch, fn):
@@ -347,7 +354,7 @@ def main():
     log(f"[bench] workload {args.workload}: batch {batch}, prompt {T}, decode steps {steps}")
     bits = I.model_weights(0)
     dm = dev.DeviceModel(bits)
-    r = Runner(torch, B, dev, dm, batch, T, steps)
+    r = Runner(torch, B, dev, dm, batch, T, steps, args.eos_id)
     if args.kernel_only:  # (the cache is not prefilled: the kernels stream it all the same)
         rl = dominant_kernel(torch, B, dev, dm, r, args.workload, args.kernel_iters, not args.no_graph)
         rl["source_sha256"] = kernel_source_digest(args.workload)
@@ -417,7 +424,7 @@ def main():
         "data": "synthetic (random-init weights N(0,0.02), uniform random token ids)",
         "config": {"workload": args.workload, "layers": 28, "batch": batch, "prompt_len": T,
                    "decode_steps": steps, "prefill_timed": prefill_timed, "hip_graph": use_graph,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", **({"eos_id": args.eos_id} if args.eos_id is not None else {})},
         "prefill_ms": round(pre_ms, 4), "decode_ms": round(dec_ms, 4),
         "prefill_tok_s": round(tokens_prefill / (pre_ms * 1e-3), 1) if prefill_timed else None,
         "decode_tok_s": round(tokens_decode / (dec_ms * 1e-3), 1) if steps > 0 else None,

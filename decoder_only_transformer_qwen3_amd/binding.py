@@ -66,12 +66,14 @@ _attn_prefill = _sig("q3_attention_prefill", ctypes.c_int, _vp, _vp, _vp, _i32, 
 _attn_decode = _sig("q3_attention_decode", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
                     _i32, _vp, _vp, _sz, _vp)
 _rope_conv = _sig("q3_rope_interleaved_to_half", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp)
+_decode_eos = _sig("q3_decode_step_eos", ctypes.c_int, ctypes.POINTER(q3_model), ctypes.POINTER(q3_kv), _i32, _vp,
+                     _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp)
 
 Q3_EPI_STORE_BF16, Q3_EPI_STORE_F32, Q3_EPI_ADD_F32, Q3_EPI_SILU_GATE = 0, 1, 2, 3
 
 EXPORTS = ("q3_status_str", "q3_rope_table_host", "q3_workspace_bytes", "q3_layer_forward",
            "q3_prefill", "q3_decode_step", "q3_argmax", "q3_linear", "q3_attention_prefill",
-           "q3_attention_decode", "q3_rope_interleaved_to_half")
+           "q3_attention_decode", "q3_rope_interleaved_to_half", "q3_decode_step_eos")
 
 
 class Q3Error(RuntimeError):
@@ -189,4 +191,13 @@ def q3_rope_interleaved_to_half(w_qkv, q_norm, k_norm, w_qkv_out, q_norm_out, k_
                     _stream(stream))
     if check:
         _check(st, "q3_rope_interleaved_to_half")
+    return st
+
+
+def q3_decode_step_eos(m: q3_model, kv: q3_kv, batch, in_ids, seq_lens, max_len_hint, eos_id, logits, out_ids, ws,
+                       ws_bytes, stream=None, check=True) -> int:
+    st = _decode_eos(ctypes.byref(m), ctypes.byref(kv), batch, _ptr(in_ids), _ptr(seq_lens), max_len_hint, eos_id,
+                     _ptr(logits), _ptr(out_ids), _ptr(ws), ws_bytes, _stream(stream))
+    if check:
+        _check(st, "q3_decode_step_eos")
     return st

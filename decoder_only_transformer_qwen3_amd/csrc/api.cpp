@@ -160,7 +160,7 @@ void run_layer(const LayerCtx& c) {
 // skinny path the last layer already left bf16(gamma_f * r) and the sums of
 // squares for every row; otherwise they are formed here for the B last rows.
 void run_head(const q3_model* m, const Ws& ws, int B, int T, float* logits, int32_t* next_ids, int32_t* seq_lens,
-              int seq_mode, int seq_val, hipStream_t s) {
+              int seq_mode, int seq_val, hipStream_t s, const int32_t* in_ids = nullptr, int eos = -1) {
   const uint16_t* X;
   const float* ssq;
   int ldx, ssq_ld, ssq_n;
@@ -197,7 +197,7 @@ void run_head(const q3_model* m, const Ws& ws, int B, int T, float* logits, int3
     a.ssq_n = ssq_n;
     launch_gemm_skinny(a, 1, EPI_LOGITS, s);
   }
-  launch_argmax_partials(ws.amax, B, n_part, next_ids, seq_lens, seq_mode, seq_val, s);
+  launch_argmax_partials(ws.amax, B, n_part, next_ids, seq_lens, seq_mode, seq_val, in_ids, eos, s);
 }
 
 inline int launch_status() { return hipGetLastError() == hipSuccess ? Q3_OK : Q3_ERR_HIP; }
@@ -308,10 +308,11 @@ int q3_prefill(const q3_model* m, const q3_kv* kv, int32_t batch, int32_t prompt
   return launch_status();
 }
 
-int q3_decode_step(const q3_model* m, const q3_kv* kv, int32_t batch, const int32_t* in_ids, int32_t* seq_lens,
-                   int32_t max_len_hint, float* logits, int32_t* out_ids, void* ws, size_t ws_bytes, void* stream) {
-  const int st =
-      q3v::check_decode_call(m, kv, batch, in_ids, seq_lens, max_len_hint, logits, out_ids, ws, ws_bytes);
+int q3_decode_step_eos(const q3_model* m, const q3_kv* kv, int32_t batch, const int32_t* in_ids, int32_t* seq_lens,
+                       int32_t max_len_hint, int32_t eos_id, float* logits, int32_t* out_ids, void* ws,
+                       size_t ws_bytes, void* stream) {
+  int st = q3v::check_decode_call(m, kv, batch, in_ids, seq_lens, max_len_hint, logits, out_ids, ws, ws_bytes);
+  if (st == Q3_OK && (eos_id < -1 || eos_id >= Q3_VOCAB)) st = Q3_ERR_SHAPE;
   if (st != Q3_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const Ws wsp = carve(ws, batch, 1);
@@ -338,8 +339,14 @@ int q3_decode_step(const q3_model* m, const q3_kv* kv, int32_t batch, const int3
     c.gamma_next = U(l + 1 < NL ? m->layer[l + 1].input_norm : m->final_norm);
     run_layer(c);
   }
-  run_head(m, wsp, batch, 1, logits ? logits : wsp.logits, out_ids, seq_lens, 2, 0, s);
+  run_head(m, wsp, batch, 1, logits ? logits : wsp.logits, out_ids, seq_lens, 2, 0, s, in_ids, eos_id);
   return launch_status();
+}
+
+int q3_decode_step(const q3_model* m, const q3_kv* kv, int32_t batch, const int32_t* in_ids, int32_t* seq_lens,
+                   int32_t max_len_hint, float* logits, int32_t* out_ids, void* ws, size_t ws_bytes, void* stream) {
+  return q3_decode_step_eos(m, kv, batch, in_ids, seq_lens, max_len_hint, -1, logits, out_ids, ws, ws_bytes,
+                            stream);
 }
 
 int q3_linear(const void* x, const void* w, void* out, int32_t m, int32_t n, int32_t k, int32_t ldo, int32_t epilogue,

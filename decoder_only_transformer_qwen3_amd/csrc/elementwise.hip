@@ -301,11 +301,15 @@ __device__ __forceinline__ void am_wave_block_reduce(float& best, int& bi, float
   }
 }
 
+// seq_mode 2 with eos >= 0: a row whose input token in_ids[r] is eos has
+// finished; it keeps its length and emits eos again (in_ids may alias
+// out_idx: it is read first).
 __device__ __forceinline__ void am_finish(int r, int bi, int32_t* out_idx, int32_t* seq_lens, int seq_mode,
-                                          int seq_val) {
-  out_idx[r] = bi;
+                                          int seq_val, const int32_t* in_ids = nullptr, int eos = -1) {
+  const bool fin = seq_mode == 2 && eos >= 0 && in_ids[r] == eos;
+  out_idx[r] = fin ? eos : bi;
   if (seq_mode == 1) seq_lens[r] = seq_val;
-  if (seq_mode == 2) seq_lens[r] += 1;
+  if (seq_mode == 2 && !fin) seq_lens[r] += 1;
 }
 
 // One block of 1024 threads per row; 16 B loads when the row is 16-byte
@@ -372,8 +376,9 @@ void launch_argmax(const float* logits, int rows, int vocab, int64_t row_stride,
 
 // Reduce the lm_head's per-block (value, index) candidates of one row.
 __global__ __launch_bounds__(1024) void k_argmax_partials(const float2* __restrict__ part, int n_part,
-                                                          int32_t* __restrict__ out_idx,
-                                                          int32_t* __restrict__ seq_lens, int seq_mode, int seq_val) {
+                                                          int32_t* out_idx, int32_t* __restrict__ seq_lens,
+                                                          int seq_mode, int seq_val, const int32_t* in_ids,
+                                                          int eos) {
   __shared__ float sv[16];
   __shared__ int si[16];
   const int r = blockIdx.x, tid = threadIdx.x;
@@ -397,13 +402,13 @@ __global__ __launch_bounds__(1024) void k_argmax_partials(const float2* __restri
     }
   }
   am_wave_block_reduce(best, bi, sv, si);
-  if (tid == 0) am_finish(r, bi, out_idx, seq_lens, seq_mode, seq_val);
+  if (tid == 0) am_finish(r, bi, out_idx, seq_lens, seq_mode, seq_val, in_ids, eos);
 }
 
 void launch_argmax_partials(const void* part, int rows, int n_part, int32_t* out_idx, int32_t* seq_lens,
-                            int seq_mode, int seq_val, hipStream_t s) {
+                            int seq_mode, int seq_val, const int32_t* in_ids, int eos, hipStream_t s) {
   hipLaunchKernelGGL(k_argmax_partials, dim3(rows), dim3(1024), 0, s, static_cast<const float2*>(part), n_part,
-                     out_idx, seq_lens, seq_mode, seq_val);
+                     out_idx, seq_lens, seq_mode, seq_val, in_ids, eos);
 }
 
 // ---------------------------------------------------------------------------

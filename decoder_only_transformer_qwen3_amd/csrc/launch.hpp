@@ -104,8 +104,10 @@ void launch_attn_decode(const uint16_t* qkv, const uint16_t* q_norm, const uint1
 
 // Final greedy choice from the lm_head's per-block (max, argmax) partials:
 // part is [rows][n_part] of (float value, int index).  seq_mode as below.
+// With seq_mode 2 and eos >= 0, rows whose input token in_ids[r] is eos
+// have finished: they emit eos and keep their length.
 void launch_argmax_partials(const void* part, int rows, int n_part, int32_t* out_idx, int32_t* seq_lens,
-                            int seq_mode, int seq_val, hipStream_t s);
+                            int seq_mode, int seq_val, const int32_t* in_ids, int eos, hipStream_t s);
 
 // Row argmax (lowest index on ties, first NaN wins).  seq_mode: 0 none,
 // 1 seq_lens[r] = seq_val, 2 seq_lens[r] += 1 (done after the argmax).

@@ -193,6 +193,22 @@ int q3_decode_step(const q3_model *m, const q3_kv *kv, int32_t batch, const int3
                    int32_t *seq_lens, int32_t max_len_hint, float *logits, int32_t *out_ids,
                    void *ws, size_t ws_bytes, void *stream);
 
+/* q3_decode_step with an end-of-sequence token ("第 3 章" §4.3: generation
+ * stops once eos_id is produced and keeps it in the output;
+ * "手写Qwen3-0.6B推理" §推理 and "古法手撕简易LLM推理器" §prefill与predict
+ * stop on EOS 151645).  The input token is the done mask: a sequence whose
+ * in_ids[b] == eos_id has finished, so out_ids[b] = eos_id and seq_lens[b]
+ * stays as it is (its logits and the cache row at seq_lens[b] are
+ * scratch).  Every other sequence steps as in q3_decode_step, so a
+ * fixed number of calls can be captured in one graph and replayed with no
+ * host check between steps; a sequence that has finished just repeats
+ * eos_id.  eos_id = -1 disables the rule (q3_decode_step).
+ * Errors: those of q3_decode_step, and Q3_ERR_SHAPE for eos_id outside
+ * -1 .. 151935. */
+int q3_decode_step_eos(const q3_model *m, const q3_kv *kv, int32_t batch, const int32_t *in_ids,
+                       int32_t *seq_lens, int32_t max_len_hint, int32_t eos_id, float *logits,
+                       int32_t *out_ids, void *ws, size_t ws_bytes, void *stream);
+
 /* Row-wise greedy argmax ("手写Qwen3-0.6B推理" §推理; "第 3 章" §4.3):
  * out_idx[r] = lowest index v with logits[r*row_stride + v] equal to the
  * row maximum (a NaN counts as larger than every number; the first NaN

@@ -120,6 +120,10 @@ def test_prefill_decode_argmax_reject_bad_arguments(B):
     assert st == B.Q3_ERR_POSITION
     st = B.q3_decode_step(m, kv, 4, 0x600000, None, 100, None, 0x610000, 0x700000, dneed, stream=0, check=False)
     assert st == B.Q3_ERR_NULL
+    eos = lambda e, hint=100: B.q3_decode_step_eos(m, kv, 4, 0x600000, 0x620000, hint, e, None, 0x610000, 0x700000,
+                                                   dneed, stream=0, check=False)
+    assert eos(B.VOCAB) == B.Q3_ERR_SHAPE and eos(-2) == B.Q3_ERR_SHAPE
+    assert eos(151645, hint=257) == B.Q3_ERR_POSITION    # the decode-step checks come first
     assert B.q3_argmax(0x800000, 2, 10, 5, 0x900000, stream=0, check=False) == B.Q3_ERR_SHAPE
     lin = lambda *a: B.q3_linear(*a, stream=0, check=False)
     assert lin(None, 0x1000, 0x2000, 1, 128, 512, 128, 0) == B.Q3_ERR_NULL

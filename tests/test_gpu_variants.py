@@ -90,3 +90,102 @@ def test_interleaved_rope_model_prefill_and_greedy_steps(lib):
     _, h_logits = O.generate_cached(O.Model(bits), ids, 1)
     assert np.max(np.abs(h_logits[0] - o_logits[0])) > 20 * np.max(np.abs(lgs[0] - o_logits[0]))
     log(f"[variant] greedy report: {rep}")
+
+
+def _expected_with_eos(gen, eos):
+    """gen [steps+1, batch]: the prefill token, then one token per free-running
+    step.  With EOS a sequence stops advancing once it has emitted eos
+    (which it keeps) and repeats eos after that."""
+    steps = gen.shape[0] - 1
+    out = np.empty((steps, gen.shape[1]), dtype=np.int64)
+    lens = np.empty(gen.shape[1], dtype=np.int64)
+    for b in range(gen.shape[1]):
+        hits = np.flatnonzero(gen[:, b] == eos)
+        stop = int(hits[0]) if hits.size else None
+        for i in range(steps):
+            out[i, b] = gen[i + 1, b] if stop is None or i + 1 <= stop else eos
+        lens[b] = steps if stop is None else min(stop, steps)
+    return out, lens
+
+
+def test_eos_done_mask_in_a_captured_decode_loop(lib):
+    """q3_decode_step_eos: batch 3, 16-token prompts, a 12-step loop captured
+    as one graph and replayed twice.  Each sequence must produce the free-run
+    tokens up to and including its first eos, then eos, and stop advancing
+    its length; one case stops a sequence at its prefill token.  Tokens up
+    to the stop are checked against the teacher-forced oracle."""
+    B, dev = lib
+    bits = I.model_weights(0)
+    dm = dev.DeviceModel(bits)
+    batch, T, steps = 3, 16, 12
+    cap = T + steps + 12                                    # a multiple of 8
+    ids = I.token_ids(8, (batch, T))
+    kv = dev.DeviceKV(batch, cap)
+    ws, nb = dev.workspace(batch, T)
+    wsd, nbd = dev.workspace(batch, 1)
+    nxt = torch.empty(batch, dtype=torch.int32, device="cuda")
+    seq = torch.empty(batch, dtype=torch.int32, device="cuda")
+    B.q3_prefill(dm.struct, kv.struct, batch, T, torch.from_numpy(ids).cuda(), None, nxt, seq, ws, nb)
+    torch.cuda.synchronize()
+    nxt0, seq0 = nxt.clone(), seq.clone()
+    free = [nxt0.cpu().numpy()]
+    for _ in range(steps):
+        B.q3_decode_step(dm.struct, kv.struct, batch, nxt, seq, cap, None, nxt, wsd, nbd)
+        free.append(nxt.cpu().numpy())
+    gen = np.stack(free).astype(np.int64)                  # [steps + 1, batch]
+    log(f"[eos] free-running tokens:\n{gen.T}")
+
+    outs = [torch.empty(batch, dtype=torch.int32, device="cuda") for _ in range(steps)]
+    for eos in (int(gen[5, 1]), int(gen[0, 0])):
+        exp_tok, exp_len = _expected_with_eos(gen, eos)
+
+        def loop():
+            inp = nxt
+            for i in range(steps):
+                B.q3_decode_step_eos(dm.struct, kv.struct, batch, inp, seq, cap, eos, None, outs[i], wsd, nbd)
+                inp = outs[i]
+
+        nxt.copy_(nxt0)
+        seq.copy_(seq0)
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            loop()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, capture_error_mode="thread_local"):
+            loop()
+        for rep in range(2):
+            nxt.copy_(nxt0)
+            seq.copy_(seq0)
+            junk = torch.randn(1000, device="cuda").sum()  # unrelated eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            got = np.stack([o.cpu().numpy() for o in outs]).astype(np.int64)
+            np.testing.assert_array_equal(got, exp_tok)
+            np.testing.assert_array_equal(seq.cpu().numpy(), T + exp_len)
+            del junk
+        log(f"[eos] eos={eos}: stops after {exp_len.tolist()} steps, replays agree")
+
+    # the tokens up to sequence 1's stop, against the teacher-forced oracle
+    om = O.Model(bits)
+    stop = int(np.flatnonzero(gen[:, 1] == int(gen[5, 1]))[0])
+    toks = gen[:stop + 1, 1].tolist()
+    _, o_logits = O.generate_cached(om, ids[1:2], stop + 1, forced=toks)
+    rep = GreedyReport()
+    wsl, nbl = dev.workspace(1, T)
+    kv1 = dev.DeviceKV(1, cap)
+    logits = torch.empty((1, B.VOCAB), dtype=torch.float32, device="cuda")
+    n1 = torch.empty(1, dtype=torch.int32, device="cuda")
+    s1 = torch.empty(1, dtype=torch.int32, device="cuda")
+    B.q3_prefill(dm.struct, kv1.struct, 1, T, torch.from_numpy(ids[1:2]).cuda(), logits, n1, s1, wsl, nbl)
+    wsd1, nbd1 = dev.workspace(1, 1)
+    for i in range(stop + 1):
+        if i:
+            n1.fill_(toks[i - 1])
+            B.q3_decode_step(dm.struct, kv1.struct, 1, n1, s1, cap, logits, n1, wsd1, nbd1)
+        torch.cuda.synchronize()
+        check_greedy_step(rep, int(n1.item()), logits.cpu().numpy()[0], o_logits[i])
+    log(f"[eos] sequence 1 up to its stop vs the oracle: {rep}")
