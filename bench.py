@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--workload", default="prefill128_decode64", choices=sorted(WORKLOADS))
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sample", default=None, metavar="T,K,P",
+                    help="decode by temperature / top-k / top-p sampling (q3_sample on the step's logits)")
     ap.add_argument("--eos-id", type=int, default=None,
                     help="decode with q3_decode_step_eos (on-device done mask) and this end-of-sequence token")
     ap.add_argument("--kernel-iters", type=int, default=200)
@@ -70,9 +72,18 @@ def parse():
 class Runner:
     """Holds device state for one workload and runs prefill / decode phases."""
 
-    def __init__(self, torch, B, dev, dm, batch, prompt_len, steps, eos_id=None):
+    def __init__(self, torch, B, dev, dm, batch, prompt_len, steps, eos_id=None, sample=None):
         self.torch, self.B, self.dev, self.dm = torch, B, dev, dm
         self.eos_id = eos_id
+        self.sample = None
+        if sample is not None:  # per-row parameters and one seeded uniform draw per step and row
+            t, k, p = sample
+            g = torch.Generator(device="cuda").manual_seed(1234)
+            self.sample = (torch.full((batch,), t, dtype=torch.float32, device="cuda"),
+                           torch.full((batch,), k, dtype=torch.int32, device="cuda"),
+                           torch.full((batch,), p, dtype=torch.float32, device="cuda"),
+                           torch.rand((max(steps, 1), batch), generator=g, device="cuda"),
+                           torch.empty((batch, B.VOCAB), dtype=torch.float32, device="cuda"))
         self.batch, self.T, self.steps = batch, prompt_len, steps
         from decoder_only_transformer_qwen3_amd import inputs as I
         self.ids_np = I.token_ids(1000 + batch, (batch, prompt_len))
@@ -101,8 +112,13 @@ class Runner:
 
     def decode_loop(self):
         B = self.B
-        for _ in range(self.steps):
-            if self.eos_id is None:
+        for i in range(self.steps):
+            if self.sample is not None:
+                temps, ks, ps, us, logits = self.sample
+                B.q3_decode_step(self.dm.struct, self.kv.struct, self.batch, self.nxt, self.seq,
+                                 self.T + self.steps, logits, self.nxt, self.ws_d, self.nb_d)
+                B.q3_sample(logits, self.batch, B.VOCAB, B.VOCAB, temps, ks, ps, us[i], self.nxt)
+            elif self.eos_id is None:
                 B.q3_decode_step(self.dm.struct, self.kv.struct, self.batch, self.nxt, self.seq,
                                  self.T + self.steps, None, self.nxt, self.ws_d, self.nb_d)
             else:
@@ -354,7 +370,11 @@ def main():
     log(f"[bench] workload {args.workload}: batch {batch}, prompt {T}, decode steps {steps}")
     bits = I.model_weights(0)
     dm = dev.DeviceModel(bits)
-    r = Runner(torch, B, dev, dm, batch, T, steps, args.eos_id)
+    sample = None
+    if args.sample:
+        t, k, p = args.sample.split(",")
+        sample = (float(t), int(k), float(p))
+    r = Runner(torch, B, dev, dm, batch, T, steps, args.eos_id, sample)
     if args.kernel_only:  # (the cache is not prefilled: the kernels stream it all the same)
         rl = dominant_kernel(torch, B, dev, dm, r, args.workload, args.kernel_iters, not args.no_graph)
         rl["source_sha256"] = kernel_source_digest(args.workload)
@@ -424,7 +444,8 @@ def main():
         "data": "synthetic (random-init weights N(0,0.02), uniform random token ids)",
         "config": {"workload": args.workload, "layers": 28, "batch": batch, "prompt_len": T,
                    "decode_steps": steps, "prefill_timed": prefill_timed, "hip_graph": use_graph,
-                   "parallelism": "single GPU", **({"eos_id": args.eos_id} if args.eos_id is not None else {})},
+                   "parallelism": "single GPU", **({"eos_id": args.eos_id} if args.eos_id is not None else {}),
+                   **({"sampling": args.sample} if args.sample else {})},
         "prefill_ms": round(pre_ms, 4), "decode_ms": round(dec_ms, 4),
         "prefill_tok_s": round(tokens_prefill / (pre_ms * 1e-3), 1) if prefill_timed else None,
         "decode_tok_s": round(tokens_decode / (dec_ms * 1e-3), 1) if steps > 0 else None,

@@ -87,6 +87,11 @@ void launch_gemm_skinny(const uint16_t* X, const uint16_t* W, void* out, int M, 
 void launch_rope_pair_permute(const uint16_t* w_qkv, const uint16_t* q_norm, const uint16_t* k_norm,
                               uint16_t* w_out, uint16_t* qn_out, uint16_t* kn_out, hipStream_t s);
 
+// Temperature / top-k / top-p sampling of `rows` logits rows (one
+// 1024-thread workgroup per row); per-row parameters and uniform draws.
+void launch_sample(const float* logits, int rows, int vocab, int64_t stride, const float* temperature,
+                   const int32_t* top_k, const float* top_p, const float* uniform, int32_t* out, hipStream_t s);
+
 // Causal GQA flash attention over the cache for B x T queries at positions start..start+T-1.
 void launch_attn_prefill(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out,
                          int B, int T, int start, int max_seq, hipStream_t s);

@@ -149,6 +149,15 @@ int check_rope_convert_call(const void* w_qkv, const void* q_norm, const void* k
   return Q3_OK;
 }
 
+int check_sample_call(const float* logits, int32_t rows, int32_t vocab, int64_t row_stride, const float* temperature,
+                      const int32_t* top_k, const float* top_p, const float* uniform, const int32_t* out_idx) {
+  if (!logits || !temperature || !top_k || !top_p || !uniform || !out_idx) return Q3_ERR_NULL;
+  if (rows < 1 || vocab < 1 || row_stride < vocab) return Q3_ERR_SHAPE;
+  if (!al4(logits) || !al4(temperature) || !al4(top_k) || !al4(top_p) || !al4(uniform) || !al4(out_idx))
+    return Q3_ERR_ALIGN;
+  return Q3_OK;
+}
+
 int check_linear_call(const void* x, const void* w, const void* out, int32_t m, int32_t n, int32_t k, int32_t ldo,
                       int32_t epilogue) {
   if (!x || !w || !out) return Q3_ERR_NULL;

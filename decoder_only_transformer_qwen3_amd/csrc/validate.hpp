@@ -46,6 +46,8 @@ int check_decode_call(const q3_model* m, const q3_kv* kv, int32_t batch, const i
 
 int check_rope_convert_call(const void* w_qkv, const void* q_norm, const void* k_norm, const void* w_qkv_out,
                             const void* q_norm_out, const void* k_norm_out);
+int check_sample_call(const float* logits, int32_t rows, int32_t vocab, int64_t row_stride, const float* temperature,
+                      const int32_t* top_k, const float* top_p, const float* uniform, const int32_t* out_idx);
 int check_linear_call(const void* x, const void* w, const void* out, int32_t m, int32_t n, int32_t k, int32_t ldo,
                       int32_t epilogue);
 

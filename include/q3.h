@@ -223,6 +223,29 @@ int q3_argmax(const float *logits, int32_t rows, int32_t vocab, int64_t row_stri
               int32_t *out_idx, void *stream);
 
 
+/* Temperature / top-k / top-p sampling of logits rows: the path "第 3 章"
+ * §4.3's Sampler.sample takes when temperatures are given (the pages name
+ * the steps; this is their plain reading).  Row r, with
+ * T = temperature[r], k = top_k[r], p = top_p[r], u = uniform[r]:
+ *   - T <= 0 (or NaN): greedy, as q3_argmax;
+ *   - z = logits / T;
+ *   - candidates: every token with z >= the k-th largest z (k = 4096 when
+ *     top_k <= 0 or > 4096, at most vocab), ordered by z descending then
+ *     index ascending, at most 4096 of them;
+ *   - softmax over the candidates; keep the shortest prefix of that order
+ *     whose mass reaches p (p outside (0, 1] means 1);
+ *   - out_idx[r] = the first kept candidate whose cumulative mass exceeds
+ *     u times the kept mass (u is clamped to [0, 1)).
+ * Arithmetic is float32; the random draw is the caller's, so a run is
+ * reproducible.
+ *   logits       float32, rows x vocab, row_stride elements apart.
+ *   temperature  float32 [rows]; top_k int32 [rows]; top_p float32 [rows];
+ *   uniform      float32 [rows]; out_idx int32 [rows]  (all device).
+ * Errors: Q3_ERR_NULL, Q3_ERR_SHAPE (rows < 1, vocab < 1,
+ * row_stride < vocab), Q3_ERR_ALIGN (4-byte alignment), Q3_ERR_HIP. */
+int q3_sample(const float *logits, int32_t rows, int32_t vocab, int64_t row_stride, const float *temperature,
+              const int32_t *top_k, const float *top_p, const float *uniform, int32_t *out_idx, void *stream);
+
 /* Epilogues of q3_linear. */
 enum {
   Q3_EPI_STORE_BF16 = 0, /* out bf16 [m, ldo]:  out[i, j] = (x W^T)[i, j]            */

@@ -179,6 +179,21 @@ def test_rope_conversion_rejects_bad_arguments(B):
     assert conv(*a) == B.Q3_ERR_ALIGN
 
 
+def test_sample_rejects_bad_arguments(B):
+    smp = lambda *a: B.q3_sample(*a, stream=0, check=False)
+    ok = [0x1000, 4, 100, 100, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000]
+    for i in (0, 4, 5, 6, 7, 8):
+        a = list(ok)
+        a[i] = None
+        assert smp(*a) == B.Q3_ERR_NULL
+    for i, bad in ((1, 0), (2, 0), (3, 99)):
+        a = list(ok)
+        a[i] = bad
+        assert smp(*a) == B.Q3_ERR_SHAPE
+    a = list(ok); a[7] = 0x5002
+    assert smp(*a) == B.Q3_ERR_ALIGN
+
+
 def test_rope_table_matches_oracle_angles(B):
     import oracle as O
     cos = np.empty((B.MAX_POS, 64), dtype=np.float32)

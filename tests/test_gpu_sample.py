@@ -1,0 +1,149 @@
+"""GPU parity of q3_sample (temperature / top-k / top-p sampling, the
+Sampler.sample path of "第 3 章" §4.3) against the oracle's definition.
+
+The draw u is an input, so the chosen token is a deterministic function of
+the row.  The kernel decides in float32 and the oracle in float64: the two
+must agree exactly except where u (or the top-k / top-p boundary) sits
+within float32 rounding of a cumulative-mass boundary; such rows must still
+choose a token the float64 definition allows within that tolerance, and
+must be rare.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+
+from gpu_common import log
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+V = 151936
+MASS_TOL = 5e-4   # relative float32 error of a cumulative sum of <= 4096 masses, with margin
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decoder_only_transformer_qwen3_amd import binding
+    return binding
+
+
+def _allowed(x, t, k, p, u, got):
+    """got is a valid float64 choice up to MASS_TOL: it is a candidate (or
+    ties the k-th value to rounding), and u * kept mass falls in its
+    cumulative interval for some top-p cut within the tolerance."""
+    z = np.asarray(x, dtype=np.float64) / t
+    kk = O.SAMPLE_MAX_CANDIDATES if (k <= 0 or k > O.SAMPLE_MAX_CANDIDATES) else k
+    kk = min(kk, z.size)
+    order = np.lexsort((np.arange(z.size), -z))
+    tau = z[order[kk - 1]]
+    cand = order[z[order] >= tau - 1e-6 * max(1.0, abs(tau))][:O.SAMPLE_MAX_CANDIDATES + 64]
+    if got not in set(cand.tolist()):
+        return False
+    e = np.exp(z[cand] - z[cand[0]])
+    cum = np.cumsum(e)
+    pp = 1.0 if not (0.0 < p <= 1.0) else p
+    j = int(np.flatnonzero(cand == got)[0])
+    lo = cum[j - 1] if j else 0.0
+    tol = MASS_TOL * cum[-1]
+    for c in range(cum.size):
+        if cum[c] + tol < pp * cum[-1]:
+            continue
+        if c and cum[c - 1] - tol >= pp * cum[-1]:
+            break
+        target = u * cum[c]
+        if j <= c and lo - tol <= target <= cum[j] + tol:
+            return True
+    return False
+
+
+def _run(B, rows, vocab, stride, temps, ks, ps, us):
+    lg = torch.from_numpy(np.ascontiguousarray(rows, dtype=np.float32)).cuda()
+    t_d = torch.tensor(temps, dtype=torch.float32, device="cuda")
+    k_d = torch.tensor(ks, dtype=torch.int32, device="cuda")
+    p_d = torch.tensor(ps, dtype=torch.float32, device="cuda")
+    u_d = torch.tensor(us, dtype=torch.float32, device="cuda")
+    out = torch.full((len(temps),), -1, dtype=torch.int32, device="cuda")
+    B.q3_sample(lg, len(temps), vocab, stride, t_d, k_d, p_d, u_d, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def test_sample_full_vocab_against_oracle(lib):
+    B = lib
+    rng = np.random.default_rng(61)
+    n = 96
+    scale = rng.choice([1.0, 3.0, 8.0], n)
+    rows = (rng.standard_normal((n, V)) * scale[:, None]).astype(np.float32)
+    rows[::7] = np.round(rows[::7] * 4) / 4          # rows with many exactly tied values
+    temps = rng.choice([0.0, 0.5, 1.0, 1.7], n).astype(np.float32)
+    ks = rng.choice([0, 1, 2, 40, 4096, 10000], n).astype(np.int32)
+    ps = rng.choice([1.0, 0.95, 0.6, 0.2], n).astype(np.float32)
+    us = rng.random(n).astype(np.float32)
+    got = _run(B, rows, V, V, temps, ks, ps, us)
+    exact = 0
+    for r in range(n):
+        x = rows[r].astype(np.float64)
+        want = O.sample(x, float(temps[r]), int(ks[r]), float(ps[r]), float(us[r]))
+        if got[r] == want:
+            exact += 1
+            continue
+        assert temps[r] > 0, f"row {r}: greedy must be exact ({got[r]} vs {want})"
+        assert _allowed(x, float(temps[r]), int(ks[r]), float(ps[r]), float(us[r]), int(got[r])), \
+            f"row {r}: token {got[r]} is not a valid draw (oracle {want})"
+    log(f"[sample] full vocab: {exact}/{n} rows exactly the oracle's token")
+    assert exact >= n - 2
+
+
+def test_sample_small_vocab_strided_and_u_sweep(lib):
+    """vocab 50 in rows 151936 apart; one row swept over a uniform grid of u:
+    each token's share of the grid is its kept softmax probability."""
+    B = lib
+    rng = np.random.default_rng(62)
+    base = (rng.standard_normal(50) * 2).astype(np.float32)
+    n = 1024
+    rows = np.zeros((n, V), dtype=np.float32)
+    rows[:, :50] = base
+    rows[:, 50:] = 1e30                              # past `vocab`: must never be read as a candidate
+    us = ((np.arange(n) + 0.5) / n).astype(np.float32)
+    for t, k, p in ((1.0, 0, 1.0), (0.7, 10, 1.0), (1.3, 0, 0.8), (1.0, 3, 0.5)):
+        got = _run(B, rows, 50, V, [t] * n, [k] * n, [p] * n, us)
+        want = np.array([O.sample(base.astype(np.float64), t, k, p, float(u)) for u in us])
+        mism = np.flatnonzero(got != want)
+        for r in mism:
+            assert _allowed(base, t, k, p, float(us[r]), int(got[r]))
+        assert mism.size <= 4, mism.size
+        log(f"[sample] vocab 50, T={t} k={k} p={p}: {n - mism.size}/{n} grid points exact, "
+            f"{len(set(got.tolist()))} distinct tokens")
+
+
+def test_sample_greedy_rows_equal_argmax(lib):
+    B = lib
+    rng = np.random.default_rng(63)
+    n = 8
+    rows = rng.standard_normal((n, V)).astype(np.float32)
+    rows[3, 1000] = rows[3, 5] = 50.0                # tie: lowest index wins
+    got = _run(B, rows, V, V, [0.0] * n, [0] * n, [1.0] * n, [0.5] * n)
+    np.testing.assert_array_equal(got, np.argmax(rows, axis=1))
+    assert got[3] == 5
+
+
+def test_sample_unaligned_rows(lib):
+    """Rows 1001 floats apart (not 16-byte aligned): the element-wise load
+    path, against the oracle."""
+    B = lib
+    rng = np.random.default_rng(64)
+    n, vocab, stride = 64, 1000, 1001
+    rows = (rng.standard_normal((n, stride)) * 2).astype(np.float32)
+    temps = rng.choice([0.0, 0.6, 1.0], n).astype(np.float32)
+    ks = rng.choice([0, 1, 7, 300], n).astype(np.int32)
+    ps = rng.choice([1.0, 0.7], n).astype(np.float32)
+    us = rng.random(n).astype(np.float32)
+    got = _run(B, rows, vocab, stride, temps, ks, ps, us)
+    for r in range(n):
+        x = rows[r, :vocab].astype(np.float64)
+        want = O.sample(x, float(temps[r]), int(ks[r]), float(ps[r]), float(us[r]))
+        assert got[r] == want or _allowed(x, float(temps[r]), int(ks[r]), float(ps[r]), float(us[r]), int(got[r]))

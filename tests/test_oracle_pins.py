@@ -362,6 +362,86 @@ def test_argmax_crafted_rows():
 
 # ------------------------------------------------------------------ model level
 
+# ------------------------------------------------------------------ sampling
+
+def _sample_brute(x, temperature, top_k, top_p, u):
+    """The sampling steps written out with Python lists, sorted() and math.exp."""
+    if temperature <= 0:
+        return max(range(len(x)), key=lambda i: (x[i], -i))
+    z = [xi / temperature for xi in x]
+    k = 4096 if (top_k <= 0 or top_k > 4096) else top_k
+    k = min(k, len(z))
+    srt = sorted(range(len(z)), key=lambda i: (-z[i], i))
+    kth = z[srt[k - 1]]
+    cand = [i for i in srt if z[i] >= kth][:4096]
+    e = [math.exp(z[i] - z[cand[0]]) for i in cand]
+    p = 1.0 if not (0.0 < top_p <= 1.0) else top_p
+    total, run, cut = sum(e), 0.0, len(e) - 1
+    for j, ej in enumerate(e):
+        run += ej
+        if run >= p * total:
+            cut = j
+            break
+    kept = e[:cut + 1]
+    target, run = u * sum(kept), 0.0
+    for j, ej in enumerate(kept):
+        run += ej
+        if run > target:
+            return cand[j]
+    return cand[cut]
+
+
+def test_sample_matches_brute_force():
+    rng = np.random.default_rng(41)
+    for trial in range(300):
+        v = int(rng.integers(1, 40))
+        x = np.round(rng.standard_normal(v) * 3, 1 if trial % 3 == 0 else 6)   # some rows with ties
+        t = float(rng.choice([0.0, 0.3, 1.0, 2.5]))
+        k = int(rng.choice([0, 1, 2, 5, 50, 5000]))
+        p = float(rng.choice([1.0, 0.95, 0.5, 0.1, 0.0]))
+        u = float(rng.random())
+        assert O.sample(x, t, k, p, u) == _sample_brute(list(x), t, k, p, u), (trial, x, t, k, p, u)
+
+
+def test_sample_greedy_cases():
+    rng = np.random.default_rng(42)
+    x = rng.standard_normal(1000)
+    for u in (0.0, 0.5, 0.999):
+        assert O.sample(x, 0.0, 0, 1.0, u) == int(np.argmax(x))       # temperature 0: greedy
+        assert O.sample(x, 0.7, 1, 1.0, u) == int(np.argmax(x))       # top-k 1 (distinct values)
+        assert O.sample(x, 0.7, 0, 1e-9, u) == int(np.argmax(x))      # top-p near 0 keeps one token
+
+
+def test_sample_inverse_cdf_frequencies_are_the_softmax():
+    """Over a uniform grid of u, each token is chosen with its softmax(x/T)
+    probability (to the grid resolution): the distribution of "第 3 章" §4.3's
+    temperature path without truncation."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(43)
+    x = rng.standard_normal(12) * 2
+    n = 20000
+    counts = np.zeros(12)
+    for i in range(n):
+        counts[O.sample(x, 1.7, 0, 1.0, (i + 0.5) / n)] += 1
+    np.testing.assert_allclose(counts / n, softmax(x / 1.7), atol=2.0 / n)
+
+
+def test_sample_top_k_and_top_p_sets():
+    from scipy.special import softmax
+    rng = np.random.default_rng(44)
+    x = rng.standard_normal(64) * 2
+    us = (np.arange(400) + 0.5) / 400
+    chosen = {O.sample(x, 1.0, 5, 1.0, u) for u in us}
+    assert chosen <= set(np.argsort(-x)[:5].tolist()) and len(chosen) == 5
+    # top-p: the kept tokens are the shortest most-probable prefix reaching the mass
+    for p in (0.3, 0.6, 0.9):
+        prob = softmax(x)[np.argsort(-x)]
+        c = int(np.argmax(np.cumsum(prob) >= p))
+        assert np.sum(prob[:c + 1]) >= p and (c == 0 or np.sum(prob[:c]) < p)
+        chosen = {O.sample(x, 1.0, 0, p, u) for u in us}
+        assert chosen == set(np.argsort(-x)[:c + 1].tolist())
+
+
 def test_causality_future_tokens_do_not_change_past():
     m, _ = tiny_model(seed=11)
     ids = I.token_ids(12, (2, 9), vocab=64)
