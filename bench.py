@@ -42,7 +42,13 @@ WORKLOADS = {
     "decode_b32_ctx2048": (32, 2048, 128, False),
     "prefill_8x4096": (8, 4096, 0, True),
     "decode_b4_ctx32768": (4, 32768, 64, False),
+    # packed ragged prefill: 16 prompts of seeded lengths in [256, 3840] (about 32K tokens)
+    "prefill_packed_ragged": (16, 0, 0, True),
 }
+
+
+def ragged_lengths(n=16, lo=256, hi=3840, seed=77):
+    return np.random.default_rng(seed).integers(lo, hi + 1, n).tolist()
 
 
 def log(*a):
@@ -86,11 +92,21 @@ class Runner:
                            torch.empty((batch, B.VOCAB), dtype=torch.float32, device="cuda"))
         self.batch, self.T, self.steps = batch, prompt_len, steps
         from decoder_only_transformer_qwen3_amd import inputs as I
-        self.ids_np = I.token_ids(1000 + batch, (batch, prompt_len))
+        self.lens = None
+        if prompt_len == 0:  # packed ragged prompts
+            self.lens = ragged_lengths(batch)
+            self.ids_np = I.token_ids(1000 + batch, (1, sum(self.lens)))[0]
+            self.cu = torch.tensor(np.concatenate([[0], np.cumsum(self.lens)]).astype(np.int32), device="cuda")
+            prompt_len = max(self.lens)
+            self.T = prompt_len
+            nb = B.q3_workspace_bytes_packed(batch, int(sum(self.lens)))
+            self.ws_p, self.nb_p = torch.empty(nb, dtype=torch.uint8, device="cuda"), nb
+        else:
+            self.ids_np = I.token_ids(1000 + batch, (batch, prompt_len))
+            self.ws_p, self.nb_p = dev.workspace(batch, prompt_len)
         self.ids = torch.from_numpy(self.ids_np).cuda()
         self.max_seq = (prompt_len + max(steps, 1) + 7) // 8 * 8  # capacity: a multiple of 8
         self.kv = dev.DeviceKV(batch, self.max_seq)
-        self.ws_p, self.nb_p = dev.workspace(batch, prompt_len)
         self.ws_d, self.nb_d = dev.workspace(batch, 1)
         self.nxt = torch.zeros(batch, dtype=torch.int32, device="cuda")
         self.seq = torch.zeros(batch, dtype=torch.int32, device="cuda")
@@ -99,6 +115,10 @@ class Runner:
 
     def prefill(self):
         B = self.B
+        if self.lens is not None:
+            B.q3_prefill_packed(self.dm.struct, self.kv.struct, self.batch, int(sum(self.lens)), self.ids, self.cu,
+                                None, max(self.lens), None, self.nxt, self.seq, self.ws_p, self.nb_p)
+            return
         B.q3_prefill(self.dm.struct, self.kv.struct, self.batch, self.T, self.ids, None, self.nxt, self.seq,
                      self.ws_p, self.nb_p)
 
@@ -206,6 +226,16 @@ def dominant_kernel(torch, B, dev, dm, r, workload, iters, use_graph=True):
             "weight bytes + activation bytes per launch"
         iters = max(iters, 280)
         reps = 28
+    elif workload == "prefill_packed_ragged":
+        # the largest GEMM over all packed rows (persistent MFMA kernel), as in the step
+        M, N, K = int(sum(r.lens)), 2 * B.INTER, B.HIDDEN
+        x = torch.randn((M, K), device="cuda").to(torch.bfloat16)
+        out = torch.empty((M, N // 2), dtype=torch.bfloat16, device="cuda")
+        w = dm.layers[0].w_gate_up
+        fn = lambda: B.q3_linear(x, w, out, M, N, K, N // 2, B.Q3_EPI_SILU_GATE)
+        algo = float(2 * M * N * K)
+        name, bound, per = f"k_gemm_persist<EPI_SILU> (gate|up, M={M} N={N} K={K})", "mfma", "2*M*N*K flops"
+        reps = 10
     elif workload in ("decode_b32_ctx2048", "decode_b4_ctx32768"):
         reps = 10
         p = T + steps // 2  # middle of the timed decode steps
@@ -247,6 +277,7 @@ KERNEL_SOURCES = {
     "decode_b32_ctx2048": ["attn_decode.hip", "common.hpp"],
     "decode_b4_ctx32768": ["attn_decode.hip", "common.hpp"],
     "prefill_8x4096": ["attn_prefill.hip", "common.hpp"],
+    "prefill_packed_ragged": ["gemm_tiled.hip", "common.hpp"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -278,8 +309,9 @@ def step_roofline(workload, pre_ms, dec_ms):
     """Whole-phase figure for context: algorithmic bytes (decode) or flops
     (prefill-bound workload) of the timed phase over its measured time."""
     batch, T, steps, prefill_timed = WORKLOADS[workload]
-    if workload == "prefill_8x4096":
-        flops = batch * T * 2 * LAYER_MATMUL_PARAMS * 28 + batch * (T * (T + 1) // 2) * 8192 * 28 \
+    if workload in ("prefill_8x4096", "prefill_packed_ragged"):
+        lens = [T] * batch if workload == "prefill_8x4096" else ragged_lengths(batch)
+        flops = sum(lens) * 2 * LAYER_MATMUL_PARAMS * 28 + sum(t * (t + 1) // 2 for t in lens) * 8192 * 28 \
             + batch * 2 * LMHEAD_PARAMS
         a = flops / (pre_ms * 1e-3) / 1e12
         return {"phase": "prefill", "bound": "mfma", "achieved": round(a, 1), "peak": BF16_PEAK_TFLOPS,
@@ -320,7 +352,7 @@ def cpu_baseline(workload, bits):
         el = time.perf_counter() - t0
         sample = f"sequence 0: {T}-token prefill + {n_dec} greedy decode steps ({T + n_dec} tokens)"
         toks = T + n_dec
-    elif workload == "prefill_8x4096":
+    elif workload in ("prefill_8x4096", "prefill_packed_ragged"):
         Tp = 1024
         t0 = time.perf_counter()
         O.prefill(om, ids[:, :Tp])
@@ -434,7 +466,7 @@ def main():
     dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     step_ms = wall * 1e3 / args.steps
 
-    tokens_prefill = batch * T if prefill_timed else 0
+    tokens_prefill = (sum(r.lens) if r.lens is not None else batch * T) if prefill_timed else 0
     tokens_decode = batch * steps
     value = (tokens_prefill + tokens_decode) / (step_ms * 1e-3)
     out = {
@@ -445,7 +477,8 @@ def main():
         "config": {"workload": args.workload, "layers": 28, "batch": batch, "prompt_len": T,
                    "decode_steps": steps, "prefill_timed": prefill_timed, "hip_graph": use_graph,
                    "parallelism": "single GPU", **({"eos_id": args.eos_id} if args.eos_id is not None else {}),
-                   **({"sampling": args.sample} if args.sample else {})},
+                   **({"sampling": args.sample} if args.sample else {}),
+                   **({"packed_lengths": r.lens, "packed_tokens": sum(r.lens)} if r.lens is not None else {})},
         "prefill_ms": round(pre_ms, 4), "decode_ms": round(dec_ms, 4),
         "prefill_tok_s": round(tokens_prefill / (pre_ms * 1e-3), 1) if prefill_timed else None,
         "decode_tok_s": round(tokens_decode / (dec_ms * 1e-3), 1) if steps > 0 else None,

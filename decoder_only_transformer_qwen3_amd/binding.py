@@ -69,13 +69,16 @@ _rope_conv = _sig("q3_rope_interleaved_to_half", ctypes.c_int, _vp, _vp, _vp, _v
 _decode_eos = _sig("q3_decode_step_eos", ctypes.c_int, ctypes.POINTER(q3_model), ctypes.POINTER(q3_kv), _i32, _vp,
                      _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp)
 _sample = _sig("q3_sample", ctypes.c_int, _vp, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp)
+_wsb_packed = _sig("q3_workspace_bytes_packed", _sz, _i32, _i32)
+_prefill_packed = _sig("q3_prefill_packed", ctypes.c_int, ctypes.POINTER(q3_model), ctypes.POINTER(q3_kv), _i32, _i32,
+                       _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp)
 
 Q3_EPI_STORE_BF16, Q3_EPI_STORE_F32, Q3_EPI_ADD_F32, Q3_EPI_SILU_GATE = 0, 1, 2, 3
 
 EXPORTS = ("q3_status_str", "q3_rope_table_host", "q3_workspace_bytes", "q3_layer_forward",
            "q3_prefill", "q3_decode_step", "q3_argmax", "q3_linear", "q3_attention_prefill",
            "q3_attention_decode", "q3_rope_interleaved_to_half", "q3_decode_step_eos",
-           "q3_sample")
+           "q3_sample", "q3_workspace_bytes_packed", "q3_prefill_packed")
 
 
 class Q3Error(RuntimeError):
@@ -211,4 +214,18 @@ def q3_sample(logits, rows, vocab, row_stride, temperature, top_k, top_p, unifor
                  _ptr(out_idx), _stream(stream))
     if check:
         _check(st, "q3_sample")
+    return st
+
+
+def q3_workspace_bytes_packed(n_seqs: int, n_tokens: int) -> int:
+    return int(_wsb_packed(n_seqs, n_tokens))
+
+
+def q3_prefill_packed(m: q3_model, kv: q3_kv, n_seqs, n_tokens, ids, cu_seqlens, start_pos, max_seq_tokens,
+                      last_logits, next_ids, seq_lens, ws, ws_bytes, stream=None, check=True) -> int:
+    st = _prefill_packed(ctypes.byref(m), ctypes.byref(kv), n_seqs, n_tokens, _ptr(ids), _ptr(cu_seqlens),
+                         _ptr(start_pos), max_seq_tokens, _ptr(last_logits), _ptr(next_ids), _ptr(seq_lens),
+                         _ptr(ws), ws_bytes, _stream(stream))
+    if check:
+        _check(st, "q3_prefill_packed")
     return st

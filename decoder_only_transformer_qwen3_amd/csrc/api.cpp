@@ -32,8 +32,8 @@ struct Ws {
   void* amax;
 };
 
-Ws carve(void* base, int32_t batch, int32_t n_tokens) {
-  const q3v::WsLayout L = q3v::ws_layout(batch, n_tokens);
+Ws carve_rows(void* base, int32_t batch, int64_t rows, bool one_token) {
+  const q3v::WsLayout L = q3v::ws_layout_rows(batch, rows, one_token);
   char* p = static_cast<char*>(base);
   Ws w;
   w.resid = reinterpret_cast<float*>(p + L.resid);
@@ -53,12 +53,19 @@ Ws carve(void* base, int32_t batch, int32_t n_tokens) {
   return w;
 }
 
+Ws carve(void* base, int32_t batch, int32_t n_tokens) {
+  return carve_rows(base, batch, (int64_t)batch * n_tokens, n_tokens == 1);
+}
+
 struct LayerCtx {
   const q3_layer_weights* w;
   const float *cos, *sin;
   uint16_t *kl, *vl;
   int B, T, max_seq, start;
   const int32_t* pos_dev;  // per-sequence start positions on the device (decode), or null
+  int M;                   // rows of the call (all sequences)
+  SeqMap sm;               // row -> (sequence, position); packed or uniform
+  int max_T;               // bound on the rows of one sequence
   int dec_splits;          // decode-attention splits (T == 1 only)
   bool dec_stream;         // decode attention in its streaming configuration (T == 1 only)
   float* resid;
@@ -80,7 +87,7 @@ inline void skinny_normed(const LayerCtx& c, const void* W, void* out, int N, in
   a.X = c.ws.h;
   a.W = U(W);
   a.out = out;
-  a.M = c.B * c.T;
+  a.M = c.M;
   a.N = N;
   a.K = C;
   a.ldo = ldo;
@@ -96,7 +103,7 @@ inline void skinny_normed(const LayerCtx& c, const void* W, void* out, int N, in
 // workgroup per column block adds the splits.
 inline void skinny_residual(const LayerCtx& c, const uint16_t* X, const void* W, int K, int n_split,
                             const uint16_t* gamma) {
-  const int M = c.B * c.T;
+  const int M = c.M;
   if (M <= GEMV_MAX_ROWS) {
     launch_gemv_resid(X, U(W), K, c.resid, M, gamma, c.ws.h, c.ws.ssq, c.s);
     return;
@@ -123,7 +130,7 @@ inline void skinny_residual(const LayerCtx& c, const uint16_t* X, const void* W,
 // and ws.ssq = the row sums of squares, and leaves the same for gamma_next;
 // above that the norms run as separate kernels around the tiled GEMMs.
 void run_layer(const LayerCtx& c) {
-  const int M = c.B * c.T;
+  const int M = c.M;
   const bool skinny = skinny_rows(M);
   const q3_layer_weights* w = c.w;
   // input RMSNorm + merged q|k|v projection
@@ -138,9 +145,9 @@ void run_layer(const LayerCtx& c) {
     launch_attn_decode(c.ws.qkv, U(w->q_norm), U(w->k_norm), c.cos, c.sin, c.kl, c.vl, c.ws.apart, c.ws.tick + 64,
                        c.ws.ao, c.B, c.max_seq, c.pos_dev, c.start, c.dec_splits, c.dec_stream, c.s);
   } else {
-    launch_qknorm_rope(c.ws.qkv, U(w->q_norm), U(w->k_norm), c.cos, c.sin, c.ws.qr, c.kl, c.vl, c.B, c.T,
-                       c.max_seq, c.pos_dev, c.start, c.s);
-    launch_attn_prefill(c.ws.qr, c.kl, c.vl, c.ws.ao, c.B, c.T, c.start, c.max_seq, c.s);
+    launch_qknorm_rope(c.ws.qkv, U(w->q_norm), U(w->k_norm), c.cos, c.sin, c.ws.qr, c.kl, c.vl, c.sm, c.max_T,
+                       c.max_seq, c.s);
+    launch_attn_prefill(c.ws.qr, c.kl, c.vl, c.ws.ao, c.sm, c.max_T, c.max_seq, c.s);
   }
   // o_proj + residual, post-attention RMSNorm, gate|up with silu(gate) * up, down + residual
   if (skinny) {
@@ -160,11 +167,19 @@ void run_layer(const LayerCtx& c) {
 // skinny path the last layer already left bf16(gamma_f * r) and the sums of
 // squares for every row; otherwise they are formed here for the B last rows.
 void run_head(const q3_model* m, const Ws& ws, int B, int T, float* logits, int32_t* next_ids, int32_t* seq_lens,
-              int seq_mode, int seq_val, hipStream_t s, const int32_t* in_ids = nullptr, int eos = -1) {
+              int seq_mode, int seq_val, hipStream_t s, const int32_t* in_ids = nullptr, int eos = -1,
+              const SeqMap* packed = nullptr) {
   const uint16_t* X;
   const float* ssq;
   int ldx, ssq_ld, ssq_n;
-  if (skinny_rows(B * T)) {
+  if (packed) {  // each sequence's last row, gathered through the row map
+    ssq_n = NSQ_BLK;
+    launch_norm_operand(ws.resid, B, 1, 0, U(m->final_norm), ws.fh, ws.ssq, ssq_n, nullptr, 0, s, packed);
+    X = ws.fh;
+    ldx = C;
+    ssq = ws.ssq;
+    ssq_ld = ssq_n;
+  } else if (skinny_rows(B * T)) {
     ssq_n = nsq_for(B * T);
     X = ws.h + (size_t)(T - 1) * C;
     ldx = T * C;
@@ -197,7 +212,7 @@ void run_head(const q3_model* m, const Ws& ws, int B, int T, float* logits, int3
     a.ssq_n = ssq_n;
     launch_gemm_skinny(a, 1, EPI_LOGITS, s);
   }
-  launch_argmax_partials(ws.amax, B, n_part, next_ids, seq_lens, seq_mode, seq_val, in_ids, eos, s);
+  launch_argmax_partials(ws.amax, B, n_part, next_ids, seq_lens, seq_mode, seq_val, in_ids, eos, s, packed);
 }
 
 inline int launch_status() { return hipGetLastError() == hipSuccess ? Q3_OK : Q3_ERR_HIP; }
@@ -256,6 +271,9 @@ int q3_layer_forward(const q3_layer_weights* w, const float* rope_cos, const flo
   c.vl = static_cast<uint16_t*>(v_layer);
   c.B = batch;
   c.T = n_tokens;
+  c.M = batch * n_tokens;
+  c.sm = SeqMap{nullptr, nullptr, batch, n_tokens, start_pos, batch * n_tokens};
+  c.max_T = n_tokens;
   c.max_seq = max_seq;
   c.start = start_pos;
   c.pos_dev = nullptr;
@@ -289,6 +307,9 @@ int q3_prefill(const q3_model* m, const q3_kv* kv, int32_t batch, int32_t prompt
   c.sin = m->rope_sin;
   c.B = batch;
   c.T = prompt_len;
+  c.M = batch * prompt_len;
+  c.sm = SeqMap{nullptr, nullptr, batch, prompt_len, 0, batch * prompt_len};
+  c.max_T = prompt_len;
   c.max_seq = kv->max_seq;
   c.start = 0;
   c.pos_dev = nullptr;
@@ -308,6 +329,52 @@ int q3_prefill(const q3_model* m, const q3_kv* kv, int32_t batch, int32_t prompt
   return launch_status();
 }
 
+size_t q3_workspace_bytes_packed(int32_t n_seqs, int32_t n_tokens) {
+  if (n_seqs < 1 || n_tokens < 1) return 0;
+  return q3v::ws_layout_rows(n_seqs, n_tokens, false).total;
+}
+
+int q3_prefill_packed(const q3_model* m, const q3_kv* kv, int32_t n_seqs, int32_t n_tokens, const int32_t* ids,
+                      const int32_t* cu_seqlens, const int32_t* start_pos, int32_t max_seq_tokens,
+                      float* last_logits, int32_t* next_ids, int32_t* seq_lens, void* ws, size_t ws_bytes,
+                      void* stream) {
+  const int st = q3v::check_prefill_packed_call(m, kv, n_seqs, n_tokens, ids, cu_seqlens, start_pos, max_seq_tokens,
+                                                last_logits, next_ids, seq_lens, ws, ws_bytes);
+  if (st != Q3_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const Ws wsp = carve_rows(ws, n_seqs, n_tokens, false);
+  const int M = n_tokens;
+  const bool sk = skinny_rows(M);
+  launch_embed(ids, U(m->embed), wsp.resid, M, sk ? U(m->layer[0].input_norm) : nullptr, wsp.h, wsp.ssq, nsq_for(M),
+               wsp.tick, wsp.n_tick, s);
+  LayerCtx c;
+  c.cos = m->rope_cos;
+  c.sin = m->rope_sin;
+  c.B = n_seqs;
+  c.T = 0;  // rows per sequence vary: never the one-token path
+  c.M = M;
+  c.sm = SeqMap{cu_seqlens, start_pos, n_seqs, 0, 0, n_tokens};
+  c.max_T = max_seq_tokens;
+  c.max_seq = kv->max_seq;
+  c.start = 0;
+  c.pos_dev = nullptr;
+  c.dec_splits = 1;
+  c.dec_stream = false;
+  c.resid = wsp.resid;
+  c.ws = wsp;
+  c.s = s;
+  for (int l = 0; l < NL; ++l) {
+    c.w = &m->layer[l];
+    c.kl = layer_cache(kv->k, l, kv);
+    c.vl = layer_cache(kv->v, l, kv);
+    c.gamma_next = U(l + 1 < NL ? m->layer[l + 1].input_norm : m->final_norm);
+    run_layer(c);
+  }
+  run_head(m, wsp, n_seqs, 0, last_logits ? last_logits : wsp.logits, next_ids, seq_lens, 3, 0, s, nullptr, -1,
+           &c.sm);
+  return launch_status();
+}
+
 int q3_decode_step_eos(const q3_model* m, const q3_kv* kv, int32_t batch, const int32_t* in_ids, int32_t* seq_lens,
                        int32_t max_len_hint, int32_t eos_id, float* logits, int32_t* out_ids, void* ws,
                        size_t ws_bytes, void* stream) {
@@ -324,6 +391,9 @@ int q3_decode_step_eos(const q3_model* m, const q3_kv* kv, int32_t batch, const 
   c.sin = m->rope_sin;
   c.B = batch;
   c.T = 1;
+  c.M = batch;
+  c.sm = SeqMap{nullptr, seq_lens, batch, 1, 0, batch};
+  c.max_T = 1;
   c.max_seq = kv->max_seq;
   c.start = 0;
   c.pos_dev = seq_lens;
@@ -366,7 +436,8 @@ int q3_attention_prefill(const void* q, const void* k_layer, const void* v_layer
                          int32_t start_pos, int32_t max_seq, void* out, void* stream) {
   const int st = q3v::check_attn_prefill_call(q, k_layer, v_layer, batch, n_tokens, start_pos, max_seq, out);
   if (st != Q3_OK) return st;
-  launch_attn_prefill(U(q), U(k_layer), U(v_layer), static_cast<uint16_t*>(out), batch, n_tokens, start_pos, max_seq,
+  const SeqMap sm{nullptr, nullptr, batch, n_tokens, start_pos, batch * n_tokens};
+  launch_attn_prefill(U(q), U(k_layer), U(v_layer), static_cast<uint16_t*>(out), sm, n_tokens, max_seq,
                       static_cast<hipStream_t>(stream));
   return launch_status();
 }

@@ -2,7 +2,8 @@
 // chunk at an offset):  o_h[t] = sum_{j <= p(t)} softmax_j(q_h[t].k_g[j] / sqrt(128)) v_g[j]
 // with g = h / 2 ("手写Qwen3-0.6B推理" §Attention; "第 3 章" §3.3).
 //
-// One workgroup = one KV head g of one sequence and 64 query positions, for
+// One workgroup = one KV head g of one sequence and 64 query positions
+// (sequences may differ in length and start: packed rows), for
 // both query heads 2g and 2g+1 that share g, so each K/V tile staged in LDS
 // feeds 128 query rows.  4 waves: wave w takes head 2g + w/2 and 32
 // positions.  Two workgroups share a CU, so each SIMD runs two waves whose
@@ -52,12 +53,15 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_prefill(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k_cache,
                                                          const uint16_t* __restrict__ v_cache,
-                                                         uint16_t* __restrict__ out, int T, int start,
-                                                         int max_seq) {
+                                                         uint16_t* __restrict__ out, SeqMap sm, int max_seq) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[FA_NS][2][FA_TILE];
 
   const int qt = gridDim.x - 1 - blockIdx.x;  // longest (latest) tiles first
   const int g = blockIdx.y, b = blockIdx.z;
+  const int T = sm_len(sm, b), row0 = sm_row0(sm, b);
+  int start = sm_start(sm, b);
+  start = start < 0 ? 0 : start;
+  if (qt * FA_BQ >= T || start + T > max_seq) return;  // past this sequence's rows (whole workgroup)
   const int tid = threadIdx.x, l = tid & 63, lq = l & 31, lh = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
   const int hq = 2 * g + (w >> 1);
@@ -74,7 +78,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   {
     int tq = t0 + lq;
     tq = tq < T ? tq : T - 1;
-    const uint16_t* qrow = q + ((size_t)b * T + tq) * QDIM + hq * D + 8 * lh;
+    const uint16_t* qrow = q + ((size_t)row0 + tq) * QDIM + hq * D + 8 * lh;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qreg[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s);
   }
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (tq < T) {
       const float inv = 1.0f / l_tot;
-      uint16_t* orow = out + ((size_t)b * T + tq) * QDIM + hq * D;
+      uint16_t* orow = out + ((size_t)row0 + tq) * QDIM + hq * D;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -254,10 +258,10 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   }
 }
 
-void launch_attn_prefill(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out, int B,
-                         int T, int start, int max_seq, hipStream_t s) {
-  const dim3 grid((T + FA_BQ - 1) / FA_BQ, HKV, B);
-  hipLaunchKernelGGL(k_attn_prefill, grid, dim3(256), 0, s, q, k_cache, v_cache, out, T, start, max_seq);
+void launch_attn_prefill(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out,
+                         const SeqMap& sm, int max_T, int max_seq, hipStream_t s) {
+  const dim3 grid((max_T + FA_BQ - 1) / FA_BQ, HKV, sm.n);
+  hipLaunchKernelGGL(k_attn_prefill, grid, dim3(256), 0, s, q, k_cache, v_cache, out, sm, max_seq);
 }
 
 }  // namespace q3

@@ -90,6 +90,47 @@ __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70);
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Rows of a multi-token call and the (sequence, position) each belongs to.
+// Uniform: n sequences of T rows, row m = s*T + t at position
+// (pos ? pos[s] : start) + t.  Packed (off != null): sequence s owns rows
+// off[s] .. off[s+1]-1 at positions (pos ? pos[s] : 0) + t, and there are
+// rows = off[n] of them.  The row offsets come from the caller's device
+// memory, so every lookup is clamped to [0, rows]: bad offsets give wrong
+// sequences, never out-of-range rows.
+struct SeqMap {
+  const int32_t* off;
+  const int32_t* pos;
+  int n, T, start, rows;
+};
+__device__ __forceinline__ int sm_row0(const SeqMap& sm, int s) {
+  if (!sm.off) return s * sm.T;
+  const int r = sm.off[s];
+  return r < 0 ? 0 : (r > sm.rows ? sm.rows : r);
+}
+__device__ __forceinline__ int sm_len(const SeqMap& sm, int s) {
+  if (!sm.off) return sm.T;
+  const int r1 = sm.off[s + 1];
+  const int e = r1 < 0 ? 0 : (r1 > sm.rows ? sm.rows : r1);
+  const int b = sm_row0(sm, s);
+  return e > b ? e - b : 0;
+}
+__device__ __forceinline__ int sm_start(const SeqMap& sm, int s) {
+  return sm.pos ? sm.pos[s] : (sm.off ? 0 : sm.start);
+}
+// the sequence holding row m: the last s with off[s] <= m (binary search)
+__device__ __forceinline__ int sm_seq(const SeqMap& sm, int m) {
+  if (!sm.off) return m / sm.T;
+  int lo = 0, hi = sm.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (sm.off[mid] <= m)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);

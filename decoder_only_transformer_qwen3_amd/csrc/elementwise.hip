@@ -77,12 +77,18 @@ void launch_embed(const int32_t* ids, const uint16_t* E, float* resid, int M, co
 __global__ __launch_bounds__(256) void k_norm_operand(const float* __restrict__ resid, int n_rows, int row_step,
                                                       int row_off, const uint16_t* __restrict__ gamma,
                                                       uint16_t* __restrict__ hg, float* __restrict__ ssq, int nsq,
-                                                      int* __restrict__ counters, int n_counters) {
+                                                      int* __restrict__ counters, int n_counters, SeqMap last) {
   clear_tickets(counters, n_counters);
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= n_rows) return;
-  const f32x4* src = reinterpret_cast<const f32x4*>(resid + ((size_t)r * row_step + row_off) * C + 16 * lane);
+  // packed rows (last.off set): the last row of sequence r
+  size_t row = (size_t)r * row_step + row_off;
+  if (last.off) {
+    const int e = sm_row0(last, r) + sm_len(last, r);
+    row = e > 0 ? (size_t)(e - 1) : 0;
+  }
+  const f32x4* src = reinterpret_cast<const f32x4*>(resid + row * C + 16 * lane);
   float x[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -96,10 +102,12 @@ __global__ __launch_bounds__(256) void k_norm_operand(const float* __restrict__ 
 }
 
 void launch_norm_operand(const float* resid, int n_rows, int row_step, int row_off, const uint16_t* gamma,
-                         uint16_t* hg, float* ssq, int nsq, int* counters, int n_counters, hipStream_t s) {
+                         uint16_t* hg, float* ssq, int nsq, int* counters, int n_counters, hipStream_t s,
+                         const SeqMap* last) {
   const int blocks = n_rows > 0 ? (n_rows + 3) / 4 : 1;  // one block still clears the tickets
+  const SeqMap none{nullptr, nullptr, 0, 1, 0, 0};
   hipLaunchKernelGGL(k_norm_operand, dim3(blocks), dim3(256), 0, s, resid, n_rows, row_step, row_off,
-                     gamma, hg, ssq, nsq, counters, n_counters);
+                     gamma, hg, ssq, nsq, counters, n_counters, last ? *last : none);
 }
 
 // ---------------------------------------------------------------- RMSNorm
@@ -167,14 +175,13 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ k_norm,
                                                       const float* __restrict__ rope_cos,
                                                       const float* __restrict__ rope_sin, uint16_t* __restrict__ q_out,
-                                                      uint16_t* __restrict__ k_cache, int B, int T, int max_seq,
-                                                      const int32_t* __restrict__ pos_dev, int start) {
+                                                      uint16_t* __restrict__ k_cache, SeqMap sm, int max_seq) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + wave;
   const int m = gw / 6, hg = gw - m * 6;
-  if (m >= B * T) return;
-  const int b = m / T, t = m - b * T;
-  const int p = (pos_dev ? pos_dev[b] : start) + t;
+  if (m >= sm.rows) return;
+  const int b = sm_seq(sm, m), t = m - sm_row0(sm, b);
+  const int p = sm_start(sm, b) + t;
   const int head = hg * 4 + (lane >> 4);  // 0..15 query heads, 16..23 key heads
   const int j4 = 4 * (lane & 15);
   const uint16_t* src = qkv + (size_t)m * QKV_N + head * D;
@@ -220,11 +227,12 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(const uint16_t* __restrict
 // sequence): the block's tokens are staged in LDS and written back as
 // position-contiguous 8-byte groups; positions outside the call's range are
 // left untouched (they may hold earlier tokens).
-__global__ __launch_bounds__(256) void k_v_store(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ v_cache, int B,
-                                                 int T, int max_seq, const int32_t* __restrict__ pos_dev, int start) {
+__global__ __launch_bounds__(256) void k_v_store(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ v_cache,
+                                                 SeqMap sm, int max_seq) {
   __shared__ uint16_t tile[VBLK][D];
   const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int p_first = (pos_dev ? pos_dev[b] : start);
+  const int T = sm_len(sm, b), row0 = sm_row0(sm, b);
+  const int p_first = sm_start(sm, b);
   const int pb = (p_first >> 3) + blockIdx.x;  // position block
   const int p_lo = p_first > pb * VBLK ? p_first : pb * VBLK;
   const int p_hi = (p_first + T) < (pb + 1) * VBLK ? (p_first + T) : (pb + 1) * VBLK;
@@ -234,7 +242,7 @@ __global__ __launch_bounds__(256) void k_v_store(const uint16_t* __restrict__ qk
     const int p = pb * VBLK + tt;
     u32x2 v = {0u, 0u};
     if (p >= p_lo && p < p_hi) {
-      const size_t m = (size_t)b * T + (p - p_first);
+      const size_t m = (size_t)row0 + (p - p_first);
       v = *reinterpret_cast<const u32x2*>(qkv + m * QKV_N + (HQ + HKV) * D + g * D + d4);
     }
     *reinterpret_cast<u32x2*>(&tile[tt][d4]) = v;
@@ -256,14 +264,13 @@ __global__ __launch_bounds__(256) void k_v_store(const uint16_t* __restrict__ qk
 
 void launch_qknorm_rope(const uint16_t* qkv, const uint16_t* q_norm, const uint16_t* k_norm,
                         const float* rope_cos, const float* rope_sin, uint16_t* q_out, uint16_t* k_cache,
-                        uint16_t* v_cache, int B, int T, int max_seq, const int32_t* pos_dev, int start,
-                        hipStream_t s) {
-  const int waves = B * T * 6;
+                        uint16_t* v_cache, const SeqMap& sm, int max_T, int max_seq, hipStream_t s) {
+  const int waves = sm.rows * 6;
   hipLaunchKernelGGL(k_qk_norm_rope, dim3((waves + 3) / 4), dim3(256), 0, s, qkv, q_norm, k_norm, rope_cos, rope_sin,
-                     q_out, k_cache, B, T, max_seq, pos_dev, start);
-  // an unaligned run of T positions touches at most T/8 + 2 blocks
-  const int nblk = T / VBLK + 2;
-  hipLaunchKernelGGL(k_v_store, dim3(nblk, HKV, B), dim3(256), 0, s, qkv, v_cache, B, T, max_seq, pos_dev, start);
+                     q_out, k_cache, sm, max_seq);
+  // an unaligned run of up to max_T positions touches at most max_T/8 + 2 blocks
+  const int nblk = max_T / VBLK + 2;
+  hipLaunchKernelGGL(k_v_store, dim3(nblk, HKV, sm.n), dim3(256), 0, s, qkv, v_cache, sm, max_seq);
 }
 
 // ---------------------------------------------------------------- argmax
@@ -304,12 +311,15 @@ __device__ __forceinline__ void am_wave_block_reduce(float& best, int& bi, float
 // seq_mode 2 with eos >= 0: a row whose input token in_ids[r] is eos has
 // finished; it keeps its length and emits eos again (in_ids may alias
 // out_idx: it is read first).
+// seq_mode 3 (packed prefill): seq_lens[r] = start + rows of sequence r.
 __device__ __forceinline__ void am_finish(int r, int bi, int32_t* out_idx, int32_t* seq_lens, int seq_mode,
-                                          int seq_val, const int32_t* in_ids = nullptr, int eos = -1) {
+                                          int seq_val, const int32_t* in_ids = nullptr, int eos = -1,
+                                          const SeqMap* sm = nullptr) {
   const bool fin = seq_mode == 2 && eos >= 0 && in_ids[r] == eos;
   out_idx[r] = fin ? eos : bi;
   if (seq_mode == 1) seq_lens[r] = seq_val;
   if (seq_mode == 2 && !fin) seq_lens[r] += 1;
+  if (seq_mode == 3) seq_lens[r] = sm_start(*sm, r) + sm_len(*sm, r);
 }
 
 // One block of 1024 threads per row; 16 B loads when the row is 16-byte
@@ -378,7 +388,7 @@ void launch_argmax(const float* logits, int rows, int vocab, int64_t row_stride,
 __global__ __launch_bounds__(1024) void k_argmax_partials(const float2* __restrict__ part, int n_part,
                                                           int32_t* out_idx, int32_t* __restrict__ seq_lens,
                                                           int seq_mode, int seq_val, const int32_t* in_ids,
-                                                          int eos) {
+                                                          int eos, SeqMap sm) {
   __shared__ float sv[16];
   __shared__ int si[16];
   const int r = blockIdx.x, tid = threadIdx.x;
@@ -402,13 +412,15 @@ __global__ __launch_bounds__(1024) void k_argmax_partials(const float2* __restri
     }
   }
   am_wave_block_reduce(best, bi, sv, si);
-  if (tid == 0) am_finish(r, bi, out_idx, seq_lens, seq_mode, seq_val, in_ids, eos);
+  if (tid == 0) am_finish(r, bi, out_idx, seq_lens, seq_mode, seq_val, in_ids, eos, &sm);
 }
 
 void launch_argmax_partials(const void* part, int rows, int n_part, int32_t* out_idx, int32_t* seq_lens,
-                            int seq_mode, int seq_val, const int32_t* in_ids, int eos, hipStream_t s) {
+                            int seq_mode, int seq_val, const int32_t* in_ids, int eos, hipStream_t s,
+                            const SeqMap* sm) {
+  const SeqMap none{nullptr, nullptr, 0, 1, 0, 0};
   hipLaunchKernelGGL(k_argmax_partials, dim3(rows), dim3(1024), 0, s, static_cast<const float2*>(part), n_part,
-                     out_idx, seq_lens, seq_mode, seq_val, in_ids, eos);
+                     out_idx, seq_lens, seq_mode, seq_val, in_ids, eos, sm ? *sm : none);
 }
 
 // ---------------------------------------------------------------------------

@@ -26,8 +26,10 @@ void launch_embed(const int32_t* ids, const uint16_t* E, float* resid, int M, co
 
 // hg[r] = bf16(gamma * resid[r*row_step + row_off]) and ssq[r][nsq] for r < n_rows;
 // clears n_counters tickets.
+// With `last` (packed rows), row r is instead the last row of sequence r.
 void launch_norm_operand(const float* resid, int n_rows, int row_step, int row_off, const uint16_t* gamma,
-                         uint16_t* hg, float* ssq, int nsq, int* counters, int n_counters, hipStream_t s);
+                         uint16_t* hg, float* ssq, int nsq, int* counters, int n_counters, hipStream_t s,
+                         const SeqMap* last = nullptr);
 
 // For r < n_rows, row = r*row_step + row_off:
 //   resid[row] += sum_{j < n_part} part[j][row]      (written back when n_part > 0)
@@ -36,12 +38,12 @@ void launch_norm_operand(const float* resid, int n_rows, int row_step, int row_o
 void launch_rmsnorm(float* resid, const float* part, int n_part, int part_rows, const uint16_t* gamma,
                     uint16_t* out, int n_rows, int row_step, int row_off, hipStream_t s);
 
-// Per-head q/k RMSNorm + NeoX RoPE + KV-cache write for M = B*T rows of the
-// merged qkv projection.  Position of row b*T+t is (pos_dev ? pos_dev[b] : start) + t.
+// Per-head q/k RMSNorm + NeoX RoPE + KV-cache write for the sm.rows rows of
+// the merged qkv projection, each at its sequence and position (SeqMap);
+// max_T bounds the rows of one sequence.
 void launch_qknorm_rope(const uint16_t* qkv, const uint16_t* q_norm, const uint16_t* k_norm,
                         const float* rope_cos, const float* rope_sin, uint16_t* q_out, uint16_t* k_cache,
-                        uint16_t* v_cache, int B, int T, int max_seq, const int32_t* pos_dev, int start,
-                        hipStream_t s);
+                        uint16_t* v_cache, const SeqMap& sm, int max_T, int max_seq, hipStream_t s);
 
 // MFMA tiled GEMM, out = X[M,K] * W[N,K]^T with the chosen epilogue.
 // Requires N % 128 == 0 (EPI_SILU: N = 2*ldo-columns, (N/2) % 64 == 0), K % 64 == 0.
@@ -92,9 +94,11 @@ void launch_rope_pair_permute(const uint16_t* w_qkv, const uint16_t* q_norm, con
 void launch_sample(const float* logits, int rows, int vocab, int64_t stride, const float* temperature,
                    const int32_t* top_k, const float* top_p, const float* uniform, int32_t* out, hipStream_t s);
 
-// Causal GQA flash attention over the cache for B x T queries at positions start..start+T-1.
+// Causal GQA flash attention over the cache for the rows of a multi-token
+// call: the rows of sequence s at positions start_s .. start_s + T_s - 1
+// (SeqMap); max_T bounds T_s.
 void launch_attn_prefill(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out,
-                         int B, int T, int start, int max_seq, hipStream_t s);
+                         const SeqMap& sm, int max_T, int max_seq, hipStream_t s);
 
 // Split-K decode attention for one new token per sequence, from the raw
 // merged projection qkv [B][4096]: per-head q/k RMSNorm + RoPE of the new
@@ -111,8 +115,10 @@ void launch_attn_decode(const uint16_t* qkv, const uint16_t* q_norm, const uint1
 // part is [rows][n_part] of (float value, int index).  seq_mode as below.
 // With seq_mode 2 and eos >= 0, rows whose input token in_ids[r] is eos
 // have finished: they emit eos and keep their length.
+// seq_mode 3: seq_lens[r] = start + rows of sequence r of *sm (packed prefill).
 void launch_argmax_partials(const void* part, int rows, int n_part, int32_t* out_idx, int32_t* seq_lens,
-                            int seq_mode, int seq_val, const int32_t* in_ids, int eos, hipStream_t s);
+                            int seq_mode, int seq_val, const int32_t* in_ids, int eos, hipStream_t s,
+                            const SeqMap* sm = nullptr);
 
 // Row argmax (lowest index on ties, first NaN wins).  seq_mode: 0 none,
 // 1 seq_lens[r] = seq_val, 2 seq_lens[r] += 1 (done after the argmax).

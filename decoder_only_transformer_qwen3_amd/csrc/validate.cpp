@@ -10,9 +10,15 @@ static inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static inline bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 WsLayout ws_layout(int32_t batch, int32_t n_tokens) {
+  if (batch < 1 || n_tokens < 1) return WsLayout{};
+  return ws_layout_rows(batch, (int64_t)batch * n_tokens, n_tokens == 1);
+}
+
+WsLayout ws_layout_rows(int32_t batch, int64_t rows, bool one_token) {
   WsLayout L{};
-  if (batch < 1 || n_tokens < 1) return L;
-  const size_t M = (size_t)batch * (size_t)n_tokens;
+  if (batch < 1 || rows < 1) return L;
+  const size_t M = (size_t)rows;
+  const int32_t n_tokens = one_token ? 1 : 2;  // only "one token per sequence" matters below
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -155,6 +161,24 @@ int check_sample_call(const float* logits, int32_t rows, int32_t vocab, int64_t 
   if (rows < 1 || vocab < 1 || row_stride < vocab) return Q3_ERR_SHAPE;
   if (!al4(logits) || !al4(temperature) || !al4(top_k) || !al4(top_p) || !al4(uniform) || !al4(out_idx))
     return Q3_ERR_ALIGN;
+  return Q3_OK;
+}
+
+int check_prefill_packed_call(const q3_model* m, const q3_kv* kv, int32_t n_seqs, int32_t n_tokens,
+                              const int32_t* ids, const int32_t* cu_seqlens, const int32_t* start_pos,
+                              int32_t max_seq_tokens, const float* last_logits, const int32_t* next_ids,
+                              const int32_t* seq_lens, const void* ws, size_t ws_bytes) {
+  if (!m || !kv || !ids || !cu_seqlens || !next_ids || !seq_lens || !ws) return Q3_ERR_NULL;
+  if (model_null(m) || !kv->k || !kv->v) return Q3_ERR_NULL;
+  if (kv->batch < 1 || kv->max_seq < 8 || kv->max_seq > Q3_MAX_POS || (kv->max_seq % 8) != 0) return Q3_ERR_SHAPE;
+  if (n_seqs < 1 || n_seqs > kv->batch || n_tokens < n_seqs || n_tokens > MAX_TOKENS) return Q3_ERR_SHAPE;
+  if (max_seq_tokens < 1 || max_seq_tokens > n_tokens) return Q3_ERR_SHAPE;
+  if (max_seq_tokens > kv->max_seq) return Q3_ERR_POSITION;
+  if (model_misaligned(m) || !al16(kv->k) || !al16(kv->v) || !al4(ids) || !al4(cu_seqlens) ||
+      (start_pos && !al4(start_pos)) || !al4(next_ids) || !al4(seq_lens) || (last_logits && !al16(last_logits)) ||
+      !al16(ws))
+    return Q3_ERR_ALIGN;
+  if (ws_bytes < ws_layout_rows(n_seqs, n_tokens, false).total) return Q3_ERR_WORKSPACE;
   return Q3_OK;
 }
 

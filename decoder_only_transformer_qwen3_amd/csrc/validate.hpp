@@ -22,6 +22,9 @@ struct WsLayout {
 
 // Byte offsets of every workspace region for `batch` x `n_tokens` (256-B aligned).
 WsLayout ws_layout(int32_t batch, int32_t n_tokens);
+// `rows` token rows over `batch` sequences (packed calls: rows = tokens of
+// all sequences); one_token: every sequence adds exactly one token (decode).
+WsLayout ws_layout_rows(int32_t batch, int64_t rows, bool one_token);
 
 // Workgroup tickets in the workspace: 64 column blocks + 8 per sequence.
 inline int ticket_count(int32_t batch) { return 64 + 8 * batch; }
@@ -48,6 +51,10 @@ int check_rope_convert_call(const void* w_qkv, const void* q_norm, const void* k
                             const void* q_norm_out, const void* k_norm_out);
 int check_sample_call(const float* logits, int32_t rows, int32_t vocab, int64_t row_stride, const float* temperature,
                       const int32_t* top_k, const float* top_p, const float* uniform, const int32_t* out_idx);
+int check_prefill_packed_call(const q3_model* m, const q3_kv* kv, int32_t n_seqs, int32_t n_tokens,
+                              const int32_t* ids, const int32_t* cu_seqlens, const int32_t* start_pos,
+                              int32_t max_seq_tokens, const float* last_logits, const int32_t* next_ids,
+                              const int32_t* seq_lens, const void* ws, size_t ws_bytes);
 int check_linear_call(const void* x, const void* w, const void* out, int32_t m, int32_t n, int32_t k, int32_t ldo,
                       int32_t epilogue);
 

@@ -171,6 +171,33 @@ int q3_prefill(const q3_model *m, const q3_kv *kv, int32_t batch, int32_t prompt
                const int32_t *ids, float *last_logits, int32_t *next_ids, int32_t *seq_lens,
                void *ws, size_t ws_bytes, void *stream);
 
+/* Prefill of packed, ragged sequences: n_seqs prompts of different
+ * lengths concatenated into n_tokens rows ("第 3 章" §3.1 feeds the
+ * engine's packed [tokens, C] layout with per-sequence positions and takes
+ * logits only at each sequence's last position, §4.1).  Sequence s owns
+ * rows cu_seqlens[s] .. cu_seqlens[s+1] - 1 and cache row s of kv; its
+ * tokens sit at positions p0 .. p0 + len - 1 with p0 = start_pos[s] (0
+ * when start_pos is NULL), so a call can also continue sequences whose
+ * cache already holds positions 0 .. p0 - 1 (chunked prefill).
+ *   ids         int32 [n_tokens];  cu_seqlens int32 [n_seqs + 1];
+ *   start_pos   int32 [n_seqs] or NULL  (all device).
+ *   max_seq_tokens  host bound on every sequence's length (sizes grids).
+ *   last_logits float32 [n_seqs, 151936] or NULL; next_ids int32 [n_seqs]
+ *               (greedy argmax); seq_lens int32 [n_seqs] set to p0 + len.
+ *   ws          q3_workspace_bytes_packed(n_seqs, n_tokens) bytes.
+ * The caller guarantees cu_seqlens[0] = 0, lengths >= 1 and <=
+ * max_seq_tokens, cu_seqlens[n_seqs] = n_tokens and p0 + len <= kv->max_seq;
+ * otherwise results are unspecified, with no out-of-range access.
+ * Errors: Q3_ERR_NULL, Q3_ERR_SHAPE (n_seqs outside 1 .. kv->batch,
+ * n_tokens < n_seqs, max_seq_tokens outside 1 .. n_tokens, cache shape),
+ * Q3_ERR_POSITION (max_seq_tokens > kv->max_seq), Q3_ERR_ALIGN,
+ * Q3_ERR_WORKSPACE, Q3_ERR_HIP. */
+size_t q3_workspace_bytes_packed(int32_t n_seqs, int32_t n_tokens);
+int q3_prefill_packed(const q3_model *m, const q3_kv *kv, int32_t n_seqs, int32_t n_tokens, const int32_t *ids,
+                      const int32_t *cu_seqlens, const int32_t *start_pos, int32_t max_seq_tokens,
+                      float *last_logits, int32_t *next_ids, int32_t *seq_lens, void *ws, size_t ws_bytes,
+                      void *stream);
+
 /* One greedy decode step for `batch` sequences ("古法手撕简易LLM推理器"
  * §prefill与predict, predict loop): sequence b feeds token in_ids[b] at
  * position seq_lens[b], appends its K/V at that cache row, attends to rows

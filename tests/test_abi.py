@@ -124,6 +124,24 @@ def test_prefill_decode_argmax_reject_bad_arguments(B):
                                                    dneed, stream=0, check=False)
     assert eos(B.VOCAB) == B.Q3_ERR_SHAPE and eos(-2) == B.Q3_ERR_SHAPE
     assert eos(151645, hint=257) == B.Q3_ERR_POSITION    # the decode-step checks come first
+    pneed = B.q3_workspace_bytes_packed(3, 200)
+    assert pneed > 0 and B.q3_workspace_bytes_packed(0, 5) == 0
+
+    def pk(**kw):
+        a = dict(n_seqs=3, n_tokens=200, ids=0x600000, cu=0x630000, start=None, mx=120, logits=None,
+                 nxt=0x610000, seq=0x620000, ws=0x700000, nb=pneed)
+        a.update(kw)
+        return B.q3_prefill_packed(m, kv, a["n_seqs"], a["n_tokens"], a["ids"], a["cu"], a["start"], a["mx"],
+                                   a["logits"], a["nxt"], a["seq"], a["ws"], a["nb"], stream=0, check=False)
+
+    assert pk(cu=None) == B.Q3_ERR_NULL
+    assert pk(n_seqs=5) == B.Q3_ERR_SHAPE              # more sequences than cache rows
+    assert pk(n_tokens=2) == B.Q3_ERR_SHAPE            # fewer tokens than sequences
+    assert pk(mx=201) == B.Q3_ERR_SHAPE                # a sequence longer than all the tokens
+    assert pk(n_tokens=300, mx=260, nb=B.q3_workspace_bytes_packed(3, 300)) == B.Q3_ERR_POSITION
+    assert pk(cu=0x630002) == B.Q3_ERR_ALIGN
+    assert pk(start=0x640001) == B.Q3_ERR_ALIGN
+    assert pk(nb=pneed - 1) == B.Q3_ERR_WORKSPACE
     assert B.q3_argmax(0x800000, 2, 10, 5, 0x900000, stream=0, check=False) == B.Q3_ERR_SHAPE
     lin = lambda *a: B.q3_linear(*a, stream=0, check=False)
     assert lin(None, 0x1000, 0x2000, 1, 128, 512, 128, 0) == B.Q3_ERR_NULL
