@@ -28,7 +28,9 @@
 // Softmax works in the log2 domain with the hardware exp2; the running max
 // is raised only when a score exceeds it by more than 8, so most tiles skip
 // the O rescale (p = 2^(s - m) stays below 256).  The causal mask is applied
-// only on tiles that reach past a wave's first query.
+// only on tiles that reach past a wave's first query.  Positions of the last
+// tile at or past the sequence's end are zeroed in LDS once, so masked
+// (p = 0) keys never meet garbage values in the V operand.
 //
 // MFMA lane layouts (32x32x16): A row l%32, B column l%32, k-slot (l/32, j);
 // C column l%32, rows 8*(i/4) + 4*(l/32) + (i%4).
@@ -126,6 +128,15 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's part of tile j landed
     __builtin_amdgcn_s_barrier();        // all of tile j is in LDS; stage (j+1)%2 is free
     if (j + 1 < n_kt) issue(j + 1);
+    if (j == n_kt - 1 && n_kt * FA_BK > kv_len) {  // zero the V positions past the end, once
+      uint16_t* vz = lds[j % FA_NS][1];
+      const int first = kv_len - j * FA_BK;
+      for (int e = tid; e < (FA_BK - first) * D; e += 256) {
+        const int p = first + e / D, d = e % D;
+        vz[(p >> 3) * (D * VBLK) + d * VBLK + (p & 7)] = 0;
+      }
+      __syncthreads();
+    }
     if (j >= wave_kt) continue;          // past this wave's causal range (wave-uniform)
 
     const uint16_t* ks = lds[j % FA_NS][0];
@@ -216,7 +227,6 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       auto vread = [&](int x) {
         return *reinterpret_cast<const u32x4*>(vb0 + 2 * (x >> 2) * (D * VBLK) + 32 * (x & 3) * VBLK);
       };
-      const int vvalid = kv_len - (j * FA_BK + 8 * lh);  // valid positions of this lane's first chunk
       u32x4 va[4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) va[x] = vread(x);
@@ -225,12 +235,6 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       for (int x = 0; x < 16; ++x) {
         const int st = x >> 2, db = x & 3;
         u32x4 a = va[x & 3];
-        if (v_tail) {  // positions at or past kv_len may hold anything: zero them
-          const int valid = vvalid - 16 * st;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            a[e] &= (2 * e + 1 < valid) ? 0xffffffffu : ((2 * e < valid) ? 0x0000ffffu : 0u);
-        }
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pb[st]), oacc[db], 0, 0, 0);
         if (x + 4 < 16) va[x & 3] = vread(x + 4);
         __builtin_amdgcn_sched_barrier(0);
