@@ -407,7 +407,13 @@ def main():
         t, k, p = args.sample.split(",")
         sample = (float(t), int(k), float(p))
     r = Runner(torch, B, dev, dm, batch, T, steps, args.eos_id, sample)
-    if args.kernel_only:  # (the cache is not prefilled: the kernels stream it all the same)
+    if args.kernel_only:
+        # no prefill ran: give the layer-0 cache the attention kernels read
+        # N(0, 1) values, as a prefill would leave there (all-zero keys would
+        # time a different, lower-power instruction stream)
+        gen = torch.Generator(device="cuda").manual_seed(5)
+        for c in (r.kv.k[0], r.kv.v[0]):
+            c.copy_(torch.randn(c.shape, device="cuda", generator=gen).to(torch.bfloat16))
         rl = dominant_kernel(torch, B, dev, dm, r, args.workload, args.kernel_iters, not args.no_graph)
         rl["source_sha256"] = kernel_source_digest(args.workload)
         print(json.dumps({"workload": args.workload, "roofline": rl}), flush=True)
