@@ -5,8 +5,9 @@ Shapes cover the one-layer workload (1 x 16 tokens), the skinny/tiled GEMM
 boundary (64 / 65 rows), several tiles with a ragged tail, a multi-token
 chunk at an offset into a filled cache, decode-shaped calls (one token) at
 small, capacity-edge and full sizes (batch 32 over 2048 cached positions,
-batch 4 over 32768), and the 8 x 4096 prefill shape (one sequence checked
-against the oracle).
+batch 4 over 32768, 65 rows on the tiled GEMMs), the last position the
+rotary table holds (40959), and the 8 x 4096 prefill shape (one sequence
+checked against the oracle).
 """
 import numpy as np
 import pytest
@@ -99,6 +100,9 @@ def run_layer_case(lib, layer0, rope, batch, T, start, max_seq, check_seqs=None,
     (5, 3, 13, 16),       # tiny chunk, several sequences, cache full afterwards
     (2, 11, 53, 72),      # unaligned chunk spanning three 8-position V blocks
     (1, 200, 0, 200),     # 128-position query tiles with a ragged last tile
+    (65, 1, 100, 128),    # 65 decode rows: the tiled GEMMs with one token per sequence
+    (1, 1, 40959, 40960), # decode at the last position of the rotary table
+    (1, 64, 40896, 40960),  # a prefill chunk ending at the position limit
 ])
 def test_layer_forward_parity(lib, layer0, rope, batch, T, start, max_seq):
     run_layer_case(lib, layer0, rope, batch, T, start, max_seq)
