@@ -26,7 +26,7 @@ constexpr int GEMV_MAX_ROWS = 8;
 struct Ws {
   float* resid;
   uint16_t *h, *qkv, *qr, *ao, *act, *fh;
-  float *part, *apart, *logits, *ssq;
+  float *part, *tpart, *apart, *logits, *ssq;
   int* tick;  // 64 column-block tickets, then batch * 8 attention tickets
   int n_tick;
   void* amax;
@@ -43,6 +43,7 @@ Ws carve_rows(void* base, int32_t batch, int64_t rows, bool one_token) {
   w.ao = reinterpret_cast<uint16_t*>(p + L.ao);
   w.act = reinterpret_cast<uint16_t*>(p + L.act);
   w.part = reinterpret_cast<float*>(p + L.part);
+  w.tpart = reinterpret_cast<float*>(p + L.tpart);
   w.apart = reinterpret_cast<float*>(p + L.apart);
   w.logits = reinterpret_cast<float*>(p + L.logits);
   w.amax = p + L.amax;
@@ -77,6 +78,13 @@ struct LayerCtx {
 inline const uint16_t* U(const void* p) { return static_cast<const uint16_t*>(p); }
 
 inline bool skinny_rows(int M) { return M <= q3v::SKINNY_MAX_ROWS; }
+
+// Tiled / persistent GEMM of the layer's rows, with the K split the
+// workspace was sized for.
+inline void tiled(const LayerCtx& c, const uint16_t* X, const void* W, void* out, int N, int K, int ldo, Epi epi) {
+  const int n_split = q3v::tiled_splits(c.M, N, K, epi == EPI_SILU);
+  launch_gemm_tiled(X, U(W), out, c.M, N, K, ldo, epi, c.s, n_split, c.ws.tpart);
+}
 
 // Partial sums of squares per residual row (see NSQ in common.hpp).
 inline int nsq_for(int M) { return M <= GEMV_MAX_ROWS ? NSQ : NSQ_BLK; }
@@ -138,7 +146,7 @@ void run_layer(const LayerCtx& c) {
     skinny_normed(c, w->w_qkv, c.ws.qkv, QKV_N, QKV_N, EPI_BF16);
   } else {
     launch_rmsnorm(c.resid, nullptr, 0, M, U(w->input_norm), c.ws.h, M, 1, 0, c.s);
-    launch_gemm_tiled(c.ws.h, U(w->w_qkv), c.ws.qkv, M, QKV_N, C, QKV_N, EPI_BF16, c.s);
+    tiled(c, c.ws.h, w->w_qkv, c.ws.qkv, QKV_N, C, QKV_N, EPI_BF16);
   }
   // q/k RMSNorm + RoPE, K/V into the cache, causal GQA attention
   if (c.T == 1) {
@@ -155,10 +163,10 @@ void run_layer(const LayerCtx& c) {
     skinny_normed(c, w->w_gate_up, c.ws.act, 2 * I, I, EPI_SILU);
     skinny_residual(c, c.ws.act, w->w_down, I, SPLIT_DOWN, c.gamma_next);
   } else {
-    launch_gemm_tiled(c.ws.ao, U(w->w_o), c.resid, M, C, QDIM, C, EPI_ADD_F32, c.s);
+    tiled(c, c.ws.ao, w->w_o, c.resid, C, QDIM, C, EPI_ADD_F32);
     launch_rmsnorm(c.resid, nullptr, 0, M, U(w->post_norm), c.ws.h, M, 1, 0, c.s);
-    launch_gemm_tiled(c.ws.h, U(w->w_gate_up), c.ws.act, M, 2 * I, C, I, EPI_SILU, c.s);
-    launch_gemm_tiled(c.ws.act, U(w->w_down), c.resid, M, C, I, C, EPI_ADD_F32, c.s);
+    tiled(c, c.ws.h, w->w_gate_up, c.ws.act, 2 * I, C, I, EPI_SILU);
+    tiled(c, c.ws.act, w->w_down, c.resid, C, I, C, EPI_ADD_F32);
   }
 }
 

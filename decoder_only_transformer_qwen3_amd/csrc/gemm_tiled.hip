@@ -35,15 +35,17 @@ constexpr int GM = 8;
 template <int EPI, int WN, int WM>
 __global__ __launch_bounds__(256, (WN * WM > 4) ? 1 : 2) void k_gemm_tiled(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ out, int M, int N, int K,
-    int ldo, int n_tiles, int m_tiles) {
+    int ldo, int n_tiles, int m_tiles, int n_split, float* __restrict__ part) {
   constexpr int BN = 64 * WN, BM = 64 * WM;
   constexpr int W_CHUNKS = BN * TB_K / 8 / 256;  // 16 B chunks per thread
   constexpr int X_CHUNKS = BM * TB_K / 8 / 256;
   __shared__ __attribute__((aligned(16))) uint16_t Ws[2][BN * T_LDS];
   __shared__ __attribute__((aligned(16))) uint16_t Xs[2][BM * T_LDS];
 
-  // ---- tile scheduling (XCD-contiguous, grouped)
-  const int nwg = gridDim.x, bid = blockIdx.x;
+  // ---- tile scheduling (XCD-contiguous, grouped); workgroup bid takes K
+  // split bid / tiles of tile bid % tiles
+  const int nwg = m_tiles * n_tiles;
+  const int split = blockIdx.x / nwg, bid = blockIdx.x - split * nwg;
   int logical = bid;
   if ((nwg & 7) == 0) logical = (bid & 7) * (nwg >> 3) + (bid >> 3);
   const int group_size = GM * n_tiles;
@@ -56,6 +58,7 @@ __global__ __launch_bounds__(256, (WN * WM > 4) ? 1 : 2) void k_gemm_tiled(
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lq = l & 31, lh = l >> 5;
   const int wn = w >> 1, wm = w & 1;
+  const int k_begin = split * (K / n_split);
 
   // ---- global load assignment
   const uint16_t* wsrc[W_CHUNKS];
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(256, (WN * WM > 4) ? 1 : 2) void k_gemm_tiled(
     } else {
       wrow = tile_n * BN + row;
     }
-    wsrc[i] = W + (size_t)wrow * K + kc;
+    wsrc[i] = W + (size_t)wrow * K + k_begin + kc;
     wlds[i] = row * T_LDS + kc;
   }
 #pragma unroll
@@ -85,7 +88,7 @@ __global__ __launch_bounds__(256, (WN * WM > 4) ? 1 : 2) void k_gemm_tiled(
     const int row = c >> 3, kc = (c & 7) * 8;
     int xrow = tile_m * BM + row;
     xrow = xrow < M ? xrow : M - 1;
-    xsrc[i] = X + (size_t)xrow * K + kc;
+    xsrc[i] = X + (size_t)xrow * K + k_begin + kc;
     xlds[i] = row * T_LDS + kc;
   }
 
@@ -108,7 +111,7 @@ __global__ __launch_bounds__(256, (WN * WM > 4) ? 1 : 2) void k_gemm_tiled(
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
-  const int nk = K / TB_K;
+  const int nk = K / TB_K / n_split;
   constexpr int NS = TB_K / 16;  // MFMA k-steps per K tile
   // operand registers, double-buffered across k-steps so the LDS reads of
   // step s+1 are in flight while step s's MFMAs issue
@@ -154,6 +157,32 @@ __global__ __launch_bounds__(256, (WN * WM > 4) ? 1 : 2) void k_gemm_tiled(
     }
     __syncthreads();
     if (more) read_ops(Ws[cur ^ 1], Xs[cur ^ 1], 0, 0);
+  }
+
+  if (n_split > 1) {
+    // K split: store this split's fp32 sums at [split][m][W row]; a reduce
+    // kernel adds the splits in order and applies the epilogue
+    float* pp = part + (size_t)split * M * N;
+#pragma unroll
+    for (int mb = 0; mb < WM; ++mb) {
+      const int m = tile_m * BM + wm * 32 * WM + mb * 32 + lq;
+      if (m >= M) continue;
+#pragma unroll
+      for (int nb = 0; nb < WN; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          int wrow;
+          if constexpr (EPI == EPI_SILU) {
+            const int idx = tile_n * (BN / 2) + wn * (16 * WN) + (nb % (WN / 2)) * 32 + 8 * g + 4 * lh;
+            wrow = (nb >= WN / 2) ? (N >> 1) + idx : idx;
+          } else {
+            wrow = tile_n * BN + wn * 32 * WN + nb * 32 + 8 * g + 4 * lh;
+          }
+          *reinterpret_cast<f32x4*>(pp + (size_t)m * N + wrow) =
+              f32x4{acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2], acc[nb][mb][4 * g + 3]};
+        }
+    }
+    return;
   }
 
   // ---- epilogue: lane holds features 8*(i/4) + 4*lh + (i%4) of token lq in each block
@@ -440,31 +469,72 @@ static void launch_persist(const uint16_t* X, const uint16_t* W, void* out, int 
                      m_tiles, per_xcd);
 }
 
+// Sum of the K splits in split order, then the epilogue: one thread per 4
+// output columns of one row.
+template <int EPI>
+__global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ part, int n_split, int M, int N,
+                                                      void* __restrict__ out, int ldo) {
+  const int cols = (EPI == EPI_SILU) ? N / 2 : N;
+  const int per_row = cols / 4;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= M * per_row) return;
+  const int m = e / per_row, n = 4 * (e - m * per_row);
+  const size_t stride = (size_t)M * N;
+  const float* p = part + (size_t)m * N + n;
+  f32x4 v = *reinterpret_cast<const f32x4*>(p);
+  for (int sp = 1; sp < n_split; ++sp) v += *reinterpret_cast<const f32x4*>(p + sp * stride);
+  if constexpr (EPI == EPI_SILU) {
+    const float* q = p + N / 2;
+    f32x4 u = *reinterpret_cast<const f32x4*>(q);
+    for (int sp = 1; sp < n_split; ++sp) u += *reinterpret_cast<const f32x4*>(q + sp * stride);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = v[i] / (1.0f + __expf(-v[i])) * u[i];
+  }
+  if constexpr (EPI == EPI_BF16 || EPI == EPI_SILU) {
+    u32x2 o;
+    o.x = pack_bf2(v[0], v[1]);
+    o.y = pack_bf2(v[2], v[3]);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + (size_t)m * ldo + n) = o;
+  } else if constexpr (EPI == EPI_F32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)m * ldo + n) = v;
+  } else {  // EPI_ADD_F32
+    f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)m * ldo + n);
+    *dst = *dst + v;
+  }
+}
+
 template <int EPI, int WN, int WM>
-static void launch_t(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo, hipStream_t s) {
+static void launch_t(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo, hipStream_t s,
+                     int n_split, float* part) {
   constexpr int BN = 64 * WN, BM = 64 * WM;
   const int m_tiles = (M + BM - 1) / BM;
   const int n_tiles = (EPI == EPI_SILU) ? (N / 2) / (BN / 2) : N / BN;
-  hipLaunchKernelGGL((k_gemm_tiled<EPI, WN, WM>), dim3(m_tiles * n_tiles), dim3(256), 0, s, X, W, out, M, N, K, ldo,
-                     n_tiles, m_tiles);
+  hipLaunchKernelGGL((k_gemm_tiled<EPI, WN, WM>), dim3(m_tiles * n_tiles * n_split), dim3(256), 0, s, X, W, out, M,
+                     N, K, ldo, n_tiles, m_tiles, n_split, part);
+  if (n_split > 1) {
+    const int per_row = ((EPI == EPI_SILU) ? N / 2 : N) / 4;
+    hipLaunchKernelGGL((k_split_reduce<EPI>), dim3((M * per_row + 255) / 256), dim3(256), 0, s, part, n_split, M, N,
+                       out, ldo);
+  }
 }
 
 template <int EPI>
-static void launch_e(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo, hipStream_t s) {
+static void launch_e(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo, hipStream_t s,
+                     int n_split, float* part) {
   // the 256 x 256 tile needs N % 256 == 0 and enough token tiles to fill the chip
   if (M >= 2048 && (N % 256) == 0)
     launch_persist<EPI>(X, W, out, M, N, K, ldo, s);
   else
-    launch_t<EPI, 2, 2>(X, W, out, M, N, K, ldo, s);
+    launch_t<EPI, 2, 2>(X, W, out, M, N, K, ldo, s, part ? n_split : 1, part);
 }
 
 void launch_gemm_tiled(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo, Epi epi,
-                       hipStream_t s) {
+                       hipStream_t s, int n_split, float* part) {
   switch (epi) {
-    case EPI_BF16: launch_e<EPI_BF16>(X, W, out, M, N, K, ldo, s); break;
-    case EPI_F32: launch_e<EPI_F32>(X, W, out, M, N, K, ldo, s); break;
-    case EPI_ADD_F32: launch_e<EPI_ADD_F32>(X, W, out, M, N, K, ldo, s); break;
-    case EPI_SILU: launch_e<EPI_SILU>(X, W, out, M, N, K, ldo, s); break;
+    case EPI_BF16: launch_e<EPI_BF16>(X, W, out, M, N, K, ldo, s, n_split, part); break;
+    case EPI_F32: launch_e<EPI_F32>(X, W, out, M, N, K, ldo, s, n_split, part); break;
+    case EPI_ADD_F32: launch_e<EPI_ADD_F32>(X, W, out, M, N, K, ldo, s, n_split, part); break;
+    case EPI_SILU: launch_e<EPI_SILU>(X, W, out, M, N, K, ldo, s, n_split, part); break;
     default: break;
   }
 }

@@ -16,7 +16,7 @@ constexpr int SKINNY_MAX_ROWS = 64;  // row counts up to this use the skinny GEM
 constexpr int64_t MAX_TOKENS = 1 << 22;
 
 struct WsLayout {
-  size_t resid, h, qkv, qr, ao, act, part, apart, logits, amax, fh, ssq, tick;
+  size_t resid, h, qkv, qr, ao, act, part, tpart, apart, logits, amax, fh, ssq, tick;
   size_t total;
 };
 
@@ -25,6 +25,40 @@ WsLayout ws_layout(int32_t batch, int32_t n_tokens);
 // `rows` token rows over `batch` sequences (packed calls: rows = tokens of
 // all sequences); one_token: every sequence adds exactly one token (decode).
 WsLayout ws_layout_rows(int32_t batch, int64_t rows, bool one_token);
+
+// Tiled-GEMM K splits for row counts between the skinny and the persistent
+// paths: a 128 x 128 output tile per workgroup leaves most of the chip idle
+// when there are few tiles (128 rows x 1024 features: 8 tiles), so the K
+// range is split until about 256 workgroups run, each with at least two
+// 64-wide K steps, at most 16 splits.  The splits' fp32 sums go to the
+// workspace and a second kernel adds them in split order.
+inline int64_t tiled_tiles(int64_t M, int N, bool silu) {
+  return ((M + 127) / 128) * (silu ? (N / 2) / 64 : N / 128);
+}
+inline int tiled_splits(int64_t M, int N, int K, bool silu) {
+  if (M <= SKINNY_MAX_ROWS || (M >= 2048 && N % 256 == 0)) return 1;  // skinny / persistent paths
+  const int64_t tiles = tiled_tiles(M, N, silu);
+  const int ksteps = K / 64;
+  int s = 1;
+  while (tiles * s < 256 && 2 * s <= 16 && ksteps % (2 * s) == 0 && ksteps / (2 * s) >= 2) s *= 2;
+  return s;
+}
+// Partial-sum bytes of one layer's four projections at `rows` rows (the largest).
+inline int64_t tiled_part_bytes(int64_t rows) {
+  int64_t b = 0;
+  const int64_t c[4][3] = {{Q3_QKV_ROWS, Q3_HIDDEN, 0},
+                           {Q3_HIDDEN, Q3_N_HEADS * Q3_HEAD_DIM, 0},
+                           {2 * Q3_INTER, Q3_HIDDEN, 1},
+                           {Q3_HIDDEN, Q3_INTER, 0}};
+  for (const auto& p : c) {
+    const int s = tiled_splits(rows, (int)p[0], (int)p[1], p[2] != 0);
+    if (s > 1) {
+      const int64_t t = (int64_t)s * rows * p[0] * 4;
+      b = t > b ? t : b;
+    }
+  }
+  return b;
+}
 
 // Workgroup tickets in the workspace: 64 column blocks + 8 per sequence.
 inline int ticket_count(int32_t batch) { return 64 + 8 * batch; }
