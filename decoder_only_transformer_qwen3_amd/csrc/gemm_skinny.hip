@@ -290,32 +290,46 @@ __global__ __launch_bounds__(256) void k_gemv_resid(const uint16_t* __restrict__
   u32x4 wv[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) wv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr + 512 * i));
-  float acc[MR];
-#pragma unroll
-  for (int m = 0; m < MR; ++m) acc[m] = 0.f;
+  // activation rows (rows past M re-read row M - 1 and are not stored), then
+  // the residual entries and the gain of column n: all loads are issued
+  // before the first is waited on, with no branch in between (a branch join
+  // would make the compiler drain the weight loads first)
+  u32x4 xv[MR][NCH];
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
-    if (m < M) {
-      const uint16_t* xr = X + (size_t)m * K + 8 * l;
+    const uint16_t* xr = X + (size_t)(m < M ? m : M - 1) * K + 8 * l;
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + 512 * i);
+    for (int i = 0; i < NCH; ++i) xv[m][i] = *reinterpret_cast<const u32x4*>(xr + 512 * i);
+  }
+  float rpre[MR];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[m] = dot2_bf16(wv[i][e], xv[e], acc[m]);
-      }
-    }
+  for (int m = 0; m < MR; ++m) rpre[m] = resid[(size_t)(m < M ? m : M - 1) * C + n];
+  const uint16_t* gp = gamma ? gamma : W;  // (any readable address when there is no gain)
+  float gpre = bf2f(gp[n]);
+  // keep these loads here (the compiler would otherwise sink them into the
+  // finishing lane's branch, after the reduction)
+#pragma unroll
+  for (int m = 0; m < MR; ++m) asm volatile("" : "+v"(rpre[m]));
+  asm volatile("" : "+v"(gpre));
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    acc[m] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[m] = dot2_bf16(wv[i][e], xv[m][i][e], acc[m]);
   }
 #pragma unroll
-  for (int m = 0; m < MR; ++m) acc[m] = wave_sum(acc[m]);
+  for (int m = 0; m < MR; ++m) acc[m] = wave_sum_dpp(acc[m]);
   if (l == 0) {
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
       if (m < M) {
-        float* rp = resid + (size_t)m * C + n;
-        const float r = *rp + acc[m];
-        *rp = r;
+        const float r = rpre[m] + acc[m];
+        resid[(size_t)m * C + n] = r;
         if (gamma) {
-          hg[(size_t)m * C + n] = (uint16_t)f2bf(r * bf2f(gamma[n]));
+          hg[(size_t)m * C + n] = (uint16_t)f2bf(r * gpre);
           rsq[w][m] = r * r;
         }
       }
