@@ -91,11 +91,12 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
     m = m < M ? m : M - 1;
     xp[nb] = X + (size_t)m * a.ldx + k_base;
   }
-  f32x4 acc[RB][NB];
+  // two accumulator sets (even / odd k-steps) halve the dependent MFMA chain
+  f32x4 acc[RB][NB], acc2[RB][NB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = acc2[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = kspan >> 5;  // 32-wide k-steps in this workgroup's range
   for (int s0 = w; s0 < nsteps; s0 += WV * U) {
@@ -116,10 +117,15 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          acc[rb][nb] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u][rb]), as_bf16x8(bx[u][nb]), acc[rb][nb], 0, 0, 0);
+        for (int nb = 0; nb < NB; ++nb) {
+          f32x4& c = (u & 1) ? acc2[rb][nb] : acc[rb][nb];
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u][rb]), as_bf16x8(bx[u][nb]), c, 0, 0, 0);
+        }
   }
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[rb][nb] += acc2[rb][nb];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -130,8 +136,7 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < SQV; ++i) ss += i < sqv ? (sq[i].x + sq[i].y) + (sq[i].z + sq[i].w) : 0.f;
-#pragma unroll
-    for (int o = 1; o < SG; o <<= 1) ss += __shfl_xor(ss, o, 64);
+    ss = group_sum_dpp<SG>(ss);
     if (t < 256 && (t % SG) == 0 && sm < NB * 16) rsc[sm] = 1.0f / sqrtf(ss * (1.0f / C) + EPS);
   }
   __syncthreads();
