@@ -99,6 +99,11 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
     for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = acc2[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = kspan >> 5;  // 32-wide k-steps in this workgroup's range
+  // k-step of load u: with an even U a wave takes adjacent pairs of 32-wide
+  // steps, so each weight row's 128-byte lines are read whole by one wave
+  auto kstep = [&](int s0, int u) {
+    return (U % 2 == 0) ? (s0 - w) + 2 * ((u >> 1) * WV + w) + (u & 1) : s0 + WV * u;
+  };
   for (int s0 = w; s0 < nsteps; s0 += WV * U) {
     u32x4 wa[U][RB];
     u32x4 bx[U][NB];
@@ -106,11 +111,11 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        wa[u][rb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp[rb] + (size_t)(s0 + WV * u) * 32));
+        wa[u][rb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp[rb] + (size_t)kstep(s0, u) * 32));
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) bx[u][nb] = *reinterpret_cast<const u32x4*>(xp[nb] + (size_t)(s0 + WV * u) * 32);
+      for (int nb = 0; nb < NB; ++nb) bx[u][nb] = *reinterpret_cast<const u32x4*>(xp[nb] + (size_t)kstep(s0, u) * 32);
     __builtin_amdgcn_sched_barrier(0);  // every load of the step is in flight before the first MFMA waits
 #pragma unroll
     for (int u = 0; u < U; ++u)
