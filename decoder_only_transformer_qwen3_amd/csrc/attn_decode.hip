@@ -117,6 +117,36 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_decode(const uint16_t*
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, col = l & 15, grp = l >> 4;
+  const size_t head_base = ((size_t)b * HKV + g) * max_seq * D;
+  const uint16_t* kbase = k_cache + head_base;
+  const uint16_t* vbase = v_cache + head_base;
+  // key of A row `col` in score chain `set`: 8*(col/4) + 4*set + col%4 (see the header)
+  const int krel0 = 8 * (col >> 2) + (col & 3);
+  // two tiles' registers per wave: while one tile is computed, the next is in flight
+  u32x4 kA[8], vA[8], kB[8], vB[8];
+#define Q3_DEC_LOAD_TILE_AT(TB, KR, VR, LK, LB)                                            \
+  {                                                                                        \
+    const int tb_ = (TB);                                                                  \
+    _Pragma("unroll") for (int set = 0; set < 2; ++set) {                                  \
+      int key = tb_ + krel0 + 4 * set;                                                     \
+      key = key < (LK) ? key : (LK);                                                       \
+      const uint16_t* kp = kbase + (size_t)key * D + 8 * grp;                              \
+      _Pragma("unroll") for (int st = 0; st < 4; ++st) KR[4 * set + st] =                  \
+          ld_kv<NT>(kp + 32 * st);                                                         \
+    }                                                                                      \
+    int pb_ = tb_ + 8 * grp;                                                               \
+    pb_ = pb_ < (LB) ? pb_ : (LB);                                                         \
+    const uint16_t* vp = vbase + (size_t)pb_ * D + col * VBLK;                             \
+    _Pragma("unroll") for (int db = 0; db < 8; ++db) VR[db] =                              \
+        ld_kv<NT>(vp + 16 * db * VBLK);                                                    \
+  }
+  // With one split the range starts at key 0, so a wave's first tile is known
+  // before the sequence's position is: load it now (clamped to the cache;
+  // keys past the position are masked and their values zeroed below), in
+  // parallel with the position load rather than after it.
+  const bool spec = n_split == 1;
+  if (spec) Q3_DEC_LOAD_TILE_AT(w * DT, kA, vA, max_seq - 1, (max_seq - 1) & ~7);
+
   const int p = pos_dev ? pos_dev[b] : start;
   int n = p + 1;
   n = n < max_seq ? n : max_seq;
@@ -128,35 +158,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_decode(const uint16_t*
   const int n_tile = k1 > k0 ? (k1 - k0 + DT - 1) / DT : 0;
   const int last_key = k1 - 1, last_blk = (k1 - 1) & ~7;
 
-  const size_t head_base = ((size_t)b * HKV + g) * max_seq * D;
-  const uint16_t* kbase = k_cache + head_base;
-  const uint16_t* vbase = v_cache + head_base;
-
-  // key of A row `col` in score chain `set`: 8*(col/4) + 4*set + col%4 (see the header)
-  const int krel0 = 8 * (col >> 2) + (col & 3);
-  // two tiles' registers per wave: while one tile is computed, the next is in flight
-  u32x4 kA[8], vA[8], kB[8], vB[8];
-#define Q3_DEC_LOAD_TILE(T, KR, VR)                                                        \
-  {                                                                                        \
-    const int tb_ = k0 + (T) * DT;                                                         \
-    _Pragma("unroll") for (int set = 0; set < 2; ++set) {                                  \
-      int key = tb_ + krel0 + 4 * set;                                                     \
-      key = key < last_key ? key : last_key;                                               \
-      const uint16_t* kp = kbase + (size_t)key * D + 8 * grp;                              \
-      _Pragma("unroll") for (int st = 0; st < 4; ++st) KR[4 * set + st] =                  \
-          ld_kv<NT>(kp + 32 * st);                                                         \
-    }                                                                                      \
-    int pb_ = tb_ + 8 * grp;                                                               \
-    pb_ = pb_ < last_blk ? pb_ : last_blk;                                                 \
-    const uint16_t* vp = vbase + (size_t)pb_ * D + col * VBLK;                             \
-    _Pragma("unroll") for (int db = 0; db < 8; ++db) VR[db] =                              \
-        ld_kv<NT>(vp + 16 * db * VBLK);                                                    \
-  }
+#define Q3_DEC_LOAD_TILE(T, KR, VR) Q3_DEC_LOAD_TILE_AT(k0 + (T) * DT, KR, VR, last_key, last_blk)
 
   // a wave's tiles are w, w + 4, w + 8, ...; loads past the last tile re-load
   // it (clamped), so every iteration issues the same number of loads
   auto clamp_tile = [&](int tt) { return tt < n_tile ? tt : n_tile - 1; };
-  if (n_tile > 0) Q3_DEC_LOAD_TILE(clamp_tile(w), kA, vA);
+  if (!spec && n_tile > 0) Q3_DEC_LOAD_TILE(clamp_tile(w), kA, vA);
 
   // ---- the new token: rows of the wave hold q(2g), q(2g+1), k(g), v(g); lane j dims 8j..8j+7
   {
@@ -281,6 +288,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_decode(const uint16_t*
     process(t + NW, kB, vB);
   }
 #undef Q3_DEC_LOAD_TILE
+#undef Q3_DEC_LOAD_TILE_AT
 
   // ---- combine the 4 waves: lane (grp, col < 2) holds dims 16*db + 4*grp + i of head col
   l_run += __shfl_xor(l_run, 16, 64);
