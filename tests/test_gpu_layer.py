@@ -101,6 +101,7 @@ def run_layer_case(lib, layer0, rope, batch, T, start, max_seq, check_seqs=None,
     (2, 11, 53, 72),      # unaligned chunk spanning three 8-position V blocks
     (1, 200, 0, 200),     # 128-position query tiles with a ragged last tile
     (65, 1, 100, 128),    # 65 decode rows: the tiled GEMMs with one token per sequence
+    (97, 2, 10, 16),      # 194 rows over 97 sequences: two row tiles, K split
     (1, 1, 40959, 40960), # decode at the last position of the rotary table
     (1, 64, 40896, 40960),  # a prefill chunk ending at the position limit
 ])
