@@ -46,8 +46,7 @@ constexpr int PART_STRIDE = D + 2;
 constexpr int DEC_SPLIT_CAP = 64;
 constexpr float DEC_RESCALE_SLACK = 8.0f;
 
-__device__ __forceinline__ void load_row8(const uint16_t* src, float (&f)[8]) {
-  const u32x4 w = *reinterpret_cast<const u32x4*>(src);
+__device__ __forceinline__ void unpack_row8(const u32x4 w, float (&f)[8]) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     f[2 * e] = bf_lo(w[e]);
@@ -56,17 +55,33 @@ __device__ __forceinline__ void load_row8(const uint16_t* src, float (&f)[8]) {
 }
 
 // RMSNorm of the head row spread over a 16-lane row (lane j holds dims
-// 8j..8j+7), gain, then NeoX RoPE with the table row of position p.
+// 8j..8j+7): the reciprocal RMS, then gain (gbits: dims 8j..8j+7) and NeoX
+// RoPE with the table entries of lane j's frequencies 8(j%8)..8(j%8)+7.
+__device__ __forceinline__ float row_rinv8(const float (&f)[8]);
+__device__ __forceinline__ void gain_rope8(float (&f)[8], float rinv, const u32x4 gbits, const f32x4 c0,
+                                           const f32x4 c1, const f32x4 s0, const f32x4 s1, int j);
+// The same from memory: gain row and table rows of position p.
 __device__ __forceinline__ void norm_rope8(float (&f)[8], const uint16_t* __restrict__ gamma,
                                            const float* __restrict__ cos_row, const float* __restrict__ sin_row,
                                            int j) {
+  const float rinv = row_rinv8(f);
+  const u32x4 gbits = *reinterpret_cast<const u32x4*>(gamma + 8 * j);
+  const int i0 = 8 * (j & 7);
+  gain_rope8(f, rinv, gbits, *reinterpret_cast<const f32x4*>(cos_row + i0),
+             *reinterpret_cast<const f32x4*>(cos_row + i0 + 4), *reinterpret_cast<const f32x4*>(sin_row + i0),
+             *reinterpret_cast<const f32x4*>(sin_row + i0 + 4), j);
+}
+__device__ __forceinline__ float row_rinv8(const float (&f)[8]) {
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
   ss = row16_sum(ss);
-  const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + EPS);
+  return 1.0f / sqrtf(ss * (1.0f / D) + EPS);
+}
+__device__ __forceinline__ void gain_rope8(float (&f)[8], float rinv, const u32x4 gbits, const f32x4 c0,
+                                           const f32x4 c1, const f32x4 s0, const f32x4 s1, int j) {
   float g[8];
-  load_row8(gamma + 8 * j, g);
+  unpack_row8(gbits, g);
   float o[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -74,11 +89,6 @@ __device__ __forceinline__ void norm_rope8(float (&f)[8], const uint16_t* __rest
     // partner dim (i + 64 for lanes 0..7, i - 64 for lanes 8..15): DPP row_ror:8
     o[e] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(f[e]), 0x128, 0xf, 0xf, false));
   }
-  const int i0 = 8 * (j & 7);
-  const f32x4 c0 = *reinterpret_cast<const f32x4*>(cos_row + i0);
-  const f32x4 c1 = *reinterpret_cast<const f32x4*>(cos_row + i0 + 4);
-  const f32x4 s0 = *reinterpret_cast<const f32x4*>(sin_row + i0);
-  const f32x4 s1 = *reinterpret_cast<const f32x4*>(sin_row + i0 + 4);
   const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
   const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
   const float sgn = j < 8 ? -1.0f : 1.0f;  // x_i c - x_{i+64} s  |  x_{i+64} c + x_i s
@@ -96,7 +106,7 @@ __device__ __forceinline__ u32x4 ld_kv(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
-template <bool NT, int NW>
+template <bool NT, int NW, bool ONE>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_decode(const uint16_t* __restrict__ qkv,
                                                         const uint16_t* __restrict__ q_norm,
                                                         const uint16_t* __restrict__ k_norm,
@@ -140,14 +150,36 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_decode(const uint16_t*
     _Pragma("unroll") for (int db = 0; db < 8; ++db) VR[db] =                              \
         ld_kv<NT>(vp + 16 * db * VBLK);                                                    \
   }
-  // With one split the range starts at key 0, so a wave's first tile is known
-  // before the sequence's position is: load it now (clamped to the cache;
-  // keys past the position are masked and their values zeroed below), in
-  // parallel with the position load rather than after it.
-  const bool spec = n_split == 1;
-  if (spec) Q3_DEC_LOAD_TILE_AT(w * DT, kA, vA, max_seq - 1, (max_seq - 1) & ~7);
-
+  // The new token's row (wave rows hold q(2g), q(2g+1), k(g), v(g); lane j
+  // dims 8j..8j+7), its gain and its rotary table entries.  With one split
+  // (ONE) the key range starts at 0, so a wave's first tile is known before
+  // the sequence's position is and is loaded in parallel with it (clamped
+  // to the cache; keys past the position are masked and their values
+  // zeroed below).  With caches that stay in the last-level cache (EARLY)
+  // the row and the gain are loaded before that tile (waiting for them then
+  // does not wait for the tile) and the table entries as soon as the
+  // position is known; otherwise they are loaded as the norm needs them,
+  // which was measured faster there, as was loading only one tile here.
+  constexpr bool EARLY = ONE && !NT;
+  u32x4 xin, gin;
+  f32x4 c0, c1, s0, s1;
+  if constexpr (EARLY) {
+    const int off = grp < 2 ? (2 * g + grp) * D : QDIM + (grp - 2) * HKV * D + g * D;
+    xin = *reinterpret_cast<const u32x4*>(qkv + (size_t)b * QKV_N + off + 8 * col);
+    gin = *reinterpret_cast<const u32x4*>((grp < 2 ? q_norm : k_norm) + 8 * col);
+  }
+  if constexpr (ONE) Q3_DEC_LOAD_TILE_AT(w * DT, kA, vA, max_seq - 1, (max_seq - 1) & ~7);
   const int p = pos_dev ? pos_dev[b] : start;
+  if constexpr (EARLY) {
+    const int pc = p < 0 ? 0 : (p >= MAXPOS ? MAXPOS - 1 : p);
+    const int i0 = 8 * (col & 7);
+    const float* cos_row = rope_cos + (size_t)pc * ROPE_HALF + i0;
+    const float* sin_row = rope_sin + (size_t)pc * ROPE_HALF + i0;
+    c0 = *reinterpret_cast<const f32x4*>(cos_row);
+    c1 = *reinterpret_cast<const f32x4*>(cos_row + 4);
+    s0 = *reinterpret_cast<const f32x4*>(sin_row);
+    s1 = *reinterpret_cast<const f32x4*>(sin_row + 4);
+  }
   int n = p + 1;
   n = n < max_seq ? n : max_seq;
   n = n > 0 ? n : 0;
@@ -160,23 +192,38 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_decode(const uint16_t*
 
 #define Q3_DEC_LOAD_TILE(T, KR, VR) Q3_DEC_LOAD_TILE_AT(k0 + (T) * DT, KR, VR, last_key, last_blk)
 
-  // a wave's tiles are w, w + 4, w + 8, ...; loads past the last tile re-load
-  // it (clamped), so every iteration issues the same number of loads
+  // a wave's tiles are w, w + NW, w + 2 NW, ...; loads past the last tile
+  // re-load it (clamped), so every iteration issues the same number of loads
   auto clamp_tile = [&](int tt) { return tt < n_tile ? tt : n_tile - 1; };
-  if (!spec && n_tile > 0) Q3_DEC_LOAD_TILE(clamp_tile(w), kA, vA);
+  if constexpr (!ONE) {
+    if (n_tile > 0) Q3_DEC_LOAD_TILE(clamp_tile(w), kA, vA);
+  }
 
-  // ---- the new token: rows of the wave hold q(2g), q(2g+1), k(g), v(g); lane j dims 8j..8j+7
+  // ---- the new token: q/k norm and rotation, v as is
   {
-    const int pc = p < 0 ? 0 : (p >= MAXPOS ? MAXPOS - 1 : p);
-    const uint16_t* row = qkv + (size_t)b * QKV_N +
-                          (grp < 2 ? (2 * g + grp) * D : (grp == 2 ? QDIM + g * D : QDIM + HKV * D + g * D));
     float f[8];
-    load_row8(row + 8 * col, f);
+    if constexpr (EARLY) {
+      unpack_row8(xin, f);
+    } else {
+      const uint16_t* row = qkv + (size_t)b * QKV_N +
+                            (grp < 2 ? (2 * g + grp) * D : (grp == 2 ? QDIM + g * D : QDIM + HKV * D + g * D));
+      unpack_row8(*reinterpret_cast<const u32x4*>(row + 8 * col), f);
+    }
     float r[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) r[e] = f[e];
-    norm_rope8(r, grp < 2 ? q_norm : k_norm, rope_cos + (size_t)pc * ROPE_HALF, rope_sin + (size_t)pc * ROPE_HALF,
-               col);
+    if constexpr (EARLY) {
+      gain_rope8(r, row_rinv8(r), gin, c0, c1, s0, s1, col);
+      // computed on every lane (the v rows discard it), which keeps the
+      // table loads out of a branch, where they would be issued only after
+      // the norm
+#pragma unroll
+      for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(r[e]));
+    } else {
+      const int pc = p < 0 ? 0 : (p >= MAXPOS ? MAXPOS - 1 : p);
+      norm_rope8(r, grp < 2 ? q_norm : k_norm, rope_cos + (size_t)pc * ROPE_HALF,
+                 rope_sin + (size_t)pc * ROPE_HALF, col);
+    }
     u32x4 pk;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -368,12 +415,18 @@ void launch_attn_decode(const uint16_t* qkv, const uint16_t* q_norm, const uint1
                         bool streaming, hipStream_t s) {
   // streaming: caches far larger than the last-level cache, 8-wave workgroups
   // with nontemporal loads; otherwise 4-wave workgroups with ordinary loads
-  if (streaming)
-    hipLaunchKernelGGL((k_attn_decode<true, 8>), dim3(n_split, HKV, B), dim3(512), 0, s, qkv, q_norm, k_norm,
-                       rope_cos, rope_sin, k_cache, v_cache, part, counters, out, max_seq, pos_dev, start, n_split);
-  else
-    hipLaunchKernelGGL((k_attn_decode<false, 4>), dim3(n_split, HKV, B), dim3(256), 0, s, qkv, q_norm, k_norm,
-                       rope_cos, rope_sin, k_cache, v_cache, part, counters, out, max_seq, pos_dev, start, n_split);
+  const dim3 grid(n_split, HKV, B);
+#define Q3_DEC_LAUNCH(NT_, NW_, ONE_)                                                                    \
+  hipLaunchKernelGGL((k_attn_decode<NT_, NW_, ONE_>), grid, dim3(64 * NW_), 0, s, qkv, q_norm, k_norm, rope_cos, \
+                     rope_sin, k_cache, v_cache, part, counters, out, max_seq, pos_dev, start, n_split)
+  if (streaming) {
+    if (n_split == 1) Q3_DEC_LAUNCH(true, 8, true);
+    else Q3_DEC_LAUNCH(true, 8, false);
+  } else {
+    if (n_split == 1) Q3_DEC_LAUNCH(false, 4, true);
+    else Q3_DEC_LAUNCH(false, 4, false);
+  }
+#undef Q3_DEC_LAUNCH
 }
 
 }  // namespace q3

@@ -149,6 +149,15 @@ def test_attention_decode_unaligned_positions(lib, rope):
     _decode_case(lib, rope, 6, 160, [7, 8, 31, 32, 33, 159])
 
 
+@pytest.mark.parametrize("batch,max_seq,positions", [
+    (1, 1024, [1000]),          # caches in the last-level cache, key range split 4 ways
+    (2, 600, [300, 517]),       # same, 3 splits, one sequence's range ending early
+])
+def test_attention_decode_cached_split(lib, rope, batch, max_seq, positions):
+    """Caches small enough to stay cached, with more than one key split."""
+    _decode_case(lib, rope, batch, max_seq, positions)
+
+
 def test_attention_decode_batch32_ctx2048(lib, rope):
     _decode_case(lib, rope, 32, 2176, [2048 + (i % 7) for i in range(32)], check_seqs=[0, 13, 31])
 
