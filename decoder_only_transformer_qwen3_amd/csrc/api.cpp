@@ -150,8 +150,13 @@ void run_layer(const LayerCtx& c) {
   }
   // q/k RMSNorm + RoPE, K/V into the cache, causal GQA attention
   if (c.T == 1) {
+    // decode of up to 8 rows whose attention leaves most CUs idle: the launch
+    // also reads the gate|up and down weights into the L2s that the skinny
+    // GEMM and the GEMV will read them through
+    const bool warm = M <= GEMV_MAX_ROWS && c.dec_splits * HKV * c.B <= 64;
     launch_attn_decode(c.ws.qkv, U(w->q_norm), U(w->k_norm), c.cos, c.sin, c.kl, c.vl, c.ws.apart, c.ws.tick + 64,
-                       c.ws.ao, c.B, c.max_seq, c.pos_dev, c.start, c.dec_splits, c.dec_stream, c.s);
+                       c.ws.ao, c.B, c.max_seq, c.pos_dev, c.start, c.dec_splits, c.dec_stream, c.s,
+                       warm ? w->w_gate_up : nullptr, warm ? w->w_down : nullptr);
   } else {
     launch_qknorm_rope(c.ws.qkv, U(w->q_norm), U(w->k_norm), c.cos, c.sin, c.ws.qr, c.kl, c.vl, c.sm, c.max_T,
                        c.max_seq, c.s);
