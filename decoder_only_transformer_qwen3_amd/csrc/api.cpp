@@ -71,6 +71,7 @@ struct LayerCtx {
   bool dec_stream;         // decode attention in its streaming configuration (T == 1 only)
   float* resid;
   const uint16_t* gamma_next;  // gain of the norm that follows this layer, or null
+  const void* w_qkv_next;      // the next layer's merged q|k|v weight, or null
   Ws ws;
   hipStream_t s;
 };
@@ -151,12 +152,14 @@ void run_layer(const LayerCtx& c) {
   // q/k RMSNorm + RoPE, K/V into the cache, causal GQA attention
   if (c.T == 1) {
     // decode of up to 8 rows whose attention leaves most CUs idle: the launch
-    // also reads the gate|up and down weights into the L2s that the skinny
-    // GEMM and the GEMV will read them through
+    // also reads the gate|up and down weights and the next layer's q|k|v
+    // weight into the L2s that the skinny GEMM and the GEMV will read them
+    // through (the last layer re-reads its own q|k|v: nothing useful follows)
     const bool warm = M <= GEMV_MAX_ROWS && c.dec_splits * HKV * c.B <= 64;
+    const void* next_qkv = c.w_qkv_next ? c.w_qkv_next : w->w_qkv;
     launch_attn_decode(c.ws.qkv, U(w->q_norm), U(w->k_norm), c.cos, c.sin, c.kl, c.vl, c.ws.apart, c.ws.tick + 64,
                        c.ws.ao, c.B, c.max_seq, c.pos_dev, c.start, c.dec_splits, c.dec_stream, c.s,
-                       warm ? w->w_gate_up : nullptr, warm ? w->w_down : nullptr);
+                       warm ? w->w_gate_up : nullptr, warm ? w->w_down : nullptr, warm ? next_qkv : nullptr);
   } else {
     launch_qknorm_rope(c.ws.qkv, U(w->q_norm), U(w->k_norm), c.cos, c.sin, c.ws.qr, c.kl, c.vl, c.sm, c.max_T,
                        c.max_seq, c.s);
@@ -294,6 +297,7 @@ int q3_layer_forward(const q3_layer_weights* w, const float* rope_cos, const flo
   c.dec_stream = q3v::decode_streaming(batch, start_pos + 1);
   c.resid = residual;
   c.gamma_next = nullptr;
+  c.w_qkv_next = nullptr;
   c.ws = carve(ws, batch, n_tokens);
   c.s = s;
   const int M = batch * n_tokens;
@@ -336,6 +340,7 @@ int q3_prefill(const q3_model* m, const q3_kv* kv, int32_t batch, int32_t prompt
     c.kl = layer_cache(kv->k, l, kv);
     c.vl = layer_cache(kv->v, l, kv);
     c.gamma_next = U(l + 1 < NL ? m->layer[l + 1].input_norm : m->final_norm);
+    c.w_qkv_next = l + 1 < NL ? m->layer[l + 1].w_qkv : nullptr;
     run_layer(c);
   }
   run_head(m, wsp, batch, prompt_len, last_logits ? last_logits : wsp.logits, next_ids, seq_lens, 1, prompt_len, s);
@@ -381,6 +386,7 @@ int q3_prefill_packed(const q3_model* m, const q3_kv* kv, int32_t n_seqs, int32_
     c.kl = layer_cache(kv->k, l, kv);
     c.vl = layer_cache(kv->v, l, kv);
     c.gamma_next = U(l + 1 < NL ? m->layer[l + 1].input_norm : m->final_norm);
+    c.w_qkv_next = l + 1 < NL ? m->layer[l + 1].w_qkv : nullptr;
     run_layer(c);
   }
   run_head(m, wsp, n_seqs, 0, last_logits ? last_logits : wsp.logits, next_ids, seq_lens, 3, 0, s, nullptr, -1,
@@ -420,6 +426,7 @@ int q3_decode_step_eos(const q3_model* m, const q3_kv* kv, int32_t batch, const 
     c.kl = layer_cache(kv->k, l, kv);
     c.vl = layer_cache(kv->v, l, kv);
     c.gamma_next = U(l + 1 < NL ? m->layer[l + 1].input_norm : m->final_norm);
+    c.w_qkv_next = l + 1 < NL ? m->layer[l + 1].w_qkv : nullptr;
     run_layer(c);
   }
   run_head(m, wsp, batch, 1, logits ? logits : wsp.logits, out_ids, seq_lens, 2, 0, s, in_ids, eos_id);
