@@ -71,6 +71,13 @@ struct LayerCtx {
   bool dec_stream;         // decode attention in its streaming configuration (T == 1 only)
   float* resid;
   const uint16_t* gamma_next;  // gain of the norm that follows this layer, or null
+  // Tiled path (65-2047 rows): a residual projection split over K may leave
+  // its fp32 split sums in ws.tpart for the RMSNorm that reads the residual
+  // next, which adds them (one kernel fewer).  defer_down: this layer's down
+  // projection may do so (a next layer follows); in_pending: the residual
+  // entering this layer still owes the previous layer's down split sums.
+  bool defer_down;
+  bool in_pending;
   const void* w_qkv_next;      // the next layer's merged q|k|v weight, or null
   Ws ws;
   hipStream_t s;
@@ -85,6 +92,15 @@ inline bool skinny_rows(int M) { return M <= q3v::SKINNY_MAX_ROWS; }
 inline void tiled(const LayerCtx& c, const uint16_t* X, const void* W, void* out, int N, int K, int ldo, Epi epi) {
   const int n_split = q3v::tiled_splits(c.M, N, K, epi == EPI_SILU);
   launch_gemm_tiled(X, U(W), out, c.M, N, K, ldo, epi, c.s, n_split, c.ws.tpart);
+}
+
+// Residual projection on the tiled path whose split sums (if K is split) are
+// left in ws.tpart for the next RMSNorm; returns the number of splits left
+// there (0: the residual is already complete).
+inline int tiled_resid_deferred(const LayerCtx& c, const uint16_t* X, const void* W, int K) {
+  const int n_split = q3v::tiled_splits(c.M, C, K, false);
+  launch_gemm_tiled(X, U(W), c.resid, c.M, C, K, C, EPI_ADD_F32, c.s, n_split, c.ws.tpart, n_split == 1);
+  return n_split > 1 ? n_split : 0;
 }
 
 // Partial sums of squares per residual row (see NSQ in common.hpp).
@@ -146,7 +162,9 @@ void run_layer(const LayerCtx& c) {
   if (skinny) {
     skinny_normed(c, w->w_qkv, c.ws.qkv, QKV_N, QKV_N, EPI_BF16);
   } else {
-    launch_rmsnorm(c.resid, nullptr, 0, M, U(w->input_norm), c.ws.h, M, 1, 0, c.s);
+    const int pend = c.in_pending ? q3v::tiled_splits(M, C, I, false) : 1;
+    launch_rmsnorm(c.resid, pend > 1 ? c.ws.tpart : nullptr, pend > 1 ? pend : 0, M, U(w->input_norm), c.ws.h, M,
+                   1, 0, c.s);
     tiled(c, c.ws.h, w->w_qkv, c.ws.qkv, QKV_N, C, QKV_N, EPI_BF16);
   }
   // q/k RMSNorm + RoPE, K/V into the cache, causal GQA attention
@@ -171,10 +189,13 @@ void run_layer(const LayerCtx& c) {
     skinny_normed(c, w->w_gate_up, c.ws.act, 2 * I, I, EPI_SILU);
     skinny_residual(c, c.ws.act, w->w_down, I, SPLIT_DOWN, c.gamma_next);
   } else {
-    tiled(c, c.ws.ao, w->w_o, c.resid, C, QDIM, C, EPI_ADD_F32);
-    launch_rmsnorm(c.resid, nullptr, 0, M, U(w->post_norm), c.ws.h, M, 1, 0, c.s);
+    const int po = tiled_resid_deferred(c, c.ws.ao, w->w_o, QDIM);
+    launch_rmsnorm(c.resid, po ? c.ws.tpart : nullptr, po, M, U(w->post_norm), c.ws.h, M, 1, 0, c.s);
     tiled(c, c.ws.h, w->w_gate_up, c.ws.act, 2 * I, C, I, EPI_SILU);
-    tiled(c, c.ws.act, w->w_down, c.resid, C, I, C, EPI_ADD_F32);
+    if (c.defer_down)
+      tiled_resid_deferred(c, c.ws.act, w->w_down, I);
+    else
+      tiled(c, c.ws.act, w->w_down, c.resid, C, I, C, EPI_ADD_F32);
   }
 }
 
@@ -298,6 +319,8 @@ int q3_layer_forward(const q3_layer_weights* w, const float* rope_cos, const flo
   c.resid = residual;
   c.gamma_next = nullptr;
   c.w_qkv_next = nullptr;
+  c.defer_down = false;
+  c.in_pending = false;
   c.ws = carve(ws, batch, n_tokens);
   c.s = s;
   const int M = batch * n_tokens;
@@ -340,6 +363,8 @@ int q3_prefill(const q3_model* m, const q3_kv* kv, int32_t batch, int32_t prompt
     c.kl = layer_cache(kv->k, l, kv);
     c.vl = layer_cache(kv->v, l, kv);
     c.gamma_next = U(l + 1 < NL ? m->layer[l + 1].input_norm : m->final_norm);
+    c.in_pending = l > 0;        // (only acted on where the previous layer deferred)
+    c.defer_down = l + 1 < NL;
     c.w_qkv_next = l + 1 < NL ? m->layer[l + 1].w_qkv : nullptr;
     run_layer(c);
   }
@@ -386,6 +411,8 @@ int q3_prefill_packed(const q3_model* m, const q3_kv* kv, int32_t n_seqs, int32_
     c.kl = layer_cache(kv->k, l, kv);
     c.vl = layer_cache(kv->v, l, kv);
     c.gamma_next = U(l + 1 < NL ? m->layer[l + 1].input_norm : m->final_norm);
+    c.in_pending = l > 0;        // (only acted on where the previous layer deferred)
+    c.defer_down = l + 1 < NL;
     c.w_qkv_next = l + 1 < NL ? m->layer[l + 1].w_qkv : nullptr;
     run_layer(c);
   }
@@ -426,6 +453,8 @@ int q3_decode_step_eos(const q3_model* m, const q3_kv* kv, int32_t batch, const 
     c.kl = layer_cache(kv->k, l, kv);
     c.vl = layer_cache(kv->v, l, kv);
     c.gamma_next = U(l + 1 < NL ? m->layer[l + 1].input_norm : m->final_norm);
+    c.in_pending = l > 0;        // (only acted on where the previous layer deferred)
+    c.defer_down = l + 1 < NL;
     c.w_qkv_next = l + 1 < NL ? m->layer[l + 1].w_qkv : nullptr;
     run_layer(c);
   }

@@ -128,13 +128,22 @@ __global__ __launch_bounds__(256) void k_rmsnorm(float* __restrict__ resid, cons
 #pragma unroll
   for (int j = 0; j < 4; ++j) v[j] = x[lane + 64 * j];
   if (n_part > 0) {
-    for (int p = 0; p < n_part; ++p) {
+    // the split sums in split order, then the residual: the same additions
+    // as the split-K reduce kernel's residual epilogue
+    f32x4 ps[4];
+    const f32x4* p0 = reinterpret_cast<const f32x4*>(part + row * C);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ps[j] = p0[lane + 64 * j];
+    for (int p = 1; p < n_part; ++p) {
       const f32x4* pp = reinterpret_cast<const f32x4*>(part + ((size_t)p * part_rows + row) * C);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] += pp[lane + 64 * j];
+      for (int j = 0; j < 4; ++j) ps[j] += pp[lane + 64 * j];
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x[lane + 64 * j] = v[j];
+    for (int j = 0; j < 4; ++j) {
+      v[j] = v[j] + ps[j];
+      x[lane + 64 * j] = v[j];
+    }
   }
   if (out == nullptr) return;
   float ss = 0.f;

@@ -505,13 +505,13 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ 
 
 template <int EPI, int WN, int WM>
 static void launch_t(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo, hipStream_t s,
-                     int n_split, float* part) {
+                     int n_split, float* part, bool reduce) {
   constexpr int BN = 64 * WN, BM = 64 * WM;
   const int m_tiles = (M + BM - 1) / BM;
   const int n_tiles = (EPI == EPI_SILU) ? (N / 2) / (BN / 2) : N / BN;
   hipLaunchKernelGGL((k_gemm_tiled<EPI, WN, WM>), dim3(m_tiles * n_tiles * n_split), dim3(256), 0, s, X, W, out, M,
                      N, K, ldo, n_tiles, m_tiles, n_split, part);
-  if (n_split > 1) {
+  if (n_split > 1 && reduce) {
     const int per_row = ((EPI == EPI_SILU) ? N / 2 : N) / 4;
     hipLaunchKernelGGL((k_split_reduce<EPI>), dim3((M * per_row + 255) / 256), dim3(256), 0, s, part, n_split, M, N,
                        out, ldo);
@@ -520,21 +520,21 @@ static void launch_t(const uint16_t* X, const uint16_t* W, void* out, int M, int
 
 template <int EPI>
 static void launch_e(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo, hipStream_t s,
-                     int n_split, float* part) {
+                     int n_split, float* part, bool reduce) {
   // the 256 x 256 tile needs N % 256 == 0 and enough token tiles to fill the chip
   if (M >= 2048 && (N % 256) == 0)
     launch_persist<EPI>(X, W, out, M, N, K, ldo, s);
   else
-    launch_t<EPI, 2, 2>(X, W, out, M, N, K, ldo, s, part ? n_split : 1, part);
+    launch_t<EPI, 2, 2>(X, W, out, M, N, K, ldo, s, part ? n_split : 1, part, reduce);
 }
 
 void launch_gemm_tiled(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo, Epi epi,
-                       hipStream_t s, int n_split, float* part) {
+                       hipStream_t s, int n_split, float* part, bool reduce) {
   switch (epi) {
-    case EPI_BF16: launch_e<EPI_BF16>(X, W, out, M, N, K, ldo, s, n_split, part); break;
-    case EPI_F32: launch_e<EPI_F32>(X, W, out, M, N, K, ldo, s, n_split, part); break;
-    case EPI_ADD_F32: launch_e<EPI_ADD_F32>(X, W, out, M, N, K, ldo, s, n_split, part); break;
-    case EPI_SILU: launch_e<EPI_SILU>(X, W, out, M, N, K, ldo, s, n_split, part); break;
+    case EPI_BF16: launch_e<EPI_BF16>(X, W, out, M, N, K, ldo, s, n_split, part, reduce); break;
+    case EPI_F32: launch_e<EPI_F32>(X, W, out, M, N, K, ldo, s, n_split, part, reduce); break;
+    case EPI_ADD_F32: launch_e<EPI_ADD_F32>(X, W, out, M, N, K, ldo, s, n_split, part, reduce); break;
+    case EPI_SILU: launch_e<EPI_SILU>(X, W, out, M, N, K, ldo, s, n_split, part, reduce); break;
     default: break;
   }
 }

@@ -49,9 +49,11 @@ void launch_qknorm_rope(const uint16_t* qkv, const uint16_t* q_norm, const uint1
 // Requires N % 128 == 0 (EPI_SILU: N = 2*ldo-columns, (N/2) % 64 == 0), K % 64 == 0.
 // n_split > 1 (128 x 128 tiles only; (K / 64) % n_split == 0) splits K:
 // part holds n_split * M * N fp32 partial sums, added in split order by a
-// second kernel that applies the epilogue.
+// second kernel that applies the epilogue.  reduce = false (EPI_ADD_F32
+// into a [M][1024] residual) leaves that sum to the RMSNorm that reads the
+// residual next (launch_rmsnorm with part / n_split).
 void launch_gemm_tiled(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo,
-                       Epi epi, hipStream_t s, int n_split = 1, float* part = nullptr);
+                       Epi epi, hipStream_t s, int n_split = 1, float* part = nullptr, bool reduce = true);
 
 // MFMA skinny GEMM for M <= 64 rows (weight streaming), split into n_split K ranges.
 // Requires N % 16 == 0 and (K / n_split) % 512 == 0; EPI_PARTIAL writes [n_split][M][N].
