@@ -65,6 +65,8 @@ _linear = _sig("q3_linear", ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
 _attn_prefill = _sig("q3_attention_prefill", ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp)
 _attn_decode = _sig("q3_attention_decode", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
                     _i32, _vp, _vp, _sz, _vp)
+_attn_decode_warm = _sig("q3_attention_decode_warm", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                         _vp, _i32, _vp, _vp, _sz, _vp, _vp, _vp, _vp)
 _rope_conv = _sig("q3_rope_interleaved_to_half", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp)
 _decode_eos = _sig("q3_decode_step_eos", ctypes.c_int, ctypes.POINTER(q3_model), ctypes.POINTER(q3_kv), _i32, _vp,
                      _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp)
@@ -77,7 +79,7 @@ Q3_EPI_STORE_BF16, Q3_EPI_STORE_F32, Q3_EPI_ADD_F32, Q3_EPI_SILU_GATE = 0, 1, 2,
 
 EXPORTS = ("q3_status_str", "q3_rope_table_host", "q3_workspace_bytes", "q3_layer_forward",
            "q3_prefill", "q3_decode_step", "q3_argmax", "q3_linear", "q3_attention_prefill",
-           "q3_attention_decode", "q3_rope_interleaved_to_half", "q3_decode_step_eos",
+           "q3_attention_decode", "q3_attention_decode_warm", "q3_rope_interleaved_to_half", "q3_decode_step_eos",
            "q3_sample", "q3_workspace_bytes_packed", "q3_prefill_packed")
 
 
@@ -187,6 +189,17 @@ def q3_attention_decode(qkv, q_norm, k_norm, rope_cos, rope_sin, k_layer, v_laye
                       _stream(stream))
     if check:
         _check(st, "q3_attention_decode")
+    return st
+
+
+def q3_attention_decode_warm(qkv, q_norm, k_norm, rope_cos, rope_sin, k_layer, v_layer, batch, max_seq, positions,
+                             max_len_hint, out, ws, ws_bytes, w_gate_up, w_down, w_qkv_next, stream=None,
+                             check=True) -> int:
+    st = _attn_decode_warm(_ptr(qkv), _ptr(q_norm), _ptr(k_norm), _ptr(rope_cos), _ptr(rope_sin), _ptr(k_layer),
+                           _ptr(v_layer), batch, max_seq, _ptr(positions), max_len_hint, _ptr(out), _ptr(ws),
+                           ws_bytes, _ptr(w_gate_up), _ptr(w_down), _ptr(w_qkv_next), _stream(stream))
+    if check:
+        _check(st, "q3_attention_decode_warm")
     return st
 
 

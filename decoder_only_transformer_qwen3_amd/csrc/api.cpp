@@ -491,21 +491,39 @@ int q3_attention_prefill(const void* q, const void* k_layer, const void* v_layer
   return launch_status();
 }
 
+int q3_attention_decode_warm(const void* qkv, const void* q_norm, const void* k_norm, const float* rope_cos,
+                             const float* rope_sin, void* k_layer, void* v_layer, int32_t batch, int32_t max_seq,
+                             const int32_t* positions, int32_t max_len_hint, void* out, void* ws, size_t ws_bytes,
+                             const void* w_gate_up, const void* w_down, const void* w_qkv_next, void* stream) {
+  int st = q3v::check_attn_decode_call(qkv, q_norm, k_norm, rope_cos, rope_sin, k_layer, v_layer, batch, max_seq,
+                                       positions, max_len_hint, out, ws, ws_bytes);
+  if (st != Q3_OK) return st;
+  const bool with_weights = w_gate_up || w_down || w_qkv_next;
+  if (with_weights) {
+    if (!w_gate_up || !w_down || !w_qkv_next) return Q3_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(w_gate_up) | reinterpret_cast<uintptr_t>(w_down) |
+         reinterpret_cast<uintptr_t>(w_qkv_next)) & 15)
+      return Q3_ERR_ALIGN;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const Ws w = carve(ws, batch, 1);
+  const int n_split = q3v::decode_splits(batch, max_len_hint);
+  const bool warm = with_weights && batch <= GEMV_MAX_ROWS && n_split * HKV * batch <= 64;
+  // the split merge's tickets start at zero (a single split takes none)
+  if (n_split > 1) launch_norm_operand(nullptr, 0, 1, 0, nullptr, nullptr, nullptr, NSQ, w.tick, w.n_tick, s);
+  launch_attn_decode(U(qkv), U(q_norm), U(k_norm), rope_cos, rope_sin, static_cast<uint16_t*>(k_layer),
+                     static_cast<uint16_t*>(v_layer), w.apart, w.tick + 64, static_cast<uint16_t*>(out), batch,
+                     max_seq, positions, 0, n_split, q3v::decode_streaming(batch, max_len_hint), s,
+                     warm ? w_gate_up : nullptr, warm ? w_down : nullptr, warm ? w_qkv_next : nullptr);
+  return launch_status();
+}
+
 int q3_attention_decode(const void* qkv, const void* q_norm, const void* k_norm, const float* rope_cos,
                         const float* rope_sin, void* k_layer, void* v_layer, int32_t batch, int32_t max_seq,
                         const int32_t* positions, int32_t max_len_hint, void* out, void* ws, size_t ws_bytes,
                         void* stream) {
-  const int st = q3v::check_attn_decode_call(qkv, q_norm, k_norm, rope_cos, rope_sin, k_layer, v_layer, batch,
-                                             max_seq, positions, max_len_hint, out, ws, ws_bytes);
-  if (st != Q3_OK) return st;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  const Ws w = carve(ws, batch, 1);
-  launch_norm_operand(nullptr, 0, 1, 0, nullptr, nullptr, nullptr, NSQ, w.tick, w.n_tick, s);  // zero the tickets
-  launch_attn_decode(U(qkv), U(q_norm), U(k_norm), rope_cos, rope_sin, static_cast<uint16_t*>(k_layer),
-                     static_cast<uint16_t*>(v_layer), w.apart, w.tick + 64, static_cast<uint16_t*>(out), batch,
-                     max_seq, positions, 0, q3v::decode_splits(batch, max_len_hint),
-                     q3v::decode_streaming(batch, max_len_hint), s);
-  return launch_status();
+  return q3_attention_decode_warm(qkv, q_norm, k_norm, rope_cos, rope_sin, k_layer, v_layer, batch, max_seq,
+                                  positions, max_len_hint, out, ws, ws_bytes, nullptr, nullptr, nullptr, stream);
 }
 
 int q3_argmax(const float* logits, int32_t rows, int32_t vocab, int64_t row_stride, int32_t* out_idx, void* stream) {

@@ -158,6 +158,41 @@ def test_attention_decode_cached_split(lib, rope, batch, max_seq, positions):
     _decode_case(lib, rope, batch, max_seq, positions)
 
 
+def test_attention_decode_warm_matches_plain(lib, rope):
+    """The entry point that also reads weights ahead into L2 (batch 1, one
+    split: the read-ahead workgroups run) gives the bits of the plain one,
+    output and written cache row alike, on two calls at different positions."""
+    B, dev = lib
+    max_seq, batch = 256, 1
+    kb, vb, _, _ = _caches(B, dev, batch, max_seq, 200, seed=61)
+    qkv = dev.to_device_bf16(I.normal_bf16(63, "warm_qkv", (batch, B.QKV_ROWS), std=1.0))
+    qn = dev.to_device_bf16(I.normal_bf16(64, "warm_qn", (B.HEAD_DIM,), std=0.02, mean=1.0))
+    kn = dev.to_device_bf16(I.normal_bf16(65, "warm_kn", (B.HEAD_DIM,), std=0.02, mean=1.0))
+    wgu = dev.to_device_bf16(I.normal_bf16(66, "warm_wgu", (2 * B.INTER, B.HIDDEN), std=0.02))
+    wdn = dev.to_device_bf16(I.normal_bf16(67, "warm_wdn", (B.HIDDEN, B.INTER), std=0.02))
+    wqk = dev.to_device_bf16(I.normal_bf16(68, "warm_wqk", (B.QKV_ROWS, B.HIDDEN), std=0.02))
+    ws, nb = dev.workspace(batch, 1)
+    for p in (160, 37):
+        log(f"[attn-decode-warm] batch={batch} p={p}")
+        outs, caches = [], []
+        for warm in (False, True):
+            kc = dev.to_device_bf16(kb)
+            vc = dev.to_device_bf16(v_dense_to_blocked(vb))
+            pos = torch.full((batch,), p, dtype=torch.int32, device="cuda")
+            out = torch.empty((batch, B.N_HEADS * B.HEAD_DIM), dtype=torch.bfloat16, device="cuda")
+            if warm:
+                B.q3_attention_decode_warm(qkv, qn, kn, rope[0], rope[1], kc, vc, batch, max_seq, pos, p + 1, out,
+                                           ws, nb, wgu, wdn, wqk)
+            else:
+                B.q3_attention_decode(qkv, qn, kn, rope[0], rope[1], kc, vc, batch, max_seq, pos, p + 1, out, ws, nb)
+            torch.cuda.synchronize()
+            outs.append(out.view(torch.int16).cpu().numpy())
+            caches.append((kc.view(torch.int16).cpu().numpy(), vc.view(torch.int16).cpu().numpy()))
+        np.testing.assert_array_equal(outs[0], outs[1])
+        np.testing.assert_array_equal(caches[0][0], caches[1][0])
+        np.testing.assert_array_equal(caches[0][1], caches[1][1])
+
+
 def test_attention_decode_batch32_ctx2048(lib, rope):
     _decode_case(lib, rope, 32, 2176, [2048 + (i % 7) for i in range(32)], check_seqs=[0, 13, 31])
 
