@@ -211,7 +211,7 @@ def dominant_kernel(torch, B, dev, dm, r, workload, iters, use_graph=True):
     """
     batch, T, steps, _ = WORKLOADS[workload]
     if workload == "prefill128_decode64":
-        # one launch per layer's weights in turn (28 x 27.3 MB read ahead, more
+        # one launch per layer's weights in turn (28 x 31.5 MB read ahead, more
         # than the 256 MB last-level cache), so they stream from HBM as in the step
         p = T + steps // 2
         qkv = torch.randn((batch, B.QKV_ROWS), device="cuda").to(torch.bfloat16)
@@ -227,14 +227,15 @@ def dominant_kernel(torch, B, dev, dm, r, workload, iters, use_graph=True):
             cursor[0] += 1
             lw, nxt = dm.layers[i], dm.layers[(i + 1) % nl]
             B.q3_attention_decode_warm(qkv, lw0.q_norm, lw0.k_norm, dm.rope_cos, dm.rope_sin, kl, vl, batch,
-                                       r.max_seq, pos, r.T + r.steps, out, r.ws_d, r.nb_d, lw.w_gate_up, lw.w_down,
-                                       nxt.w_qkv)
-        warm_bytes = (2 * B.INTER * B.HIDDEN + B.HIDDEN * B.INTER + B.QKV_ROWS * B.HIDDEN) * 2
+                                       r.max_seq, pos, r.T + r.steps, out, r.ws_d, r.nb_d, lw.w_o, lw.w_gate_up,
+                                       lw.w_down, nxt.w_qkv)
+        warm_bytes = (B.HIDDEN * B.N_HEADS * B.HEAD_DIM + 2 * B.INTER * B.HIDDEN + B.HIDDEN * B.INTER
+                      + B.QKV_ROWS * B.HIDDEN) * 2
         algo = float(batch * (p + 1) * 8 * 128 * 2 * 2 + batch * (B.QKV_ROWS + 2048) * 2 + warm_bytes)
         name, bound, per = (f"k_attn_decode + L2 read-ahead (batch {batch}, position {p}, one layer)", "hbm",
-                            "K and V bytes of positions 0..p + q|k|v in + out + the gate|up, down and next "
-                            "q|k|v weight bytes the launch reads ahead (the projections after it read them "
-                            "from L2)")
+                            "K and V bytes of positions 0..p + q|k|v in + out + the o_proj, gate|up, down and "
+                            "next q|k|v weight bytes the launch reads ahead (the projections after it read "
+                            "them from L2)")
         iters = max(iters, 280)
         reps = 28
     elif workload == "prefill_packed_ragged":

@@ -66,7 +66,7 @@ _attn_prefill = _sig("q3_attention_prefill", ctypes.c_int, _vp, _vp, _vp, _i32, 
 _attn_decode = _sig("q3_attention_decode", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
                     _i32, _vp, _vp, _sz, _vp)
 _attn_decode_warm = _sig("q3_attention_decode_warm", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
-                         _vp, _i32, _vp, _vp, _sz, _vp, _vp, _vp, _vp)
+                         _vp, _i32, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp)
 _rope_conv = _sig("q3_rope_interleaved_to_half", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp)
 _decode_eos = _sig("q3_decode_step_eos", ctypes.c_int, ctypes.POINTER(q3_model), ctypes.POINTER(q3_kv), _i32, _vp,
                      _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp)
@@ -193,11 +193,11 @@ def q3_attention_decode(qkv, q_norm, k_norm, rope_cos, rope_sin, k_layer, v_laye
 
 
 def q3_attention_decode_warm(qkv, q_norm, k_norm, rope_cos, rope_sin, k_layer, v_layer, batch, max_seq, positions,
-                             max_len_hint, out, ws, ws_bytes, w_gate_up, w_down, w_qkv_next, stream=None,
+                             max_len_hint, out, ws, ws_bytes, w_o, w_gate_up, w_down, w_qkv_next, stream=None,
                              check=True) -> int:
     st = _attn_decode_warm(_ptr(qkv), _ptr(q_norm), _ptr(k_norm), _ptr(rope_cos), _ptr(rope_sin), _ptr(k_layer),
                            _ptr(v_layer), batch, max_seq, _ptr(positions), max_len_hint, _ptr(out), _ptr(ws),
-                           ws_bytes, _ptr(w_gate_up), _ptr(w_down), _ptr(w_qkv_next), _stream(stream))
+                           ws_bytes, _ptr(w_o), _ptr(w_gate_up), _ptr(w_down), _ptr(w_qkv_next), _stream(stream))
     if check:
         _check(st, "q3_attention_decode_warm")
     return st

@@ -170,14 +170,15 @@ void run_layer(const LayerCtx& c) {
   // q/k RMSNorm + RoPE, K/V into the cache, causal GQA attention
   if (c.T == 1) {
     // decode of up to 8 rows whose attention leaves most CUs idle: the launch
-    // also reads the gate|up and down weights and the next layer's q|k|v
-    // weight into the L2s that the skinny GEMM and the GEMV will read them
-    // through (the last layer re-reads its own q|k|v: nothing useful follows)
+    // also reads the o_proj, gate|up and down weights and the next layer's
+    // q|k|v weight into the L2s that the skinny GEMM and the GEMV will read
+    // them through (the last layer re-reads its own q|k|v: nothing follows)
     const bool warm = M <= GEMV_MAX_ROWS && c.dec_splits * HKV * c.B <= 64;
     const void* next_qkv = c.w_qkv_next ? c.w_qkv_next : w->w_qkv;
     launch_attn_decode(c.ws.qkv, U(w->q_norm), U(w->k_norm), c.cos, c.sin, c.kl, c.vl, c.ws.apart, c.ws.tick + 64,
                        c.ws.ao, c.B, c.max_seq, c.pos_dev, c.start, c.dec_splits, c.dec_stream, c.s,
-                       warm ? w->w_gate_up : nullptr, warm ? w->w_down : nullptr, warm ? next_qkv : nullptr);
+                       warm ? w->w_o : nullptr, warm ? w->w_gate_up : nullptr, warm ? w->w_down : nullptr,
+                       warm ? next_qkv : nullptr);
   } else {
     launch_qknorm_rope(c.ws.qkv, U(w->q_norm), U(w->k_norm), c.cos, c.sin, c.ws.qr, c.kl, c.vl, c.sm, c.max_T,
                        c.max_seq, c.s);
@@ -494,15 +495,16 @@ int q3_attention_prefill(const void* q, const void* k_layer, const void* v_layer
 int q3_attention_decode_warm(const void* qkv, const void* q_norm, const void* k_norm, const float* rope_cos,
                              const float* rope_sin, void* k_layer, void* v_layer, int32_t batch, int32_t max_seq,
                              const int32_t* positions, int32_t max_len_hint, void* out, void* ws, size_t ws_bytes,
-                             const void* w_gate_up, const void* w_down, const void* w_qkv_next, void* stream) {
+                             const void* w_o, const void* w_gate_up, const void* w_down, const void* w_qkv_next,
+                             void* stream) {
   int st = q3v::check_attn_decode_call(qkv, q_norm, k_norm, rope_cos, rope_sin, k_layer, v_layer, batch, max_seq,
                                        positions, max_len_hint, out, ws, ws_bytes);
   if (st != Q3_OK) return st;
-  const bool with_weights = w_gate_up || w_down || w_qkv_next;
+  const bool with_weights = w_o || w_gate_up || w_down || w_qkv_next;
   if (with_weights) {
-    if (!w_gate_up || !w_down || !w_qkv_next) return Q3_ERR_NULL;
-    if ((reinterpret_cast<uintptr_t>(w_gate_up) | reinterpret_cast<uintptr_t>(w_down) |
-         reinterpret_cast<uintptr_t>(w_qkv_next)) & 15)
+    if (!w_o || !w_gate_up || !w_down || !w_qkv_next) return Q3_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(w_o) | reinterpret_cast<uintptr_t>(w_gate_up) |
+         reinterpret_cast<uintptr_t>(w_down) | reinterpret_cast<uintptr_t>(w_qkv_next)) & 15)
       return Q3_ERR_ALIGN;
   }
   const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -514,7 +516,8 @@ int q3_attention_decode_warm(const void* qkv, const void* q_norm, const void* k_
   launch_attn_decode(U(qkv), U(q_norm), U(k_norm), rope_cos, rope_sin, static_cast<uint16_t*>(k_layer),
                      static_cast<uint16_t*>(v_layer), w.apart, w.tick + 64, static_cast<uint16_t*>(out), batch,
                      max_seq, positions, 0, n_split, q3v::decode_streaming(batch, max_len_hint), s,
-                     warm ? w_gate_up : nullptr, warm ? w_down : nullptr, warm ? w_qkv_next : nullptr);
+                     warm ? w_o : nullptr, warm ? w_gate_up : nullptr, warm ? w_down : nullptr,
+                     warm ? w_qkv_next : nullptr);
   return launch_status();
 }
 
@@ -523,7 +526,8 @@ int q3_attention_decode(const void* qkv, const void* q_norm, const void* k_norm,
                         const int32_t* positions, int32_t max_len_hint, void* out, void* ws, size_t ws_bytes,
                         void* stream) {
   return q3_attention_decode_warm(qkv, q_norm, k_norm, rope_cos, rope_sin, k_layer, v_layer, batch, max_seq,
-                                  positions, max_len_hint, out, ws, ws_bytes, nullptr, nullptr, nullptr, stream);
+                                  positions, max_len_hint, out, ws, ws_bytes, nullptr, nullptr, nullptr, nullptr,
+                                  stream);
 }
 
 int q3_argmax(const float* logits, int32_t rows, int32_t vocab, int64_t row_stride, int32_t* out_idx, void* stream) {

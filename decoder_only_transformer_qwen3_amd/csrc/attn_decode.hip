@@ -113,37 +113,38 @@ __device__ __forceinline__ u32x4 ld_kv(const uint16_t* p) {
 // A decode step with a few sequences runs this kernel on a handful of CUs
 // while the rest of the chip idles, and the projections that follow are
 // latency bound on their weight reads.  Extra workgroups of this launch read
-// the gate|up and down weights, and the next layer's q|k|v weight, so that
-// each byte lands in the L2 of the XCD
+// the o_proj, gate|up and down weights, and the next layer's q|k|v weight,
+// so that each byte lands in the L2 of the XCD
 // whose workgroups will read it: workgroups are dispatched round-robin over
 // the 8 XCDs by linear id, in this launch as in the later ones, so consumer
 // workgroup i runs on XCD i % 8, and the warming workgroups of XCD x read
 // exactly the slices of the consumers i = x, x + 8, ...  Consumer slices
 // (the one-block skinny GEMM and the GEMV of up to 8 rows):
+//   o_proj  [1024][2048]: workgroup i (256) reads rows 4i..4i+3   (16 KB)
 //   gate|up [6144][1024]: workgroup i (384) reads gate rows 8i..8i+7 and
 //                         the matching up rows                    (2 x 16 KB)
 //   down    [1024][3072]: workgroup i (256) reads rows 4i..4i+3   (24 KB)
 //   q|k|v   [4096][1024]: workgroup i (256) reads rows 16i..16i+15 (32 KB)
 // in units of 4 KB (one 16-byte load per thread of a 256-thread group),
-// 3.25 MB per XCD: they stay in its 4 MB L2 until read (o_proj streams
-// 0.5 MB per XCD in between).  Warming the next q|k|v as well was measured
-// a further 2 % faster on the batch-1 decode step.
-// (Warming o_proj as well did not pay: that GEMV waits on the attention
-// output rather than on its weights.)
+// 3.75 MB per XCD, which stays in its 4 MB L2 until read.  On the batch-1
+// decode step the gate|up and down regions gave +2.6 %, the next q|k|v
+// +2.1 % more and o_proj +1.2 % more.
 constexpr int WARM_UG = ((2 * I) / 16 / 8) * 8;  // gate|up units per XCD
 constexpr int WARM_UD = (C / 4 / 8) * 6;         // down units per XCD
 constexpr int WARM_UQ = (QKV_N / 16 / 8) * 8;    // next layer's q|k|v units per XCD
-constexpr int WARM_UNITS = WARM_UG + WARM_UD + WARM_UQ;  // 832
+constexpr int WARM_UO = (C / 4 / 8) * 4;         // o_proj units per XCD
+constexpr int WARM_UNITS = WARM_UO + WARM_UG + WARM_UD + WARM_UQ;  // 960
 // Loads per thread, all in flight at once: fewer, fuller workgroups were
 // measured faster (24 loads: +1.1 % on the batch-1 decode step, 48: +2.6 %;
 // issuing them in two waits, or spreading them over more workgroups, lost).
 constexpr int WARM_LOADS = 48;
-constexpr int WARM_PER_XCD = (WARM_UNITS + WARM_LOADS - 1) / WARM_LOADS;  // 18 workgroups per XCD
+constexpr int WARM_PER_XCD = (WARM_UNITS + WARM_LOADS - 1) / WARM_LOADS;  // 20 workgroups per XCD
 static_assert(WARM_PER_XCD * WARM_LOADS >= WARM_UNITS, "every unit needs a load slot");
 
 // j: index of the warming workgroup (its linear id is congruent to j mod 8).
-__device__ __forceinline__ void warm_weights(const uint8_t* __restrict__ wgu, const uint8_t* __restrict__ wdown,
-                                             const uint8_t* __restrict__ wqkv, int j) {
+__device__ __forceinline__ void warm_weights(const uint8_t* __restrict__ wo, const uint8_t* __restrict__ wgu,
+                                             const uint8_t* __restrict__ wdown, const uint8_t* __restrict__ wqkv,
+                                             int j) {
   const int x = j & 7, r = j >> 3;  // XCD of this workgroup, its rank there
   const size_t t16 = (size_t)(threadIdx.x & 255) * 16;
   u32x4 v[WARM_LOADS];
@@ -152,7 +153,9 @@ __device__ __forceinline__ void warm_weights(const uint8_t* __restrict__ wgu, co
     int u = r * WARM_LOADS + q;  // a contiguous run of units
     u = u < WARM_UNITS ? u : r;  // no unit left: re-read the first one (keeps the loads branch-free)
     const uint8_t* a;
-    if (u < WARM_UG) {
+    if (u < WARM_UO) {
+      a = wo + (size_t)(x + 8 * (u >> 2)) * 16384 + (u & 3) * 4096;
+    } else if ((u -= WARM_UO) < WARM_UG) {  // (u counts from the gate|up region on)
       const int half = (u & 7) >> 2;
       a = wgu + (size_t)half * (I * C * 2) + (size_t)(x + 8 * (u >> 3)) * 16384 + (u & 3) * 4096;
     } else if (u < WARM_UG + WARM_UD) {
@@ -178,11 +181,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_decode(const uint16_t*
                                                         uint16_t* __restrict__ v_cache, float* __restrict__ part,
                                                         int* __restrict__ counters, uint16_t* __restrict__ out,
                                                         int max_seq, const int32_t* __restrict__ pos_dev, int start,
-                                                        int n_split, int n_seq, const uint8_t* __restrict__ warm_gu,
+                                                        int n_split, int n_seq, const uint8_t* __restrict__ warm_o,
+                                                        const uint8_t* __restrict__ warm_gu,
                                                         const uint8_t* __restrict__ warm_down,
                                                         const uint8_t* __restrict__ warm_qkv) {
   if ((int)blockIdx.z >= n_seq) {  // a warming workgroup (z-slices past the n_seq sequences)
-    warm_weights(warm_gu, warm_down, warm_qkv, blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * (blockIdx.z - n_seq)));
+    warm_weights(warm_o, warm_gu, warm_down, warm_qkv, blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * (blockIdx.z - n_seq)));
     return;
   }
   __shared__ __attribute__((aligned(16))) uint16_t qs[NW][2][D];  // per wave: rotated q of heads 2g, 2g+1
@@ -480,20 +484,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_decode(const uint16_t*
 void launch_attn_decode(const uint16_t* qkv, const uint16_t* q_norm, const uint16_t* k_norm, const float* rope_cos,
                         const float* rope_sin, uint16_t* k_cache, uint16_t* v_cache, float* part, int* counters,
                         uint16_t* out, int B, int max_seq, const int32_t* pos_dev, int start, int n_split,
-                        bool streaming, hipStream_t s, const void* warm_gate_up, const void* warm_down,
-                        const void* warm_qkv) {
+                        bool streaming, hipStream_t s, const void* warm_o, const void* warm_gate_up,
+                        const void* warm_down, const void* warm_qkv) {
   // streaming: caches far larger than the last-level cache, 8-wave workgroups
   // with nontemporal loads; otherwise 4-wave workgroups with ordinary loads
   // warming workgroups: whole z-slices of n_split * 8 after the B sequences
   // (so their linear ids keep j's residue modulo 8), 8 * WARM_PER_XCD or more
-  const bool warm = warm_gate_up && warm_down && warm_qkv;
+  const bool warm = warm_o && warm_gate_up && warm_down && warm_qkv;
   const int per_z = n_split * HKV;
   const int extra_z = warm ? (8 * WARM_PER_XCD + per_z - 1) / per_z : 0;
   const dim3 grid(n_split, HKV, B + extra_z);
 #define Q3_DEC_LAUNCH(NT_, NW_, ONE_)                                                                    \
   hipLaunchKernelGGL((k_attn_decode<NT_, NW_, ONE_>), grid, dim3(64 * NW_), 0, s, qkv, q_norm, k_norm, rope_cos, \
                      rope_sin, k_cache, v_cache, part, counters, out, max_seq, pos_dev, start, n_split, B, \
-                     static_cast<const uint8_t*>(warm_gate_up), static_cast<const uint8_t*>(warm_down), \
+                     static_cast<const uint8_t*>(warm_o), static_cast<const uint8_t*>(warm_gate_up),       \
+                     static_cast<const uint8_t*>(warm_down), \
                      static_cast<const uint8_t*>(warm_qkv))
   if (streaming) {
     if (n_split == 1) Q3_DEC_LAUNCH(true, 8, true);

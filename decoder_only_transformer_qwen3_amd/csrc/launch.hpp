@@ -111,16 +111,17 @@ void launch_attn_prefill(const uint16_t* q, const uint16_t* k_cache, const uint1
 // positions 0..p, and the log-sum-exp merge of the splits done by the last
 // workgroup of each (sequence, KV head) (counters: B*8 ints, zero on entry,
 // left zero).  out is [B][2048] bf16; part holds [B][16][n_split][130] f32.
-// warm_gate_up / warm_down / warm_qkv (all or none): the layer's gate|up
-// [6144][1024] and down [1024][3072] weights and the next layer's q|k|v
-// [4096][1024] weight, read ahead into the L2 caches that the one-block
-// skinny GEMM and the up-to-8-row GEMV will read them through (worth it only
-// when the attention itself occupies few CUs).
+// warm_o / warm_gate_up / warm_down / warm_qkv (all or none): the layer's
+// o_proj [1024][2048], gate|up [6144][1024] and down [1024][3072] weights and
+// the next layer's q|k|v [4096][1024] weight, read ahead into the L2 caches
+// that the one-block skinny GEMM and the up-to-8-row GEMV will read them
+// through (worth it only when the attention itself occupies few CUs).
 void launch_attn_decode(const uint16_t* qkv, const uint16_t* q_norm, const uint16_t* k_norm, const float* rope_cos,
                         const float* rope_sin, uint16_t* k_cache, uint16_t* v_cache, float* part, int* counters,
                         uint16_t* out, int B, int max_seq, const int32_t* pos_dev, int start, int n_split,
-                        bool streaming, hipStream_t s, const void* warm_gate_up = nullptr,
-                        const void* warm_down = nullptr, const void* warm_qkv = nullptr);
+                        bool streaming, hipStream_t s, const void* warm_o = nullptr,
+                        const void* warm_gate_up = nullptr, const void* warm_down = nullptr,
+                        const void* warm_qkv = nullptr);
 
 // Final greedy choice from the lm_head's per-block (max, argmax) partials:
 // part is [rows][n_part] of (float value, int index).  seq_mode as below.

@@ -333,19 +333,19 @@ int q3_attention_decode(const void *qkv, const void *q_norm, const void *k_norm,
 
 /* Helper: q3_attention_decode as q3_decode_step launches it for up to 8
  * sequences whose attention occupies at most 64 workgroups: the same
- * launch also reads the layer's gate|up weight (bf16 [6144][1024]), its
- * down weight (bf16 [1024][3072]) and the next layer's q|k|v weight (bf16
- * [4096][1024]) into the L2 caches of the XCDs whose workgroups read them in
- * the projections that follow.  The results are those of
+ * launch also reads the layer's o_proj weight (bf16 [1024][2048]), its
+ * gate|up weight (bf16 [6144][1024]), its down weight (bf16 [1024][3072])
+ * and the next layer's q|k|v weight (bf16 [4096][1024]) into the L2 caches
+ * of the XCDs whose workgroups read them in the projections that follow.  The results are those of
  * q3_attention_decode; only the time differs.  When the condition does not
- * hold the weights are ignored.  The three pointers are read only
+ * hold the weights are ignored.  The four pointers are read only
  * (ownership stays with the caller).
  * Errors: as q3_attention_decode, and Q3_ERR_NULL / Q3_ERR_ALIGN (16 B) for
  * the weights. */
 int q3_attention_decode_warm(const void *qkv, const void *q_norm, const void *k_norm, const float *rope_cos,
                              const float *rope_sin, void *k_layer, void *v_layer, int32_t batch, int32_t max_seq,
                              const int32_t *positions, int32_t max_len_hint, void *out, void *ws,
-                             size_t ws_bytes, const void *w_gate_up, const void *w_down,
+                             size_t ws_bytes, const void *w_o, const void *w_gate_up, const void *w_down,
                              const void *w_qkv_next, void *stream);
 
 /* Rotary-pairing conversion for weights trained with interleaved rotary

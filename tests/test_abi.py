@@ -242,15 +242,15 @@ def test_host_validation_under_sanitizers(tmp_path):
 
 
 def test_attention_decode_warm_rejects_partial_or_misaligned_weights(B):
-    """The read-ahead weights come as a set of three 16-byte-aligned pointers,
+    """The read-ahead weights come as a set of four 16-byte-aligned pointers,
     checked before any launch."""
     need = B.q3_workspace_bytes(1, 1)
     base = (0x10000, 0x11000, 0x12000, 0x13000, 0x14000, 0x20000, 0x30000, 1, 64, 0x40000, 8, 0x50000, 0x60000,
             need)
 
-    def call(gu, dn, qk):
-        return B.q3_attention_decode_warm(*base, gu, dn, qk, stream=0, check=False)
+    def call(wo, gu, dn, qk):
+        return B.q3_attention_decode_warm(*base, wo, gu, dn, qk, stream=0, check=False)
 
-    assert call(0x70000, None, 0x90000) == B.Q3_ERR_NULL
-    assert call(None, 0x80000, None) == B.Q3_ERR_NULL
-    assert call(0x70000, 0x80008, 0x90000) == B.Q3_ERR_ALIGN
+    assert call(0x68000, 0x70000, None, 0x90000) == B.Q3_ERR_NULL
+    assert call(None, None, 0x80000, None) == B.Q3_ERR_NULL
+    assert call(0x68000, 0x70000, 0x80008, 0x90000) == B.Q3_ERR_ALIGN

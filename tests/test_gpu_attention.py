@@ -168,6 +168,7 @@ def test_attention_decode_warm_matches_plain(lib, rope):
     qkv = dev.to_device_bf16(I.normal_bf16(63, "warm_qkv", (batch, B.QKV_ROWS), std=1.0))
     qn = dev.to_device_bf16(I.normal_bf16(64, "warm_qn", (B.HEAD_DIM,), std=0.02, mean=1.0))
     kn = dev.to_device_bf16(I.normal_bf16(65, "warm_kn", (B.HEAD_DIM,), std=0.02, mean=1.0))
+    wo = dev.to_device_bf16(I.normal_bf16(69, "warm_wo", (B.HIDDEN, B.N_HEADS * B.HEAD_DIM), std=0.02))
     wgu = dev.to_device_bf16(I.normal_bf16(66, "warm_wgu", (2 * B.INTER, B.HIDDEN), std=0.02))
     wdn = dev.to_device_bf16(I.normal_bf16(67, "warm_wdn", (B.HIDDEN, B.INTER), std=0.02))
     wqk = dev.to_device_bf16(I.normal_bf16(68, "warm_wqk", (B.QKV_ROWS, B.HIDDEN), std=0.02))
@@ -182,7 +183,7 @@ def test_attention_decode_warm_matches_plain(lib, rope):
             out = torch.empty((batch, B.N_HEADS * B.HEAD_DIM), dtype=torch.bfloat16, device="cuda")
             if warm:
                 B.q3_attention_decode_warm(qkv, qn, kn, rope[0], rope[1], kc, vc, batch, max_seq, pos, p + 1, out,
-                                           ws, nb, wgu, wdn, wqk)
+                                           ws, nb, wo, wgu, wdn, wqk)
             else:
                 B.q3_attention_decode(qkv, qn, kn, rope[0], rope[1], kc, vc, batch, max_seq, pos, p + 1, out, ws, nb)
             torch.cuda.synchronize()
