@@ -145,8 +145,9 @@ static_assert(WARM_PER_XCD * WARM_LOADS >= WARM_UNITS, "every unit needs a load 
 __device__ __forceinline__ void warm_weights(const uint8_t* __restrict__ wo, const uint8_t* __restrict__ wgu,
                                              const uint8_t* __restrict__ wdown, const uint8_t* __restrict__ wqkv,
                                              int j) {
+  if (threadIdx.x >= 256) return;  // 8-wave workgroups: four waves cover a unit
   const int x = j & 7, r = j >> 3;  // XCD of this workgroup, its rank there
-  const size_t t16 = (size_t)(threadIdx.x & 255) * 16;
+  const size_t t16 = (size_t)threadIdx.x * 16;
   u32x4 v[WARM_LOADS];
 #pragma unroll
   for (int q = 0; q < WARM_LOADS; ++q) {

@@ -158,13 +158,17 @@ def test_attention_decode_cached_split(lib, rope, batch, max_seq, positions):
     _decode_case(lib, rope, batch, max_seq, positions)
 
 
-def test_attention_decode_warm_matches_plain(lib, rope):
-    """The entry point that also reads weights ahead into L2 (batch 1, one
-    split: the read-ahead workgroups run) gives the bits of the plain one,
-    output and written cache row alike, on two calls at different positions."""
+@pytest.mark.parametrize("max_seq,positions", [
+    (256, (160, 37)),   # cached KV, one split, 4-wave workgroups
+    (4096, (4000,)),    # streaming KV, 8 splits, 8-wave workgroups
+])
+def test_attention_decode_warm_matches_plain(lib, rope, max_seq, positions):
+    """The entry point that also reads weights ahead into L2 (batch 1: the
+    read-ahead workgroups run) gives the bits of the plain one, output and
+    written cache row alike, on calls at different positions."""
     B, dev = lib
-    max_seq, batch = 256, 1
-    kb, vb, _, _ = _caches(B, dev, batch, max_seq, 200, seed=61)
+    batch = 1
+    kb, vb, _, _ = _caches(B, dev, batch, max_seq, max(positions) + 40 if max_seq > 256 else 200, seed=61)
     qkv = dev.to_device_bf16(I.normal_bf16(63, "warm_qkv", (batch, B.QKV_ROWS), std=1.0))
     qn = dev.to_device_bf16(I.normal_bf16(64, "warm_qn", (B.HEAD_DIM,), std=0.02, mean=1.0))
     kn = dev.to_device_bf16(I.normal_bf16(65, "warm_kn", (B.HEAD_DIM,), std=0.02, mean=1.0))
@@ -173,7 +177,7 @@ def test_attention_decode_warm_matches_plain(lib, rope):
     wdn = dev.to_device_bf16(I.normal_bf16(67, "warm_wdn", (B.HIDDEN, B.INTER), std=0.02))
     wqk = dev.to_device_bf16(I.normal_bf16(68, "warm_wqk", (B.QKV_ROWS, B.HIDDEN), std=0.02))
     ws, nb = dev.workspace(batch, 1)
-    for p in (160, 37):
+    for p in positions:
         log(f"[attn-decode-warm] batch={batch} p={p}")
         outs, caches = [], []
         for warm in (False, True):
