@@ -78,7 +78,7 @@ struct LayerCtx {
   // entering this layer still owes the previous layer's down split sums.
   bool defer_down;
   bool in_pending;
-  const void* w_qkv_next;      // the next layer's merged q|k|v weight, or null
+  const void* w_qkv_next;      // the q|k|v weight read next (layer l + 1, or layer 0 after the last), or null
   Ws ws;
   hipStream_t s;
 };
@@ -172,7 +172,8 @@ void run_layer(const LayerCtx& c) {
     // decode of up to 8 rows whose attention leaves most CUs idle: the launch
     // also reads the o_proj, gate|up and down weights and the next layer's
     // q|k|v weight into the L2s that the skinny GEMM and the GEMV will read
-    // them through (the last layer re-reads its own q|k|v: nothing follows)
+    // them through (after the last layer, layer 0's q|k|v, which the next
+    // decode step reads first; a single-layer call re-reads its own)
     const bool warm = M <= GEMV_MAX_ROWS && c.dec_splits * HKV * c.B <= 64;
     const void* next_qkv = c.w_qkv_next ? c.w_qkv_next : w->w_qkv;
     launch_attn_decode(c.ws.qkv, U(w->q_norm), U(w->k_norm), c.cos, c.sin, c.kl, c.vl, c.ws.apart, c.ws.tick + 64,
@@ -366,7 +367,7 @@ int q3_prefill(const q3_model* m, const q3_kv* kv, int32_t batch, int32_t prompt
     c.gamma_next = U(l + 1 < NL ? m->layer[l + 1].input_norm : m->final_norm);
     c.in_pending = l > 0;        // (only acted on where the previous layer deferred)
     c.defer_down = l + 1 < NL;
-    c.w_qkv_next = l + 1 < NL ? m->layer[l + 1].w_qkv : nullptr;
+    c.w_qkv_next = m->layer[(l + 1) % NL].w_qkv;  // after the last layer: the next step's first
     run_layer(c);
   }
   run_head(m, wsp, batch, prompt_len, last_logits ? last_logits : wsp.logits, next_ids, seq_lens, 1, prompt_len, s);
@@ -414,7 +415,7 @@ int q3_prefill_packed(const q3_model* m, const q3_kv* kv, int32_t n_seqs, int32_
     c.gamma_next = U(l + 1 < NL ? m->layer[l + 1].input_norm : m->final_norm);
     c.in_pending = l > 0;        // (only acted on where the previous layer deferred)
     c.defer_down = l + 1 < NL;
-    c.w_qkv_next = l + 1 < NL ? m->layer[l + 1].w_qkv : nullptr;
+    c.w_qkv_next = m->layer[(l + 1) % NL].w_qkv;  // after the last layer: the next step's first
     run_layer(c);
   }
   run_head(m, wsp, n_seqs, 0, last_logits ? last_logits : wsp.logits, next_ids, seq_lens, 3, 0, s, nullptr, -1,
@@ -456,7 +457,7 @@ int q3_decode_step_eos(const q3_model* m, const q3_kv* kv, int32_t batch, const 
     c.gamma_next = U(l + 1 < NL ? m->layer[l + 1].input_norm : m->final_norm);
     c.in_pending = l > 0;        // (only acted on where the previous layer deferred)
     c.defer_down = l + 1 < NL;
-    c.w_qkv_next = l + 1 < NL ? m->layer[l + 1].w_qkv : nullptr;
+    c.w_qkv_next = m->layer[(l + 1) % NL].w_qkv;  // after the last layer: the next step's first
     run_layer(c);
   }
   run_head(m, wsp, batch, 1, logits ? logits : wsp.logits, out_ids, seq_lens, 2, 0, s, in_ids, eos_id);
