@@ -58,8 +58,15 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                                                          uint16_t* __restrict__ out, SeqMap sm, int max_seq) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[FA_NS][2][FA_TILE];
 
-  const int qt = gridDim.x - 1 - blockIdx.x;  // longest (latest) tiles first
-  const int g = blockIdx.y, b = blockIdx.z;
+  // XCD-aware order: workgroups go round-robin to the 8 XCDs by linear id,
+  // so KV head g = id % 8 stays on one XCD, and that XCD walks its slots
+  // sequence by sequence, longest (latest) query tiles first: the query
+  // tiles of one (sequence, KV head) run together on one XCD and share its
+  // L2 for their K/V tiles.
+  static_assert(HKV == 8, "one KV head per XCD");
+  const int n_qt = gridDim.x / (HKV * sm.n);
+  const int g = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int b = slot / n_qt, qt = n_qt - 1 - (slot - b * n_qt);
   const int T = sm_len(sm, b), row0 = sm_row0(sm, b);
   int start = sm_start(sm, b);
   start = start < 0 ? 0 : start;
@@ -264,7 +271,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
 void launch_attn_prefill(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out,
                          const SeqMap& sm, int max_T, int max_seq, hipStream_t s) {
-  const dim3 grid((max_T + FA_BQ - 1) / FA_BQ, HKV, sm.n);
+  const dim3 grid(((max_T + FA_BQ - 1) / FA_BQ) * HKV * sm.n);
   hipLaunchKernelGGL(k_attn_prefill, grid, dim3(256), 0, s, q, k_cache, v_cache, out, sm, max_seq);
 }
 
