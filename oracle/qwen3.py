@@ -33,7 +33,7 @@ import numpy as np
 __all__ = [
     "Cfg", "QWEN3", "widen_bf16", "rmsnorm", "silu", "rope_inv_freq", "rope", "rope_interleaved", "apply_rope",
     "attention", "LayerW", "Model", "KVCache", "embed", "layer_forward",
-    "final_logits", "prefill", "decode_step", "argmax_lowest", "sample", "SAMPLE_MAX_CANDIDATES",
+    "final_logits", "prefill", "decode_step", "argmax_lowest", "sample",
     "generate_nocache", "generate_cached",
 ]
 
@@ -279,19 +279,17 @@ def argmax_lowest(logits: np.ndarray) -> np.ndarray:
     return np.argmax(np.atleast_2d(logits), axis=-1).astype(np.int64)
 
 
-SAMPLE_MAX_CANDIDATES = 4096
-
-
 def sample(logits: np.ndarray, temperature: float, top_k: int, top_p: float, u: float) -> int:
     """Temperature / top-k / top-p sampling of one logits row, the path
     "第 3 章" §4.3 (Sampler.sample) takes when temperatures are given; the
-    pages name its steps but print no body, so this is their plain reading:
+    pages name its steps but print no body, so this is their plain reading
+    over the whole vocabulary:
 
-    1. temperature <= 0 means greedy: argmax_lowest.
+    1. temperature <= 0 (or NaN) means greedy: argmax_lowest.
     2. z = logits / temperature.
-    3. Candidates: every token whose z is at least the k-th largest z
-       (k = top_k, or 4096 when top_k <= 0 or > 4096; at most the vocab),
-       in order of z descending, index ascending, at most 4096 of them.
+    3. Candidates: every token whose z is at least the k-th largest z, ties
+       included (k = top_k; top_k <= 0 or >= the vocabulary size means every
+       token), in order of z descending, index ascending.
     4. Softmax over the candidates; keep the shortest prefix of that order
        whose probability mass reaches top_p (top_p outside (0, 1] means 1).
     5. The token at the first position of the kept prefix whose cumulative
@@ -302,11 +300,10 @@ def sample(logits: np.ndarray, temperature: float, top_k: int, top_p: float, u: 
         return int(argmax_lowest(x)[0])
     z = x / temperature
     v = z.size
-    k = SAMPLE_MAX_CANDIDATES if (top_k <= 0 or top_k > SAMPLE_MAX_CANDIDATES) else top_k
-    k = min(k, v)
+    k = v if (top_k <= 0 or top_k >= v) else top_k
     order = np.lexsort((np.arange(v), -z))           # z descending, index ascending
     tau = z[order[k - 1]]
-    cand = order[z[order] >= tau][:SAMPLE_MAX_CANDIDATES]
+    cand = order[z[order] >= tau]
     e = np.exp(z[cand] - z[cand[0]])
     cum = np.cumsum(e)
     p = 1.0 if not (0.0 < top_p <= 1.0) else top_p

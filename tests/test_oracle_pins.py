@@ -369,11 +369,10 @@ def _sample_brute(x, temperature, top_k, top_p, u):
     if temperature <= 0:
         return max(range(len(x)), key=lambda i: (x[i], -i))
     z = [xi / temperature for xi in x]
-    k = 4096 if (top_k <= 0 or top_k > 4096) else top_k
-    k = min(k, len(z))
+    k = len(z) if (top_k <= 0 or top_k >= len(z)) else top_k
     srt = sorted(range(len(z)), key=lambda i: (-z[i], i))
     kth = z[srt[k - 1]]
-    cand = [i for i in srt if z[i] >= kth][:4096]
+    cand = [i for i in srt if z[i] >= kth]
     e = [math.exp(z[i] - z[cand[0]]) for i in cand]
     p = 1.0 if not (0.0 < top_p <= 1.0) else top_p
     total, run, cut = sum(e), 0.0, len(e) - 1
@@ -440,6 +439,71 @@ def test_sample_top_k_and_top_p_sets():
         assert np.sum(prob[:c + 1]) >= p and (c == 0 or np.sum(prob[:c]) < p)
         chosen = {O.sample(x, 1.0, 0, p, u) for u in us}
         assert chosen == set(np.argsort(-x)[:c + 1].tolist())
+
+
+def _sample_searchsorted(x, temperature, top_p, u):
+    """Full-vocabulary sampling with no top-k, by another route: scipy's
+    softmax over every token, a stable sort (index order among equal
+    probabilities), NumPy's cumulative sum and searchsorted."""
+    from scipy.special import softmax
+    prob = softmax(np.asarray(x, dtype=np.float64) / temperature)
+    order = np.argsort(-prob, kind="stable")
+    cum = np.cumsum(prob[order])
+    p = 1.0 if not (0.0 < top_p <= 1.0) else top_p
+    cut = int(np.searchsorted(cum, p * cum[-1], side="left"))
+    return int(order[int(np.searchsorted(cum[:cut + 1], u * cum[cut], side="right"))])
+
+
+def test_sample_full_vocabulary_matches_searchsorted_route():
+    """Rows of the whole 151,936-token vocabulary at the model's logit scale
+    (std 0.64) and wider: top-k off and top-p 1 (or a cut deep in the tail)
+    sample from every token, as the plain reading of "第 3 章" §4.3 says."""
+    rng = np.random.default_rng(45)
+    v = 151936
+    for scale, t, p in ((0.64, 1.0, 1.0), (0.64, 0.7, 0.99), (3.0, 1.0, 1.0), (1.0, 1.3, 0.8)):
+        x = rng.standard_normal(v) * scale
+        for u in (0.0, 0.013, 0.5, 0.77, 0.999):
+            for k in (0, v, v + 10):                # every form of "no top-k"
+                got = O.sample(x, t, k, p, u)
+                assert got == _sample_searchsorted(x, t, p, u), (scale, t, p, u, k)
+
+
+def test_sample_draws_reach_past_the_first_4096_candidates():
+    """A 20,000-token row whose tokens past rank 4096 carry a known mass:
+    over a grid of u the fraction of draws landing there equals that mass
+    (inverse-CDF property), so no candidate cap truncates the distribution."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(46)
+    x = rng.standard_normal(20000) * 0.64
+    prob = softmax(x)
+    tail = set(np.argsort(-x, kind="stable")[4096:].tolist())
+    tail_mass = float(np.sum(np.sort(prob)[::-1][4096:]))
+    assert tail_mass > 0.5
+    n = 1000
+    hits = sum(O.sample(x, 1.0, 0, 1.0, (i + 0.5) / n) in tail for i in range(n))
+    assert abs(hits / n - tail_mass) <= 1.5 / n
+
+
+def test_widen_bf16_bit_patterns():
+    """Hand-listed bfloat16 encodings (IEEE-754 binary32 with the low 16
+    bits dropped) through both widening routes (small arrays by shifting,
+    large arrays through torch)."""
+    cases = [(0x0000, 0.0), (0x8000, -0.0), (0x3F80, 1.0), (0xBF80, -1.0), (0x4049, 3.140625),
+             (0x0001, 2.0 ** -133), (0x007F, 127 * 2.0 ** -133), (0x0080, 2.0 ** -126),
+             (0x7F7F, (2 - 2.0 ** -7) * 2.0 ** 127), (0xFF7F, -(2 - 2.0 ** -7) * 2.0 ** 127),
+             (0x7F80, math.inf), (0xFF80, -math.inf), (0x3C00, 2.0 ** -7)]
+    bits = np.array([c[0] for c in cases], dtype=np.uint16)
+    want = np.array([c[1] for c in cases])
+    big = np.tile(bits, (1 << 20) // len(bits) + 1)
+    for got in (O.widen_bf16(bits), O.widen_bf16(big)[:len(bits)]):
+        assert got.dtype == np.float64
+        np.testing.assert_array_equal(got, want)
+        assert np.array_equal(np.signbit(got), np.signbit(want))
+    for nan_bits in (0x7FC0, 0xFFC1, 0x7F81):
+        arr = np.array([nan_bits], dtype=np.uint16)
+        assert np.isnan(O.widen_bf16(arr)[0])
+        assert np.isnan(O.widen_bf16(np.full(1 << 20, nan_bits, dtype=np.uint16))[0])
+    np.testing.assert_array_equal(O.widen_bf16(big), np.tile(want, (1 << 20) // len(bits) + 1))
 
 
 def test_causality_future_tokens_do_not_change_past():
