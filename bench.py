@@ -89,7 +89,9 @@ class Runner:
                            torch.full((batch,), k, dtype=torch.int32, device="cuda"),
                            torch.full((batch,), p, dtype=torch.float32, device="cuda"),
                            torch.rand((max(steps, 1), batch), generator=g, device="cuda"),
-                           torch.empty((batch, B.VOCAB), dtype=torch.float32, device="cuda"))
+                           torch.empty((batch, B.VOCAB), dtype=torch.float32, device="cuda"),
+                           torch.empty(B.q3_sample_workspace_bytes(batch, B.VOCAB), dtype=torch.uint8,
+                                       device="cuda"))
         self.batch, self.T, self.steps = batch, prompt_len, steps
         from decoder_only_transformer_qwen3_amd import inputs as I
         self.lens = None
@@ -134,10 +136,10 @@ class Runner:
         B = self.B
         for i in range(self.steps):
             if self.sample is not None:
-                temps, ks, ps, us, logits = self.sample
+                temps, ks, ps, us, logits, sws = self.sample
                 B.q3_decode_step(self.dm.struct, self.kv.struct, self.batch, self.nxt, self.seq,
                                  self.T + self.steps, logits, self.nxt, self.ws_d, self.nb_d)
-                B.q3_sample(logits, self.batch, B.VOCAB, B.VOCAB, temps, ks, ps, us[i], self.nxt)
+                B.q3_sample(logits, self.batch, B.VOCAB, B.VOCAB, temps, ks, ps, us[i], self.nxt, sws, sws.numel())
             elif self.eos_id is None:
                 B.q3_decode_step(self.dm.struct, self.kv.struct, self.batch, self.nxt, self.seq,
                                  self.T + self.steps, None, self.nxt, self.ws_d, self.nb_d)

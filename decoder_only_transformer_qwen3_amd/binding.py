@@ -70,7 +70,8 @@ _attn_decode_warm = _sig("q3_attention_decode_warm", ctypes.c_int, _vp, _vp, _vp
 _rope_conv = _sig("q3_rope_interleaved_to_half", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp)
 _decode_eos = _sig("q3_decode_step_eos", ctypes.c_int, ctypes.POINTER(q3_model), ctypes.POINTER(q3_kv), _i32, _vp,
                      _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp)
-_sample = _sig("q3_sample", ctypes.c_int, _vp, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp)
+_sample = _sig("q3_sample", ctypes.c_int, _vp, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
+_wsb_sample = _sig("q3_sample_workspace_bytes", _sz, _i32, _i32)
 _wsb_packed = _sig("q3_workspace_bytes_packed", _sz, _i32, _i32)
 _prefill_packed = _sig("q3_prefill_packed", ctypes.c_int, ctypes.POINTER(q3_model), ctypes.POINTER(q3_kv), _i32, _i32,
                        _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp)
@@ -80,7 +81,7 @@ Q3_EPI_STORE_BF16, Q3_EPI_STORE_F32, Q3_EPI_ADD_F32, Q3_EPI_SILU_GATE = 0, 1, 2,
 EXPORTS = ("q3_status_str", "q3_rope_table_host", "q3_workspace_bytes", "q3_layer_forward",
            "q3_prefill", "q3_decode_step", "q3_argmax", "q3_linear", "q3_attention_prefill",
            "q3_attention_decode", "q3_attention_decode_warm", "q3_rope_interleaved_to_half", "q3_decode_step_eos",
-           "q3_sample", "q3_workspace_bytes_packed", "q3_prefill_packed")
+           "q3_sample", "q3_sample_workspace_bytes", "q3_workspace_bytes_packed", "q3_prefill_packed")
 
 
 class Q3Error(RuntimeError):
@@ -221,10 +222,14 @@ def q3_decode_step_eos(m: q3_model, kv: q3_kv, batch, in_ids, seq_lens, max_len_
     return st
 
 
-def q3_sample(logits, rows, vocab, row_stride, temperature, top_k, top_p, uniform, out_idx, stream=None,
-              check=True) -> int:
+def q3_sample_workspace_bytes(rows: int, vocab: int) -> int:
+    return int(_wsb_sample(rows, vocab))
+
+
+def q3_sample(logits, rows, vocab, row_stride, temperature, top_k, top_p, uniform, out_idx, ws, ws_bytes,
+              stream=None, check=True) -> int:
     st = _sample(_ptr(logits), rows, vocab, row_stride, _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(uniform),
-                 _ptr(out_idx), _stream(stream))
+                 _ptr(out_idx), _ptr(ws), ws_bytes, _stream(stream))
     if check:
         _check(st, "q3_sample")
     return st

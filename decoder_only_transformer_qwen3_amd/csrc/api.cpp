@@ -548,11 +548,18 @@ int q3_rope_interleaved_to_half(const void* w_qkv, const void* q_norm, const voi
   return launch_status();
 }
 
+size_t q3_sample_workspace_bytes(int32_t rows, int32_t vocab) {
+  if (rows < 1 || rows > q3v::SAMPLE_MAX_ROWS || vocab < 1) return 0;
+  return q3v::sample_ws_layout(rows, vocab).total;
+}
+
 int q3_sample(const float* logits, int32_t rows, int32_t vocab, int64_t row_stride, const float* temperature,
-              const int32_t* top_k, const float* top_p, const float* uniform, int32_t* out_idx, void* stream) {
-  const int st = q3v::check_sample_call(logits, rows, vocab, row_stride, temperature, top_k, top_p, uniform, out_idx);
+              const int32_t* top_k, const float* top_p, const float* uniform, int32_t* out_idx, void* ws,
+              size_t ws_bytes, void* stream) {
+  const int st = q3v::check_sample_call(logits, rows, vocab, row_stride, temperature, top_k, top_p, uniform, out_idx,
+                                        ws, ws_bytes);
   if (st != Q3_OK) return st;
-  launch_sample(logits, rows, vocab, row_stride, temperature, top_k, top_p, uniform, out_idx,
+  launch_sample(logits, rows, vocab, row_stride, temperature, top_k, top_p, uniform, out_idx, ws,
                 static_cast<hipStream_t>(stream));
   return launch_status();
 }

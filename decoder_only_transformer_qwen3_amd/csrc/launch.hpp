@@ -94,10 +94,12 @@ void launch_gemm_skinny(const uint16_t* X, const uint16_t* W, void* out, int M, 
 void launch_rope_pair_permute(const uint16_t* w_qkv, const uint16_t* q_norm, const uint16_t* k_norm,
                               uint16_t* w_out, uint16_t* qn_out, uint16_t* kn_out, hipStream_t s);
 
-// Temperature / top-k / top-p sampling of `rows` logits rows (one
-// 1024-thread workgroup per row); per-row parameters and uniform draws.
+// Temperature / top-k / top-p sampling of `rows` logits rows over the whole
+// vocabulary (radix selects over the row in chunks, one workgroup per chunk);
+// per-row parameters and uniform draws; ws laid out by q3v::sample_ws_layout.
 void launch_sample(const float* logits, int rows, int vocab, int64_t stride, const float* temperature,
-                   const int32_t* top_k, const float* top_p, const float* uniform, int32_t* out, hipStream_t s);
+                   const int32_t* top_k, const float* top_p, const float* uniform, int32_t* out, void* ws,
+                   hipStream_t s);
 
 // Causal GQA flash attention over the cache for the rows of a multi-token
 // call: the rows of sequence s at positions start_s .. start_s + T_s - 1

@@ -1,362 +1,475 @@
-// Temperature / top-k / top-p sampling of logits rows, the path that
-// "第 3 章 前向与生成（代码走读）" §4.3 (Sampler.sample) takes when
-// temperatures are given (the greedy path is the lm_head's fused argmax).
-// Per row r, with T = temperature[r], k = top_k[r], p = top_p[r] and the
-// caller's uniform draw u = uniform[r] in [0, 1):
+// Temperature / top-k / top-p sampling of logits rows over the whole
+// vocabulary, the path that "第 3 章 前向与生成（代码走读）" §4.3
+// (Sampler.sample) takes when temperatures are given (the greedy path is the
+// lm_head's fused argmax).  Per row r, with T = temperature[r],
+// k = top_k[r], p = top_p[r] and the caller's uniform draw u = uniform[r]:
 //   T <= 0 (or NaN)  -> greedy: lowest index of the maximum;
 //   z = logits / T;
-//   candidates: every token with z >= the k-th largest z (k = 4096 when
-//     top_k <= 0 or > 4096; at most the vocabulary), ordered by z
-//     descending then index ascending, at most 4096 of them;
+//   candidates: every token with z >= the k-th largest z, ties included
+//     (k <= 0 or k >= vocab: every token), ordered by z descending then
+//     index ascending;
 //   softmax over the candidates, cumulative in that order; keep the
 //     shortest prefix whose mass reaches p (p outside (0, 1] means 1);
 //   pick the first kept position whose cumulative mass exceeds u times
 //     the kept mass.
 //
-// One 1024-thread workgroup per row:
-//   1. k-th largest z by radix select on the order-preserving 32-bit keys of
-//      z (four 8-bit digits, most significant first, LDS histograms of
-//      integer counts, so the result does not depend on thread timing;
-//      lanes of a wave that share a bin add to it with one atomic);
-//   2. the candidates gathered into LDS slots (their order is fixed by the
-//      sort; ties beyond the 4096 cap are cut in index order);
-// every pass over the row keeps 8 coalesced 16-byte loads per thread in flight;
-//   3. a bitonic sort of at most 4096 (key, index) pairs in LDS;
-//   4. exp, an in-order block scan of the masses, the top-p cut and the
-//      draw, all in float32.
+// No sort.  Every decision is a selection in the (z descending, index
+// ascending) order, found by radix select over order-preserving 32-bit keys
+// of z, most significant 8-bit digit first:
+//   - the k-th largest key, by element counts;
+//   - the top-p cut and the draw, by probability mass: masses are
+//     exp(z - z_max) in 40-bit fixed point (uint64), so every sum is exact
+//     integer arithmetic, independent of summation order, and a run is
+//     reproducible bit for bit;
+//   - inside the final key's group of equal values (equal masses) the
+//     position is a division, and the index is the j-th one with that key in
+//     index order.
+// Each row is split into G contiguous chunks, one 256-thread workgroup each.
+// A launch makes one pass over the row: every workgroup histograms its chunk
+// in LDS and writes the histogram to the workspace; the last workgroup of the
+// row (a ticket) adds the G histograms in chunk order and advances the row's
+// state.  Thirteen passes follow an initialising launch:
+//   0      row maximum (and the greedy answer) + first top-k digit
+//   1..3   top-k digits
+//   4..7   top-p digits (rows with p < 1)
+//   8..11  draw digits
+//   12     the j-th index among equal keys (only when j > 0)
+// A pass that does not apply to a row returns at once for that row.
 #include <math.h>
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "validate.hpp"
 
 namespace q3 {
 
-constexpr int SK_MAX = 4096;  // candidate cap
-constexpr int SK_T = 1024;    // threads per row
-constexpr int SK_E = 32;      // row values per thread and batch (8 x 16-byte loads in flight)
+constexpr int SP_T = 256;      // threads per workgroup (one per histogram bin)
+constexpr int SP_BINS = 256;   // 8-bit digits
+constexpr int SP_COPIES = 4;   // LDS histogram copies (lane % 4) against same-bin contention
+constexpr int SP_PAD = SP_BINS + 1;
+constexpr int SP_PASSES = 13;
+constexpr int SP_MAX_G = 32;   // chunks per row at most (q3v::sample_chunks)
+constexpr float SP_FIX = 1099511627776.0f;  // 2^40: mass fixed point
 
-// A batch of the row: thread t holds v[j] = x[base + 4 * (u * SK_T + t) + c]
-// for j = 4u + c (0 past the row end).  VEC: 16-byte loads (rows 16-byte
-// aligned); otherwise the same elements one by one.
-template <bool VEC>
-__device__ __forceinline__ void load_batch(const float* x, int vocab, int base, float (&v)[SK_E]) {
-#pragma unroll
-  for (int u = 0; u < SK_E / 4; ++u) {
-    const int i = base + 4 * (u * SK_T + (int)threadIdx.x);
-    if (VEC && i + 3 < vocab) {
-      const f32x4 q = *reinterpret_cast<const f32x4*>(x + i);
-      v[4 * u] = q.x;
-      v[4 * u + 1] = q.y;
-      v[4 * u + 2] = q.z;
-      v[4 * u + 3] = q.w;
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) v[4 * u + c] = i + c < vocab ? x[i + c] : 0.f;
-    }
-  }
-}
-__device__ __forceinline__ int batch_index(int base, int j) {
-  return base + 4 * ((j >> 2) * SK_T + (int)threadIdx.x) + (j & 3);
-}
+// Per-row state, written by the initialising launch and by each pass's
+// finishing workgroup, read by the next launch.
+struct alignas(64) SampRow {
+  float inv_t;        // 1 / T
+  float p, u;
+  int mode;           // 0: done (greedy rows after pass 0, or a result is final); 1: sampling
+  int topk;           // 1: a top-k threshold is selected (0 < k < vocab)
+  int topp;           // 1: a top-p cut is selected (p < 1)
+  uint32_t k;         // rank of the top-k threshold
+  float zmax;
+  uint32_t lo_key;    // candidates: key >= lo_key (top-k threshold, then top-p cut)
+  uint32_t prefix;    // digits selected so far by the running select
+  uint32_t tu_key;    // key of the drawn group (pass 12)
+  int32_t j;          // position of the drawn token among that key's tokens, in index order
+  uint64_t need;      // the running select's remaining count / mass to reach
+  uint64_t above;     // mass of the keys above the running select's prefix
+  uint64_t kept;      // kept mass (after the top-p cut, or all candidates)
+};
 
-// order-preserving map of float32 to uint32 (larger float -> larger key); NaN keys above +inf
-__device__ __forceinline__ uint32_t fkey(float f) {
+// order-preserving map of float32 to uint32 (larger float -> larger key);
+// -0 maps as +0.  NaN: nan_key.
+__device__ __forceinline__ uint32_t skey(float f, uint32_t nan_key) {
+  if (f != f) return nan_key;
+  if (f == 0.f) f = 0.f;
   const uint32_t b = __float_as_uint(f);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
-
-// hist[bin] += 1 for every lane with pred.  Keys of one row crowd into a
-// few bins of the leading digits, where plain LDS atomics would serialise:
-// up to four rounds count the lanes that share a leader's bin with one
-// ballot and add them with one atomic; lanes left after that add their own.
-__device__ __forceinline__ void hist_add(int* hist, bool pred, uint32_t bin) {
-  const int lane = threadIdx.x & 63;
-  bool done = !pred;
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const uint64_t rem = __ballot(!done);
-    if (rem == 0) return;
-    const int leader = __ffsll((unsigned long long)rem) - 1;
-    const uint32_t lb = __shfl(bin, leader, 64);
-    const bool same = !done && bin == lb;
-    const uint64_t group = __ballot(same);
-    if (lane == leader) atomicAdd(&hist[lb], __popcll(group));
-    done = done || same;
-  }
-  if (!done) atomicAdd(&hist[bin], 1);
+__device__ __forceinline__ float skey_inv(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+// fixed-point mass of z (0 for NaN or underflow)
+__device__ __forceinline__ uint64_t smass(float z, float zmax) {
+  const float w = expf(z - zmax);
+  return (w == w && w > 0.f) ? (uint64_t)(w * SP_FIX) : 0ull;
 }
 
-// exclusive scan of one int per thread over the workgroup; returns the total
-__device__ int block_excl_scan(int v, int* lds_warp, int& total) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int incl = v;
+struct SampWs {
+  SampRow* st;
+  int* tick;
+  uint32_t* cnt;   // [rows][G][256]
+  uint64_t* mass;  // [rows][G][256]
+  uint32_t* mini;  // [rows][G][256] lowest index per bin (last draw digit)
+  uint64_t* best;  // [rows][G] (key << 32 | ~index) maxima
+};
+
+__device__ __forceinline__ void st_dev_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev_u32(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev_u64(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// inclusive scan of one uint64 per thread over the 256 threads
+__device__ __forceinline__ uint64_t block_incl_scan_u64(uint64_t v, uint64_t* lds4) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
+    const uint64_t t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
   }
-  if (lane == 63) lds_warp[w] = incl;
+  if (lane == 63) lds4[w] = v;
   __syncthreads();
-  int base = 0, tot = 0;
-  for (int i = 0; i < SK_T / 64; ++i) {
-    const int c = lds_warp[i];
-    if (i < w) base += c;
-    tot += c;
-  }
+  uint64_t base = 0;
+  for (int i = 0; i < w; ++i) base += lds4[i];
   __syncthreads();
-  total = tot;
-  return base + incl - v;
+  return base + v;
 }
 
+__global__ __launch_bounds__(SP_T) void k_sample_init(int rows, int vocab, const float* __restrict__ temperature,
+                                                      const int32_t* __restrict__ top_k,
+                                                      const float* __restrict__ top_p,
+                                                      const float* __restrict__ uniform, SampWs ws) {
+  const int r = blockIdx.x * SP_T + threadIdx.x;
+  if (r >= rows) return;
+  SampRow s{};
+  const float t = temperature[r];
+  s.mode = t > 0.f ? 1 : 0;
+  s.inv_t = t > 0.f ? 1.0f / t : 1.0f;
+  const int k = top_k[r];
+  s.topk = (k > 0 && k < vocab) ? 1 : 0;
+  s.k = s.topk ? (uint32_t)k : 0u;
+  const float p = top_p[r];
+  s.p = (p > 0.f && p <= 1.f) ? p : 1.f;
+  s.topp = s.p < 1.f ? 1 : 0;
+  const float u = uniform[r];
+  s.u = u > 0.f ? (u < 1.f ? u : 0.99999994f) : 0.f;
+  s.lo_key = 0u;
+  ws.st[r] = s;
+  ws.tick[r] = 0;
+}
+
+// One pass (see the file comment) over chunk blockIdx.x of row blockIdx.y.
 template <bool VEC>
-__global__ __launch_bounds__(SK_T) void k_sample(const float* __restrict__ logits, int vocab, int64_t stride,
-                                                 const float* __restrict__ temperature,
-                                                 const int32_t* __restrict__ top_k, const float* __restrict__ top_p,
-                                                 const float* __restrict__ uniform, int32_t* __restrict__ out) {
-  __shared__ int hist[256];
-  __shared__ int scan_w[SK_T / 64];
-  __shared__ uint32_t ck[SK_MAX];  // candidate keys
-  __shared__ int ci[SK_MAX];       // candidate indices
-  __shared__ float cm[SK_MAX];     // cumulative masses
-  __shared__ uint32_t sel_prefix;
-  __shared__ int sel_rem, n_cand, cut, n_gt_s, n_eq_s;
-  __shared__ float red_v[SK_T / 64];
-  __shared__ int red_i[SK_T / 64];
+__global__ __launch_bounds__(SP_T) void k_sample_pass(int pass, const float* __restrict__ logits, int vocab,
+                                                      int64_t stride, int G, int chunk, SampWs ws,
+                                                      int32_t* __restrict__ out) {
+  __shared__ uint32_t h_cnt[SP_COPIES][SP_PAD];
+  __shared__ uint64_t h_mass[SP_COPIES][SP_PAD];
+  __shared__ uint32_t h_min[SP_COPIES][SP_PAD];
+  __shared__ uint64_t red[SP_T / 64];
+  __shared__ int is_last;
+  __shared__ int found;
 
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = blockIdx.y, g = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  SampRow s = ws.st[r];
+  // which select this pass runs (0: max, 1: top-k, 2: top-p, 3: draw, 4: tie index)
+  const int kind = pass == 0 ? 0 : pass <= 3 ? 1 : pass <= 7 ? 2 : pass <= 11 ? 3 : 4;
+  const bool greedy = pass == 0 && s.mode == 0;
+  if (!greedy) {
+    if (s.mode != 1) return;
+    if (kind == 1 && !s.topk) return;
+    if (kind == 2 && !s.topp) return;
+    if (kind == 4 && s.j <= 0) return;
+  }
+  // digit 3 is bits 31..24; pass 0 takes the first top-k digit
+  const int digit = kind == 0 ? 3 : kind == 1 ? 3 - pass : kind == 2 ? 7 - pass : kind == 3 ? 11 - pass : 0;
+  const int shift = 8 * digit;
+  const uint32_t hi_mask = digit == 3 ? 0u : ~((1u << (shift + 8)) - 1u);
+  const bool do_cnt = greedy ? false : (kind == 0 ? s.topk != 0 : kind != 4);
+  const bool do_mass = kind == 2 || kind == 3;
+  const bool do_min = kind == 3 && digit == 0;
+
   const float* x = logits + (size_t)r * stride;
-  const float T = temperature[r];
+  const int c0 = g * chunk, c1 = (c0 + chunk) < vocab ? (c0 + chunk) : vocab;
+  const float inv_t = greedy ? 1.0f : s.inv_t;
+  const uint32_t nan_key = greedy ? 0xffffffffu : 0u;
+  const uint32_t lo = kind == 2 ? s.lo_key : kind == 3 ? s.lo_key : 0u;
+  const uint32_t prefix = s.prefix;
+  const float zmax = s.zmax;
+  const int cp = lane & (SP_COPIES - 1);
 
-  if (!(T > 0.f)) {  // greedy: lowest index of the maximum (a NaN counts as the largest, the first NaN wins)
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int base = 0; base < vocab; base += SK_T * SK_E) {
-      float vv[SK_E];
-      load_batch<VEC>(x, vocab, base, vv);
-#pragma unroll
-      for (int j = 0; j < SK_E; ++j) {
-        const int i = batch_index(base, j);
-        const float v = vv[j];
-        const bool vn = v != v, bn = bv != bv;
-        if (i < vocab && ((vn && !bn) || (!vn && !bn && (v > bv || (v == bv && i < bi))) || (vn && bn && i < bi))) {
-          bv = v;
-          bi = i;
-        }
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      const bool on = ov != ov, bn = bv != bv;
-      if ((on && !bn) || (!on && !bn && (ov > bv || (ov == bv && oi < bi))) || (on && bn && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (lane == 0) {
-      red_v[w] = bv;
-      red_i[w] = bi;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      for (int i = 1; i < SK_T / 64; ++i) {
-        const float ov = red_v[i];
-        const int oi = red_i[i];
-        const bool on = ov != ov, bn = bv != bv;
-        if ((on && !bn) || (!on && !bn && (ov > bv || (ov == bv && oi < bi))) || (on && bn && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      out[r] = bi;
-    }
-    return;
+  for (int i = tid; i < SP_COPIES * SP_PAD; i += SP_T) {
+    (&h_cnt[0][0])[i] = 0u;
+    (&h_mass[0][0])[i] = 0ull;
+    (&h_min[0][0])[i] = 0xffffffffu;
   }
-
-  int k = top_k[r];
-  k = (k <= 0 || k > SK_MAX) ? SK_MAX : k;
-  k = k < vocab ? k : vocab;
-  float p = top_p[r];
-  p = (p > 0.f && p <= 1.f) ? p : 1.f;
-  float u = uniform[r];
-  u = u > 0.f ? (u < 1.f ? u : 0.99999994f) : 0.f;
-
-  // ---- 1. key of the k-th largest z: radix select, most significant digit first
-  if (tid == 0) {
-    sel_prefix = 0u;
-    sel_rem = k;
-  }
-  uint32_t mask = 0u;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += SK_T) hist[i] = 0;
-    __syncthreads();
-    const uint32_t prefix = sel_prefix;
-    for (int base = 0; base < vocab; base += SK_T * SK_E) {  // wave-uniform trip count: hist_add needs whole waves
-      float v[SK_E];
-      load_batch<VEC>(x, vocab, base, v);
-#pragma unroll
-      for (int j = 0; j < SK_E; ++j) {
-        const uint32_t key = fkey(v[j] / T);
-        hist_add(hist, batch_index(base, j) < vocab && (key & mask) == prefix, (key >> shift) & 255u);
-      }
-    }
-    __syncthreads();
-    if (tid == 0) {  // the bin, from the top, where the remaining rank falls
-      int rem = sel_rem, b = 255;
-      for (; b > 0; --b) {
-        if (hist[b] >= rem) break;
-        rem -= hist[b];
-      }
-      sel_rem = rem;
-      sel_prefix = prefix | ((uint32_t)b << shift);
-    }
-    mask |= 255u << shift;
-    __syncthreads();
-  }
-  const uint32_t kth = sel_prefix;
-
-  // ---- 2. candidates: keys above kth (fewer than k), then the ties (all of
-  // them when they fit under the cap; the sort below fixes the order, so the
-  // slots can be taken in any order).  When the ties overflow the cap, the
-  // lowest-index ones are kept: an ordered pass over contiguous chunks.
-  if (tid == 0) n_gt_s = 0;
   __syncthreads();
-  int my_eq = 0;
-  for (int base = 0; base < vocab; base += SK_T * SK_E) {
-    float v[SK_E];
-    load_batch<VEC>(x, vocab, base, v);
-#pragma unroll
-    for (int j = 0; j < SK_E; ++j) {
-      const int i = batch_index(base, j);
-      const uint32_t key = fkey(v[j] / T);
-      if (i < vocab && key > kth) {
-        const int slot = atomicAdd(&n_gt_s, 1);
-        ck[slot] = key;
-        ci[slot] = i;
-      } else if (i < vocab && key == kth) {
-        ++my_eq;
-      }
+
+  uint64_t best = 0;       // kind 0: max of (key << 32 | ~index)
+  uint32_t n_tie = 0;      // kind 4: elements equal to tu_key
+  auto visit = [&](float v, int i) {
+    const float z = v * inv_t;
+    const uint32_t key = skey(z, nan_key);
+    if (kind == 0) {
+      const uint64_t c = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)i;
+      best = c > best ? c : best;
+      if (do_cnt) atomicAdd(&h_cnt[cp][key >> 24], 1u);
+      return;
     }
-  }
-  int tot_eq;
-  block_excl_scan(my_eq, scan_w, tot_eq);  // (also orders the slot writes above before the reads below)
-  const int tot_gt = n_gt_s;
-  if (tid == 0) n_eq_s = tot_eq;
-  __syncthreads();
-  if (tot_gt + tot_eq <= SK_MAX) {
-    for (int base = 0; base < vocab; base += SK_T * SK_E) {
-      float v[SK_E];
-      load_batch<VEC>(x, vocab, base, v);
+    if (kind == 4) {
+      n_tie += key == s.tu_key;
+      return;
+    }
+    if (key < lo || (key & hi_mask) != prefix) return;
+    const uint32_t b = (key >> shift) & 255u;
+    atomicAdd(&h_cnt[cp][b], 1u);
+    if (do_mass) atomicAdd((unsigned long long*)&h_mass[cp][b], (unsigned long long)smass(z, zmax));
+    if (do_min) atomicMin(&h_min[cp][b], (uint32_t)i);
+  };
+  if (VEC) {
+    // c0 is a multiple of 4 and the row 16-byte aligned; 4 vectors per thread in flight
+    constexpr int U = 4;
+    int i = c0 + 4 * tid;
+    for (; i + 4 * SP_T * (U - 1) + 3 < c1; i += 4 * SP_T * U) {
+      f32x4 q[U];
 #pragma unroll
-      for (int j = 0; j < SK_E; ++j) {
-        const int i = batch_index(base, j);
-        if (i < vocab && fkey(v[j] / T) == kth) {
-          const int slot = tot_gt + atomicAdd(&n_eq_s, -1) - 1;  // counts down from tot_eq
-          ck[slot] = kth;
-          ci[slot] = i;
-        }
+      for (int u = 0; u < U; ++u) q[u] = *reinterpret_cast<const f32x4*>(x + i + 4 * SP_T * u);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) visit(q[u][c], i + 4 * SP_T * u + c);
+    }
+    for (; i < c1; i += 4 * SP_T) {
+      if (i + 3 < c1) {
+        const f32x4 q = *reinterpret_cast<const f32x4*>(x + i);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) visit(q[c], i + c);
+      } else {
+        for (int c = 0; c < 4 && i + c < c1; ++c) visit(x[i + c], i + c);
       }
     }
   } else {
-    const int chunk = (vocab + SK_T - 1) / SK_T;
-    const int c0 = tid * chunk, c1 = (c0 + chunk) < vocab ? (c0 + chunk) : vocab;
-    int n_eq = 0;
-    for (int i = c0; i < c1; ++i) n_eq += fkey(x[i] / T) == kth;
-    int unused;
-    int pos = tot_gt + block_excl_scan(n_eq, scan_w, unused);
-    for (int i = c0; i < c1 && pos < SK_MAX; ++i)
-      if (fkey(x[i] / T) == kth) {
-        ck[pos] = kth;
-        ci[pos] = i;
-        ++pos;
-      }
+    for (int i = c0 + tid; i < c1; i += SP_T) visit(x[i], i);
   }
-  const int n = (tot_gt + tot_eq) < SK_MAX ? (tot_gt + tot_eq) : SK_MAX;
-  int np2 = 1;
-  while (np2 < n) np2 <<= 1;
-  for (int j = n + tid; j < np2; j += SK_T) {  // padding sorts last
-    ck[j] = 0u;
-    ci[j] = 0x7fffffff;
+
+  // ---- this chunk's result to the workspace
+  const size_t rg = (size_t)r * G + g;
+  if (kind == 0) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint64_t t = __shfl_xor(best, o, 64);
+      best = t > best ? t : best;
+    }
+    if (lane == 0) red[tid >> 6] = best;
+  } else if (kind == 4) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) n_tie += __shfl_xor(n_tie, o, 64);
+    if (lane == 0) red[tid >> 6] = n_tie;
   }
   __syncthreads();
-
-  // ---- 3. bitonic sort: key descending, index ascending
-  for (int size = 2; size <= np2; size <<= 1) {
-    for (int stride2 = size >> 1; stride2 > 0; stride2 >>= 1) {
-      for (int j = tid; j < np2; j += SK_T) {
-        const int partner = j ^ stride2;
-        if (partner > j) {
-          const bool desc = (j & size) == 0;  // this run sorts "before-first" when desc
-          const uint32_t ka = ck[j], kb = ck[partner];
-          const int ia = ci[j], ib = ci[partner];
-          const bool a_first = ka > kb || (ka == kb && ia < ib);
-          if (a_first != desc) {
-            ck[j] = kb;
-            ck[partner] = ka;
-            ci[j] = ib;
-            ci[partner] = ia;
-          }
-        }
-      }
-      __syncthreads();
+  if (kind == 0 || kind == 4) {
+    if (tid == 0) {
+      uint64_t v = red[0];
+      for (int w = 1; w < SP_T / 64; ++w) v = kind == 0 ? (red[w] > v ? red[w] : v) : v + red[w];
+      st_dev_u64(&ws.best[rg], v);
     }
   }
+  if (do_cnt) {
+    const int b = tid;
+    uint32_t c = 0, mi = 0xffffffffu;
+    uint64_t m = 0;
+#pragma unroll
+    for (int k = 0; k < SP_COPIES; ++k) {
+      c += h_cnt[k][b];
+      m += h_mass[k][b];
+      mi = h_min[k][b] < mi ? h_min[k][b] : mi;
+    }
+    st_dev_u32(&ws.cnt[rg * SP_BINS + b], c);
+    if (do_mass) st_dev_u64(&ws.mass[rg * SP_BINS + b], m);
+    if (do_min) st_dev_u32(&ws.mini[rg * SP_BINS + b], mi);
+  }
+  vm_drain();
+  __syncthreads();
+  if (tid == 0) is_last = atomicAdd(&ws.tick[r], 1) == G - 1;
+  __syncthreads();
+  if (!is_last) return;
 
-  // ---- 4. masses in sorted order, cumulative (each thread 4 consecutive candidates, then a block scan)
-  const float zmax = x[ci[0]] / T;
-  float e[SK_MAX / SK_T];
-  float run = 0.f;
-#pragma unroll
-  for (int q = 0; q < SK_MAX / SK_T; ++q) {
-    const int j = tid * (SK_MAX / SK_T) + q;
-    e[q] = j < n ? __expf(x[ci[j]] / T - zmax) : 0.f;
-    run += e[q];
-  }
-  // float exclusive scan over threads (fixed order)
-  float incl = run;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
-  if (lane == 63) red_v[w] = incl;
-  __syncthreads();
-  float base = 0.f;
-  for (int i = 0; i < w; ++i) base += red_v[i];
-  base += incl - run;
-#pragma unroll
-  for (int q = 0; q < SK_MAX / SK_T; ++q) {
-    base += e[q];
-    const int j = tid * (SK_MAX / SK_T) + q;
-    if (j < n) cm[j] = base;
-  }
+  // ---- last workgroup of the row: combine the G chunks in chunk order.
+  // Every device-coherent load a thread needs is issued before the first is
+  // used, so their latencies overlap.
   if (tid == 0) {
-    n_cand = n;
-    cut = n - 1;      // stays if no crossing is found (only with NaN masses)
-    out[r] = ci[0];   // likewise for the draw below
+    __hip_atomic_store(&ws.tick[r], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    found = 0;
   }
+  __shared__ uint64_t per_chunk[SP_MAX_G];
+  if (kind == 0 || kind == 4) {
+    if (tid < G) per_chunk[tid] = ld_dev_u64(&ws.best[(size_t)r * G + tid]);
+    __syncthreads();
+  }
+  if (kind == 0 && tid == 0) {
+    uint64_t v = 0;
+    for (int q = 0; q < G; ++q) v = per_chunk[q] > v ? per_chunk[q] : v;
+    const int idx = (int)~(uint32_t)v;
+    out[r] = idx;  // the greedy answer, or the fallback of a sampling row (never used unless masses vanish)
+    if (greedy) {
+      ws.st[r].mode = 0;
+    } else {
+      ws.st[r].zmax = skey_inv((uint32_t)(v >> 32));
+    }
+  }
+  if (kind == 4) {
+    // the chunk holding the j-th tied token, then that token by an ordered scan of the chunk
+    __shared__ int tg, tj;
+    if (tid == 0) {
+      int j = s.j, q = 0;
+      for (; q < G; ++q) {
+        const int n = (int)per_chunk[q];
+        if (j < n) break;
+        j -= n;
+      }
+      tg = q < G ? q : G - 1;
+      tj = j;
+    }
+    __syncthreads();
+    const int q0 = tg * chunk, q1 = (q0 + chunk) < vocab ? (q0 + chunk) : vocab;
+    int before = 0;
+    for (int base = q0; base < q1; base += SP_T) {  // uniform trip count
+      const int i = base + tid;
+      const bool hit = i < q1 && skey(x[i] * s.inv_t, 0u) == s.tu_key;
+      const uint64_t bal = __ballot(hit);
+      const int wn = __popcll(bal);
+      if (lane == 0) red[tid >> 6] = (uint64_t)wn;
+      __syncthreads();
+      int wbefore = 0, tot = 0;
+      for (int w = 0; w < SP_T / 64; ++w) {
+        if (w < (tid >> 6)) wbefore += (int)red[w];
+        tot += (int)red[w];
+      }
+      const int rank = before + wbefore + __popcll(bal & ((1ull << lane) - 1ull));
+      if (hit && rank == tj) {
+        out[r] = i;
+        found = 1;
+      }
+      before += tot;
+      __syncthreads();
+      if (found || before > tj) break;
+    }
+    return;
+  }
+  if (!do_cnt) return;
+
+  // per-bin totals over the chunks (thread b holds bin 255 - b, so an
+  // inclusive scan over threads is the suffix sum from the top bin down):
+  // count, mass and lowest index of the bin
+  const int b = SP_BINS - 1 - tid;
+  uint32_t n_b = 0, min_b = 0xffffffffu;
+  uint64_t m_b = 0;
+  {
+    uint32_t c[SP_MAX_G], mi[SP_MAX_G];
+    uint64_t m[SP_MAX_G];
+#pragma unroll
+    for (int q = 0; q < SP_MAX_G; ++q) {
+      const size_t e = ((size_t)r * G + (q < G ? q : G - 1)) * SP_BINS + b;
+      c[q] = ld_dev_u32(&ws.cnt[e]);
+      m[q] = do_mass ? ld_dev_u64(&ws.mass[e]) : 0ull;
+      mi[q] = do_min ? ld_dev_u32(&ws.mini[e]) : 0xffffffffu;
+    }
+#pragma unroll
+    for (int q = 0; q < SP_MAX_G; ++q) {
+      if (q < G) {
+        n_b += c[q];
+        m_b += m[q];
+        min_b = mi[q] < min_b ? mi[q] : min_b;
+      }
+    }
+  }
+  const uint64_t v = do_mass ? m_b : (uint64_t)n_b;
+  const uint64_t incl = block_incl_scan_u64(v, red);
+  __shared__ uint64_t grand;
+  if (tid == SP_T - 1) grand = incl;
   __syncthreads();
-  const float total = cm[n - 1];
-  // top-p: the first position whose cumulative mass reaches p * total
-  for (int j = tid; j < n; j += SK_T)
-    if (cm[j] >= p * total && (j == 0 || cm[j - 1] < p * total)) cut = j;
+
+  // the threshold this select must reach, fixed on its first digit
+  uint64_t need = s.need;
+  if (digit == 3) {
+    if (kind == 1 || (kind == 0 && s.topk)) {
+      need = s.k;
+    } else if (kind == 2) {  // top-p: the shortest prefix whose mass reaches p of all candidates
+      const double pz = (double)s.p * (double)grand;
+      uint64_t pp = (uint64_t)ceil(pz);
+      pp = pp < 1 ? 1 : (pp > grand ? grand : pp);
+      need = pp;
+    } else {  // draw: first cumulative mass above u * kept
+      const uint64_t kept = s.topp ? s.kept : grand;
+      const uint64_t target = (uint64_t)floor((double)s.u * (double)kept);
+      need = target + 1;
+      if (tid == 0) ws.st[r].kept = kept;
+    }
+  }
+  const uint64_t excl = incl - v;
+  const bool mine = need >= 1 && excl < need && incl >= need;
+  if (mine) found = 1;
   __syncthreads();
-  const int c = cut;
-  const float target = u * cm[c];
-  for (int j = tid; j <= c; j += SK_T)
-    if (cm[j] > target && (j == 0 || cm[j - 1] <= target)) out[r] = ci[j];
+  if (!found) {
+    // masses vanished (a non-finite row): keep the row's maximum (written by pass 0)
+    if (tid == 0) ws.st[r].mode = 0;
+    return;
+  }
+  if (mine) {
+    const uint32_t key = prefix | ((uint32_t)b << shift);
+    const uint64_t rem = need - excl;  // >= 1
+    const uint64_t above = (digit == 3 ? 0ull : s.above) + excl;
+    SampRow& o = ws.st[r];
+    if (digit != 0) {
+      o.prefix = key;
+      o.need = rem;
+      o.above = above;
+    } else {
+      // the selected key's group: every member has the same z, hence the same mass
+      o.prefix = 0u;
+      o.need = 0;
+      o.above = 0;
+      if (kind <= 1) {
+        o.lo_key = key;  // candidates: key >= the k-th largest key
+      } else if (kind == 2) {
+        const uint64_t w = n_b ? m_b / n_b : 0;
+        uint64_t keep = w ? (rem + w - 1) / w : n_b;
+        keep = keep > n_b ? n_b : (keep < 1 ? 1 : keep);
+        o.kept = above + keep * w;
+        o.lo_key = key;  // the cut's group: only its first `keep` members are kept
+      } else {
+        const uint64_t w = n_b ? m_b / n_b : 0;
+        uint64_t jj = w ? (rem - 1) / w : 0;
+        jj = jj >= n_b ? (n_b ? n_b - 1 : 0) : jj;
+        o.tu_key = key;
+        o.j = (int32_t)jj;
+        if (jj == 0) {
+          out[r] = (int)min_b;
+          o.mode = 0;
+        }
+      }
+    }
+  }
 }
 
+static_assert(sizeof(SampRow) == q3v::SAMPLE_ROW_BYTES, "row state size must match the workspace layout");
+
 void launch_sample(const float* logits, int rows, int vocab, int64_t stride, const float* temperature,
-                   const int32_t* top_k, const float* top_p, const float* uniform, int32_t* out, hipStream_t s) {
+                   const int32_t* top_k, const float* top_p, const float* uniform, int32_t* out, void* wsp,
+                   hipStream_t s) {
+  const int G = q3v::sample_chunks(rows, vocab);
+  int chunk = (vocab + G - 1) / G;
+  chunk = (chunk + 3) & ~3;
+  const q3v::SampleWsLayout L = q3v::sample_ws_layout(rows, vocab);
+  char* p = static_cast<char*>(wsp);
+  SampWs ws;
+  ws.st = reinterpret_cast<SampRow*>(p + L.st);
+  ws.tick = reinterpret_cast<int*>(p + L.tick);
+  ws.cnt = reinterpret_cast<uint32_t*>(p + L.cnt);
+  ws.mass = reinterpret_cast<uint64_t*>(p + L.mass);
+  ws.mini = reinterpret_cast<uint32_t*>(p + L.mini);
+  ws.best = reinterpret_cast<uint64_t*>(p + L.best);
+  hipLaunchKernelGGL(k_sample_init, dim3((rows + SP_T - 1) / SP_T), dim3(SP_T), 0, s, rows, vocab, temperature,
+                     top_k, top_p, uniform, ws);
   const bool vec = ((uintptr_t)logits & 15u) == 0 && (stride & 3) == 0;
-  if (vec)
-    hipLaunchKernelGGL(k_sample<true>, dim3(rows), dim3(SK_T), 0, s, logits, vocab, stride, temperature, top_k, top_p,
-                       uniform, out);
-  else
-    hipLaunchKernelGGL(k_sample<false>, dim3(rows), dim3(SK_T), 0, s, logits, vocab, stride, temperature, top_k,
-                       top_p, uniform, out);
+  for (int pass = 0; pass < SP_PASSES; ++pass) {
+    if (vec)
+      hipLaunchKernelGGL(k_sample_pass<true>, dim3(G, rows), dim3(SP_T), 0, s, pass, logits, vocab, stride, G, chunk,
+                         ws, out);
+    else
+      hipLaunchKernelGGL(k_sample_pass<false>, dim3(G, rows), dim3(SP_T), 0, s, pass, logits, vocab, stride, G,
+                         chunk, ws, out);
+  }
 }
 
 }  // namespace q3

@@ -156,12 +156,36 @@ int check_rope_convert_call(const void* w_qkv, const void* q_norm, const void* k
   return Q3_OK;
 }
 
+SampleWsLayout sample_ws_layout(int32_t rows, int32_t vocab) {
+  SampleWsLayout L{};
+  const size_t G = (size_t)sample_chunks(rows, vocab), R = (size_t)rows;
+  auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  size_t off = 0;
+  L.st = off;
+  off += al(SAMPLE_ROW_BYTES * R);
+  L.tick = off;
+  off += al(4 * R);
+  L.cnt = off;
+  off += al(4 * R * G * 256);
+  L.mass = off;
+  off += al(8 * R * G * 256);
+  L.mini = off;
+  off += al(4 * R * G * 256);
+  L.best = off;
+  off += al(8 * R * G);
+  L.total = off;
+  return L;
+}
+
 int check_sample_call(const float* logits, int32_t rows, int32_t vocab, int64_t row_stride, const float* temperature,
-                      const int32_t* top_k, const float* top_p, const float* uniform, const int32_t* out_idx) {
-  if (!logits || !temperature || !top_k || !top_p || !uniform || !out_idx) return Q3_ERR_NULL;
-  if (rows < 1 || vocab < 1 || row_stride < vocab) return Q3_ERR_SHAPE;
-  if (!al4(logits) || !al4(temperature) || !al4(top_k) || !al4(top_p) || !al4(uniform) || !al4(out_idx))
+                      const int32_t* top_k, const float* top_p, const float* uniform, const int32_t* out_idx,
+                      const void* ws, size_t ws_bytes) {
+  if (!logits || !temperature || !top_k || !top_p || !uniform || !out_idx || !ws) return Q3_ERR_NULL;
+  if (rows < 1 || rows > SAMPLE_MAX_ROWS || vocab < 1 || row_stride < vocab) return Q3_ERR_SHAPE;
+  if (!al4(logits) || !al4(temperature) || !al4(top_k) || !al4(top_p) || !al4(uniform) || !al4(out_idx) ||
+      !al16(ws))
     return Q3_ERR_ALIGN;
+  if (ws_bytes < sample_ws_layout(rows, vocab).total) return Q3_ERR_WORKSPACE;
   return Q3_OK;
 }
 

@@ -83,8 +83,26 @@ int check_decode_call(const q3_model* m, const q3_kv* kv, int32_t batch, const i
 
 int check_rope_convert_call(const void* w_qkv, const void* q_norm, const void* k_norm, const void* w_qkv_out,
                             const void* q_norm_out, const void* k_norm_out);
+// Sampling: each row is split into sample_chunks() contiguous chunks, one
+// workgroup each (about 512 workgroups in all, at most 32 per row, chunks of
+// at least 1024 tokens); the workspace holds per-row state and per-chunk
+// 256-bin histograms.
+constexpr size_t SAMPLE_ROW_BYTES = 128;
+inline int sample_chunks(int32_t rows, int32_t vocab) {
+  int g = (int)((512 + (int64_t)rows - 1) / rows);
+  g = g > 32 ? 32 : g;
+  const int by_len = vocab / 1024;
+  g = g > by_len ? by_len : g;
+  return g < 1 ? 1 : g;
+}
+struct SampleWsLayout {
+  size_t st, tick, cnt, mass, mini, best, total;
+};
+SampleWsLayout sample_ws_layout(int32_t rows, int32_t vocab);
+constexpr int32_t SAMPLE_MAX_ROWS = 1 << 16;
 int check_sample_call(const float* logits, int32_t rows, int32_t vocab, int64_t row_stride, const float* temperature,
-                      const int32_t* top_k, const float* top_p, const float* uniform, const int32_t* out_idx);
+                      const int32_t* top_k, const float* top_p, const float* uniform, const int32_t* out_idx,
+                      const void* ws, size_t ws_bytes);
 int check_prefill_packed_call(const q3_model* m, const q3_kv* kv, int32_t n_seqs, int32_t n_tokens,
                               const int32_t* ids, const int32_t* cu_seqlens, const int32_t* start_pos,
                               int32_t max_seq_tokens, const float* last_logits, const int32_t* next_ids,

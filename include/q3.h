@@ -250,28 +250,37 @@ int q3_argmax(const float *logits, int32_t rows, int32_t vocab, int64_t row_stri
               int32_t *out_idx, void *stream);
 
 
-/* Temperature / top-k / top-p sampling of logits rows: the path "第 3 章"
- * §4.3's Sampler.sample takes when temperatures are given (the pages name
- * the steps; this is their plain reading).  Row r, with
- * T = temperature[r], k = top_k[r], p = top_p[r], u = uniform[r]:
+/* Temperature / top-k / top-p sampling of logits rows over the whole
+ * vocabulary: the path "第 3 章" §4.3's Sampler.sample takes when
+ * temperatures are given (the pages name the steps; this is their plain
+ * reading).  Row r, with T = temperature[r], k = top_k[r], p = top_p[r],
+ * u = uniform[r]:
  *   - T <= 0 (or NaN): greedy, as q3_argmax;
  *   - z = logits / T;
- *   - candidates: every token with z >= the k-th largest z (k = 4096 when
- *     top_k <= 0 or > 4096, at most vocab), ordered by z descending then
- *     index ascending, at most 4096 of them;
+ *   - candidates: every token with z >= the k-th largest z, ties included
+ *     (k <= 0 or k >= vocab: every token), ordered by z descending then
+ *     index ascending;
  *   - softmax over the candidates; keep the shortest prefix of that order
  *     whose mass reaches p (p outside (0, 1] means 1);
  *   - out_idx[r] = the first kept candidate whose cumulative mass exceeds
  *     u times the kept mass (u is clamped to [0, 1)).
- * Arithmetic is float32; the random draw is the caller's, so a run is
- * reproducible.
+ * There is no cap on the number of candidates.  z is float32 (logits times
+ * 1/T); masses are exp(z - max z) in float32, summed exactly as 40-bit fixed
+ * point integers, so a call is reproducible bit for bit; the random draw is
+ * the caller's.  Rows holding NaN or +inf give some index in [0, vocab).
  *   logits       float32, rows x vocab, row_stride elements apart.
  *   temperature  float32 [rows]; top_k int32 [rows]; top_p float32 [rows];
  *   uniform      float32 [rows]; out_idx int32 [rows]  (all device).
- * Errors: Q3_ERR_NULL, Q3_ERR_SHAPE (rows < 1, vocab < 1,
- * row_stride < vocab), Q3_ERR_ALIGN (4-byte alignment), Q3_ERR_HIP. */
+ *   ws           device workspace of q3_sample_workspace_bytes(rows, vocab)
+ *                bytes (about 100 KB per row), 16-byte aligned; no initial
+ *                content is needed.
+ * Errors: Q3_ERR_NULL, Q3_ERR_SHAPE (rows outside 1 .. 65536, vocab < 1,
+ * row_stride < vocab), Q3_ERR_ALIGN (4-byte alignment; ws 16-byte),
+ * Q3_ERR_WORKSPACE, Q3_ERR_HIP. */
+size_t q3_sample_workspace_bytes(int32_t rows, int32_t vocab);
 int q3_sample(const float *logits, int32_t rows, int32_t vocab, int64_t row_stride, const float *temperature,
-              const int32_t *top_k, const float *top_p, const float *uniform, int32_t *out_idx, void *stream);
+              const int32_t *top_k, const float *top_p, const float *uniform, int32_t *out_idx, void *ws,
+              size_t ws_bytes, void *stream);
 
 /* Epilogues of q3_linear. */
 enum {

@@ -1,6 +1,7 @@
 // Host-only checks of the C-ABI argument validation, built with g++ and the
 // address/undefined-behaviour sanitizers (no GPU, no HIP runtime).
 #include <cstdio>
+#include <initializer_list>
 #include <cstdlib>
 #include <cstdint>
 
@@ -145,6 +146,31 @@ int main() {
   EXPECT_EQ(check_argmax_call(static_cast<const float*>(A(0x100002)), 3, 10, 10, out), Q3_ERR_ALIGN);
 
   if (failures) { std::printf("%d failures\n", failures); return 1; }
+  // sampling workspace: regions in order, 256-B aligned, disjoint, sized for every row and chunk
+  for (int rows : {1, 3, 32, 1 << 16}) {
+    for (int vocab : {1, 50, 1023, 1024, 151936}) {
+      const int G = sample_chunks(rows, vocab);
+      EXPECT_EQ(G >= 1 && G <= 32 && (G == 1 || vocab / G >= 1024), true);
+      const SampleWsLayout L = sample_ws_layout(rows, vocab);
+      const size_t R = rows, RG = (size_t)rows * G;
+      EXPECT_EQ(L.st, (size_t)0);
+      EXPECT_EQ(L.tick >= L.st + SAMPLE_ROW_BYTES * R && L.cnt >= L.tick + 4 * R, true);
+      EXPECT_EQ(L.mass >= L.cnt + 4 * RG * 256 && L.mini >= L.mass + 8 * RG * 256, true);
+      EXPECT_EQ(L.best >= L.mini + 4 * RG * 256 && L.total >= L.best + 8 * RG, true);
+      EXPECT_EQ((L.tick | L.cnt | L.mass | L.mini | L.best | L.total) % 256, (size_t)0);
+    }
+  }
+  {
+    const size_t need = sample_ws_layout(4, 100).total;
+    const float* f = static_cast<const float*>(A(0x100000));
+    const int32_t* k = static_cast<const int32_t*>(A(0x200000));
+    int32_t* o = static_cast<int32_t*>(A(0x300000));
+    EXPECT_EQ(check_sample_call(f, 4, 100, 100, f, k, f, f, o, A(0x400000), need), Q3_OK);
+    EXPECT_EQ(check_sample_call(f, 4, 100, 100, f, k, f, f, o, A(0x400000), need - 1), Q3_ERR_WORKSPACE);
+    EXPECT_EQ(check_sample_call(f, 4, 100, 100, f, k, f, f, o, nullptr, need), Q3_ERR_NULL);
+    EXPECT_EQ(check_sample_call(f, 4, 100, 100, f, k, f, f, o, A(0x400004), need), Q3_ERR_ALIGN);
+    EXPECT_EQ(check_sample_call(f, SAMPLE_MAX_ROWS + 1, 100, 100, f, k, f, f, o, A(0x400000), need), Q3_ERR_SHAPE);
+  }
   std::printf("validate_test: all checks passed\n");
   return 0;
 }

@@ -199,17 +199,24 @@ def test_rope_conversion_rejects_bad_arguments(B):
 
 def test_sample_rejects_bad_arguments(B):
     smp = lambda *a: B.q3_sample(*a, stream=0, check=False)
-    ok = [0x1000, 4, 100, 100, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000]
-    for i in (0, 4, 5, 6, 7, 8):
+    need = B.q3_sample_workspace_bytes(4, 100)
+    assert need > 0 and B.q3_sample_workspace_bytes(0, 100) == 0 and B.q3_sample_workspace_bytes(4, 0) == 0
+    assert B.q3_sample_workspace_bytes(4, 151936) > B.q3_sample_workspace_bytes(4, 100)
+    ok = [0x1000, 4, 100, 100, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x10000, need]
+    for i in (0, 4, 5, 6, 7, 8, 9):
         a = list(ok)
         a[i] = None
         assert smp(*a) == B.Q3_ERR_NULL
-    for i, bad in ((1, 0), (2, 0), (3, 99)):
+    for i, bad in ((1, 0), (1, (1 << 16) + 1), (2, 0), (3, 99)):
         a = list(ok)
         a[i] = bad
         assert smp(*a) == B.Q3_ERR_SHAPE
     a = list(ok); a[7] = 0x5002
     assert smp(*a) == B.Q3_ERR_ALIGN
+    a = list(ok); a[9] = 0x10004
+    assert smp(*a) == B.Q3_ERR_ALIGN
+    a = list(ok); a[10] = need - 1
+    assert smp(*a) == B.Q3_ERR_WORKSPACE
 
 
 def test_rope_table_matches_oracle_angles(B):
