@@ -152,28 +152,37 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos, block: int = 1
     0..p exactly (bottom-right aligned; "从零开始写Qwen3（二）" §Attn warns a
     one-token decode query must see every cached key).  Scores are scaled by
     1/sqrt(D) and normalised with a max-shifted softmax
-    ("古法手撕简易LLM推理器" §工具函数).  Query rows are processed in blocks
-    only to bound memory."""
+    ("古法手撕简易LLM推理器" §工具函数).
+
+    Query rows are processed in blocks only to bound memory, and a block
+    reads keys only up to its largest position (every later key is masked
+    for all of its rows).  The steps run as float64 torch CPU ops, which use
+    every host core."""
+    import torch
     hq, tq, d = q.shape
     hkv, s_len, _ = k.shape
     assert hq % hkv == 0, "Hq must be a multiple of Hkv"
     groups = hq // hkv
     q_pos = np.asarray(q_pos, dtype=np.int64).reshape(tq)
-    key_idx = np.arange(s_len)
-    out = np.empty((hq, tq, d), dtype=np.float64)
+    qt = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float64))
+    kt = torch.from_numpy(np.ascontiguousarray(k, dtype=np.float64))
+    vt = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float64))
+    pos_t = torch.from_numpy(q_pos)
+    out = torch.empty((hq, tq, d), dtype=torch.float64)
     scale = 1.0 / np.sqrt(d)
-    for h in range(hq):
-        g = h // groups
-        for r0 in range(0, tq, block):
-            r1 = min(tq, r0 + block)
-            sc = (q[h, r0:r1] @ k[g].T) * scale                   # [tb, S]
-            visible = key_idx[None, :] <= q_pos[r0:r1, None]
-            sc = np.where(visible, sc, -np.inf)
-            m = np.max(sc, axis=-1, keepdims=True)
-            e = np.where(visible, np.exp(sc - m), 0.0)
-            w = e / np.sum(e, axis=-1, keepdims=True)
-            out[h, r0:r1] = w @ v[g]
-    return out
+    for r0 in range(0, tq, block):
+        r1 = min(tq, r0 + block)
+        n_keys = min(s_len, int(q_pos[r0:r1].max()) + 1)
+        visible = torch.arange(n_keys)[None, :] <= pos_t[r0:r1, None]       # [tb, n_keys]
+        for h in range(hq):
+            g = h // groups
+            sc = (qt[h, r0:r1] @ kt[g, :n_keys].T) * scale                      # [tb, n_keys]
+            sc = torch.where(visible, sc, -torch.inf)
+            m = torch.max(sc, dim=-1, keepdim=True).values
+            e = torch.where(visible, torch.exp(sc - m), 0.0)
+            w = e / torch.sum(e, dim=-1, keepdim=True)
+            out[h, r0:r1] = w @ vt[g, :n_keys]
+    return out.numpy()
 
 
 # ---------------------------------------------------------------- weights
