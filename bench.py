@@ -1,22 +1,24 @@
 """Benchmark of the Qwen3-0.6B-shape forward on one MI355X.
 
-Default workload (the one the headline metric is quoted on): the full
-28-layer stack with random-init bf16 weights, batch 1, a 128-token prompt of
-uniform random ids, prefill, then 64 greedy decode steps with the KV cache.
-One "step" is that whole job; it is captured once as a HIP graph (prefill
-graph + decode-loop graph) and replayed.  value = (prompt + generated
-tokens) / second.
+Default workload (the headline): the prefill-bound configuration, the full
+28-layer stack with random-init bf16 weights prefilling 8 prompts of 4096
+uniform random ids, logits at each sequence's last position.  One "step" is
+that whole prefill, captured once as a HIP graph and replayed; value =
+prompt tokens / second.  The same run then measures the decode-bound
+configuration (batch 32, 2048 cached positions, 128 greedy steps; its setup
+prefill untimed) and reports it under "decode_b32_ctx2048".
 
-Other workloads (--workload) measure the decode-bound (batch 32, 2048 cached
-positions, 128 steps), prefill-bound (8 x 4096) and long-context (batch 4,
-32768 cached positions, 64 steps) shapes; their setup prefill is untimed.
+Other workloads (--workload) measure the batch-1 prompt + greedy decode,
+long-context decode (batch 4, 32768 cached positions) and packed ragged
+prefill shapes.
 
-Besides the JSON line's headline value, the script times the dominant
-kernel alone with HIP events on the stream it runs on (through the
-library's helper entry points, same kernel, shape and launch configuration
-as inside the step) for the roofline object, reports the whole timed phase
-against the roofline (step_roofline), and times the float64 CPU oracle on a
-bounded sample of the same workload for the cpu_baseline object.
+Besides the headline value, the script times the dominant kernel alone with
+HIP events on the stream it runs on (through the library's helper entry
+points, same kernel, shape and launch configuration as inside the step) for
+the roofline object, each prefill projection alone in its in-step
+configuration (gemm_rooflines), reports the whole timed phase against the
+roofline (step_roofline), and times the float64 CPU oracle on a bounded
+sample of the same workload for the cpu_baseline object.
 """
 from __future__ import annotations
 
@@ -60,7 +62,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="prefill128_decode64", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="prefill_8x4096", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-decode-extra", action="store_true",
+                    help="with the default workload, skip the batch-32 decode measurement")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sample", default=None, metavar="T,K,P",
@@ -68,8 +72,9 @@ def parse():
     ap.add_argument("--eos-id", type=int, default=None,
                     help="decode with q3_decode_step_eos (on-device done mask) and this end-of-sequence token")
     ap.add_argument("--kernel-iters", type=int, default=200)
-    ap.add_argument("--kernel-only", action="store_true",
-                    help="time only the workload's dominant kernel (the run the counter passes profile)")
+    ap.add_argument("--kernel-only", nargs="?", const="dominant", default=None, choices=("dominant", "gemm"),
+                    help="time only the workload's dominant kernel (or, with 'gemm', its four prefill "
+                         "projections): the runs the counter passes profile")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="copy 1 GiB on the device three times (counter calibration) and exit")
     return ap.parse_args()
@@ -212,6 +217,7 @@ def dominant_kernel(torch, B, dev, dm, r, workload, iters, use_graph=True):
     - 8 x 4096 prefill: the causal flash-attention kernel.
     """
     batch, T, steps, _ = WORKLOADS[workload]
+    extra = {}
     if workload == "prefill128_decode64":
         # one launch per layer's weights in turn (28 x 31.5 MB read ahead, more
         # than the 256 MB last-level cache), so they stream from HBM as in the step
@@ -233,11 +239,12 @@ def dominant_kernel(torch, B, dev, dm, r, workload, iters, use_graph=True):
                                        lw.w_down, nxt.w_qkv)
         warm_bytes = (B.HIDDEN * B.N_HEADS * B.HEAD_DIM + 2 * B.INTER * B.HIDDEN + B.HIDDEN * B.INTER
                       + B.QKV_ROWS * B.HIDDEN) * 2
-        algo = float(batch * (p + 1) * 8 * 128 * 2 * 2 + batch * (B.QKV_ROWS + 2048) * 2 + warm_bytes)
+        extra["read_ahead_bytes_per_launch"] = warm_bytes
+        algo = float(batch * (p + 1) * 8 * 128 * 2 * 2 + batch * (B.QKV_ROWS + 2048) * 2)
         name, bound, per = (f"k_attn_decode + L2 read-ahead (batch {batch}, position {p}, one layer)", "hbm",
-                            "K and V bytes of positions 0..p + q|k|v in + out + the o_proj, gate|up, down and "
-                            "next q|k|v weight bytes the launch reads ahead (the projections after it read "
-                            "them from L2)")
+                            "the attention's own bytes: K and V of positions 0..p + q|k|v in + out (the "
+                            "weights the same launch reads ahead for the projections after it are "
+                            "read_ahead_bytes_per_launch, not counted here)")
         iters = max(iters, 280)
         reps = 28
     elif workload == "prefill_packed_ragged":
@@ -278,9 +285,45 @@ def dominant_kernel(torch, B, dev, dm, r, workload, iters, use_graph=True):
     else:
         achieved, peak, unit = algo / t / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
     traffic = measured_traffic(workload)
-    return {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": round(traffic) if traffic else None, "kernel": name,
-            "avg_launch_us": round(t * 1e6, 2), "algorithmic_per_launch": algo, "algorithmic_unit": per}
+    out = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+           "frac": round(achieved / peak, 4), "traffic": round(traffic) if traffic else None, "kernel": name,
+           "avg_launch_us": round(t * 1e6, 2), "algorithmic_per_launch": algo, "algorithmic_unit": per}
+    if "read_ahead_bytes_per_launch" in extra:
+        out.update(extra)
+        out["achieved_with_read_ahead"] = round((algo + extra["read_ahead_bytes_per_launch"]) / t / 1e9, 1)
+    return out
+
+
+# The four projections of a layer as the prefill runs them (persistent MFMA
+# GEMM at >= 2048 rows): name, N (weight rows), K, epilogue.
+PREFILL_GEMMS = (("q|k|v", 4096, 1024, "Q3_EPI_STORE_BF16"), ("o_proj + residual", 1024, 2048, "Q3_EPI_ADD_F32"),
+                 ("gate|up + silu(gate)*up", 6144, 1024, "Q3_EPI_SILU_GATE"),
+                 ("down + residual", 1024, 3072, "Q3_EPI_ADD_F32"))
+
+
+def gemm_rooflines(torch, B, dm, M, iters, use_graph=True):
+    """Each prefill projection alone at M rows, in the launch configuration the
+    layer uses (q3_linear runs the same kernel and epilogue as the step), timed
+    with HIP events on its stream; fraction of the bf16 MFMA peak."""
+    res = []
+    lw = dm.layers[0]
+    weights = {4096: lw.w_qkv, 6144: lw.w_gate_up}
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    for name, N, K, epi in PREFILL_GEMMS:
+        x = torch.randn((M, K), device="cuda", generator=gen).to(torch.bfloat16)
+        w = weights.get(N, lw.w_o if K == 2048 else lw.w_down)
+        e = getattr(B, epi)
+        cols = N // 2 if e == B.Q3_EPI_SILU_GATE else N
+        dt = torch.float32 if e == B.Q3_EPI_ADD_F32 else torch.bfloat16
+        out = torch.zeros((M, cols), dtype=dt, device="cuda")
+        fn = lambda x=x, w=w, out=out, N=N, K=K, e=e, cols=cols: B.q3_linear(x, w, out, M, N, K, cols, e)
+        t = _time_launches(torch, fn, iters, 10, use_graph)
+        tf = 2.0 * M * N * K / t / 1e12
+        res.append({"gemm": name, "M": M, "N": N, "K": K, "avg_launch_us": round(t * 1e6, 2),
+                    "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / BF16_PEAK_TFLOPS, 4)})
+        del x, out
+    return res
 
 
 # Source files of each workload's dominant kernel.  The HBM traffic measured
@@ -338,8 +381,17 @@ def step_roofline(workload, pre_ms, dec_ms):
             "frac": round(a / HBM_PEAK_GBS, 4), "bytes_per_step": round(per_step)}
 
 
-def cpu_baseline(workload, bits):
-    """The float64 oracle on a bounded sample of the workload (host cores)."""
+def cpu_baseline(workload, bits, om=None):
+    """The float64 oracle on a bounded sample of the workload (host cores):
+    - batch-1 prompt + decode: the whole workload (one sequence), repeated to
+      about 10 s;
+    - 8 x 4096 prefill: sequence 0's full 4096-token prefill;
+    - packed prefill: the first packed sequence's full prefill;
+    - decode workloads: sequence 0, a few greedy decode steps at the
+      workload's full context.  The float64 cache of those positions is
+      filled with seeded N(0, 1) values instead of an oracle prefill of the
+      prompt (hours of float64 work at 32768 positions); the timed steps are
+      the oracle's own decode arithmetic over that many cached positions."""
     import oracle as O
     from decoder_only_transformer_qwen3_amd import inputs as I
     try:
@@ -352,10 +404,11 @@ def cpu_baseline(workload, bits):
         threads = os.cpu_count()
     batch, T, steps, _ = WORKLOADS[workload]
     t0 = time.perf_counter()
-    om = O.Model(bits)
+    if om is None:
+        om = O.Model(bits)
     setup = time.perf_counter() - t0
-    ids = I.token_ids(1000 + batch, (batch, T))[:1]
     if workload == "prefill128_decode64":
+        ids = I.token_ids(1000 + batch, (batch, T))[:1]
         n_dec = steps  # the whole workload: prefill + every decode step, repeated to about 10 s
         reps, el = 0, 0.0
         while reps < 8 and (reps == 0 or el < 10.0):
@@ -370,73 +423,50 @@ def cpu_baseline(workload, bits):
         sample = (f"sequence 0: {T}-token prefill + {n_dec} greedy decode steps ({T + n_dec} tokens), "
                   f"the whole workload, run {reps} times")
         toks = (T + n_dec) * reps
-    elif workload in ("prefill_8x4096", "prefill_packed_ragged"):
-        Tp = 1024
+    elif workload == "prefill_8x4096":
+        ids = I.token_ids(1000 + batch, (batch, T))[:1]
         t0 = time.perf_counter()
-        O.prefill(om, ids[:, :Tp])
+        O.prefill(om, ids)
         el = time.perf_counter() - t0
-        sample = f"sequence 0, first {Tp} prompt tokens: prefill"
-        toks = Tp
+        sample = f"sequence 0: its full {T}-token prefill with last-position logits"
+        toks = T
+    elif workload == "prefill_packed_ragged":
+        n0 = ragged_lengths(batch)[0]
+        ids = I.token_ids(1000 + batch, (1, sum(ragged_lengths(batch))))[:, :n0]
+        t0 = time.perf_counter()
+        O.prefill(om, ids)
+        el = time.perf_counter() - t0
+        sample = f"packed sequence 0: its full {n0}-token prefill"
+        toks = n0
     else:
-        # decode-bound: the oracle decodes the whole batch at once; a float64 KV cache of the
-        # workload's length would not fit in host memory, so the steps run over a 16-token cache
-        Tp, n_dec = 16, 4
-        idsb = I.token_ids(1000 + batch, (batch, T))[:, :Tp]
-        _, nxt, cache, _ = O.prefill(om, idsb, max_seq=Tp + n_dec)
-        toks_in = nxt
+        n_dec = 4
+        rng = np.random.default_rng(77)
+        cache = O.KVCache(om.cfg, len(om.layers), 1, T + n_dec)
+        for li in range(len(om.layers)):
+            cache.k[li][:, :, :T] = rng.standard_normal((1, 8, T, 128))
+            cache.v[li][:, :, :T] = rng.standard_normal((1, 8, T, 128))
+        tok = int(I.token_ids(1000 + batch, (batch, 1))[0, 0])
         t0 = time.perf_counter()
         for i in range(n_dec):
-            _, toks_in = O.decode_step(om, cache, toks_in, np.full(batch, Tp + i))
+            _, nx = O.decode_step(om, cache, [tok], [T + i])
+            tok = int(nx[0])
         el = time.perf_counter() - t0
-        sample = (f"batch {batch}: {n_dec} greedy decode steps over a {Tp}-token cache "
-                  f"(untimed {Tp}-token prefill)")
-        toks = batch * n_dec
+        sample = (f"sequence 0: {n_dec} greedy decode steps at positions {T}..{T + n_dec - 1} over a float64 "
+                  f"cache of {T} positions (seeded N(0,1) cache content, not an oracle prefill)")
+        toks = n_dec
     return {"value": round(toks / el, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": sample, "seconds": round(el, 2), "weights_setup_s": round(setup, 2)}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "the hot path runs on one GPU only; --gpus must be 1",
-                          "n_gpus_requested": args.gpus}))
-        sys.exit(2)
-    import torch
-    from decoder_only_transformer_qwen3_amd import binding as B
-    from decoder_only_transformer_qwen3_amd import device as dev
-    from decoder_only_transformer_qwen3_amd import inputs as I
-
-    torch.cuda.set_device(0)
-    if args.calibrate_copy:
-        x = torch.empty(1 << 28, device="cuda")
-        y = torch.empty_like(x)
-        for _ in range(3):
-            y.copy_(x)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibration": "device copy", "bytes_read": 4 << 28, "bytes_written": 4 << 28,
-                          "launches": 3}), flush=True)
-        return
-    batch, T, steps, prefill_timed = WORKLOADS[args.workload]
-    log(f"[bench] workload {args.workload}: batch {batch}, prompt {T}, decode steps {steps}")
-    bits = I.model_weights(0)
-    dm = dev.DeviceModel(bits)
+def run_workload(args, workload, torch, B, dev, dm):
+    """Time one workload's step; returns its fields of the bench line."""
+    batch, T, steps, prefill_timed = WORKLOADS[workload]
+    log(f"[bench] workload {workload}: batch {batch}, prompt {T}, decode steps {steps}")
     sample = None
     if args.sample:
         t, k, p = args.sample.split(",")
         sample = (float(t), int(k), float(p))
     r = Runner(torch, B, dev, dm, batch, T, steps, args.eos_id, sample)
-    if args.kernel_only:
-        # no prefill ran: give the layer-0 cache the attention kernels read
-        # N(0, 1) values, as a prefill would leave there (all-zero keys would
-        # time a different, lower-power instruction stream)
-        gen = torch.Generator(device="cuda").manual_seed(5)
-        for c in (r.kv.k[0], r.kv.v[0]):
-            c.copy_(torch.randn(c.shape, device="cuda", generator=gen).to(torch.bfloat16))
-        rl = dominant_kernel(torch, B, dev, dm, r, args.workload, args.kernel_iters, not args.no_graph)
-        rl["source_sha256"] = kernel_source_digest(args.workload)
-        print(json.dumps({"workload": args.workload, "roofline": rl}), flush=True)
-        return
-
     use_graph = not args.no_graph
     # setup prefill (untimed); decode-only workloads restart from this state each step
     r.prefill()
@@ -489,16 +519,14 @@ def main():
     pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     step_ms = wall * 1e3 / args.steps
+    log(f"[bench] {workload}: {step_ms:.3f} ms per step")
 
     tokens_prefill = (sum(r.lens) if r.lens is not None else batch * T) if prefill_timed else 0
     tokens_decode = batch * steps
     value = (tokens_prefill + tokens_decode) / (step_ms * 1e-3)
-    out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (random-init weights N(0,0.02), uniform random token ids)",
-        "config": {"workload": args.workload, "layers": 28, "batch": batch, "prompt_len": T,
+    res = {
+        "value": round(value, 2), "ms_per_step": round(step_ms, 4),
+        "config": {"workload": workload, "layers": 28, "batch": batch, "prompt_len": T,
                    "decode_steps": steps, "prefill_timed": prefill_timed, "hip_graph": use_graph,
                    "parallelism": "single GPU", **({"eos_id": args.eos_id} if args.eos_id is not None else {}),
                    **({"sampling": args.sample} if args.sample else {}),
@@ -508,14 +536,87 @@ def main():
         "decode_tok_s": round(tokens_decode / (dec_ms * 1e-3), 1) if steps > 0 else None,
     }
     try:
-        out["roofline"] = dominant_kernel(torch, B, dev, dm, r, args.workload, args.kernel_iters)
+        res["roofline"] = dominant_kernel(torch, B, dev, dm, r, workload, args.kernel_iters, use_graph)
     except Exception as e:  # pragma: no cover
         log(f"[bench] kernel timing failed: {e}")
-        out["roofline"] = None
-    out["step_roofline"] = step_roofline(args.workload, pre_ms, dec_ms)
+        res["roofline"] = None
+    res["step_roofline"] = step_roofline(workload, pre_ms, dec_ms)
+    if workload in ("prefill_8x4096", "prefill_packed_ragged"):
+        M = int(sum(r.lens)) if r.lens is not None else batch * T
+        del r
+        torch.cuda.empty_cache()
+        res["gemm_rooflines"] = gemm_rooflines(torch, B, dm, M, max(args.kernel_iters // 4, 20), use_graph)
+    else:
+        del r
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "the hot path runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+    import torch
+    from decoder_only_transformer_qwen3_amd import binding as B
+    from decoder_only_transformer_qwen3_amd import device as dev
+    from decoder_only_transformer_qwen3_amd import inputs as I
+
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        x = torch.empty(1 << 28, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": 4 << 28, "bytes_written": 4 << 28,
+                          "launches": 3}), flush=True)
+        return
+    bits = I.model_weights(0)
+    dm = dev.DeviceModel(bits)
+    if args.kernel_only:
+        batch, T, steps, _ = WORKLOADS[args.workload]
+        sample = None
+        r = Runner(torch, B, dev, dm, batch, T, steps, args.eos_id, sample)
+        # no prefill ran: give the layer-0 cache the attention kernels read
+        # N(0, 1) values, as a prefill would leave there (all-zero keys would
+        # time a different, lower-power instruction stream)
+        gen = torch.Generator(device="cuda").manual_seed(5)
+        for c in (r.kv.k[0], r.kv.v[0]):
+            c.copy_(torch.randn(c.shape, device="cuda", generator=gen).to(torch.bfloat16))
+        if args.kernel_only == "gemm":
+            M = batch * T if T else int(sum(r.lens))
+            del r
+            rl = gemm_rooflines(torch, B, dm, M, args.kernel_iters, not args.no_graph)
+            print(json.dumps({"workload": args.workload, "gemm_rooflines": rl}), flush=True)
+            return
+        rl = dominant_kernel(torch, B, dev, dm, r, args.workload, args.kernel_iters, not args.no_graph)
+        rl["source_sha256"] = kernel_source_digest(args.workload)
+        print(json.dumps({"workload": args.workload, "roofline": rl}), flush=True)
+        return
+
+    res = run_workload(args, args.workload, torch, B, dev, dm)
+    out = {
+        "metric": METRIC, "value": res["value"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (random-init weights N(0,0.02), uniform random token ids)",
+    }
+    out.update({k: v for k, v in res.items() if k not in ("value", "ms_per_step")})
+    extra = None
+    if args.workload == "prefill_8x4096" and not args.no_decode_extra and args.sample is None \
+            and args.eos_id is None:
+        extra = run_workload(args, "decode_b32_ctx2048", torch, B, dev, dm)
+        out["decode_b32_ctx2048"] = {k: extra[k] for k in ("value", "ms_per_step", "decode_ms", "decode_tok_s",
+                                                          "roofline", "step_roofline", "config")}
     if not args.no_cpu_baseline:
+        import oracle as O
         log("[bench] timing the float64 oracle on the host")
-        out["cpu_baseline"] = cpu_baseline(args.workload, bits)
+        om = O.Model(bits)
+        out["cpu_baseline"] = cpu_baseline(args.workload, bits, om)
+        if extra is not None:
+            out["decode_b32_ctx2048"]["cpu_baseline"] = cpu_baseline("decode_b32_ctx2048", bits, om)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

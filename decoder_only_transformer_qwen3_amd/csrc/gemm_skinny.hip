@@ -371,10 +371,6 @@ void launch_gemv_resid(const uint16_t* X, const uint16_t* W, int K, float* resid
   else launch_gemv_mr<8>(X, W, K, resid, M, gamma, hg, ssq_out, s);
 }
 
-#ifndef Q3_PARTIAL_RB
-#define Q3_PARTIAL_RB(epi) 1
-#endif
-
 template <int NB, int RB, int EPI, int WV, int U>
 static void launch_k(const SkinnyArgs& a, int gx, int n_split, hipStream_t s) {
   hipLaunchKernelGGL((k_gemm_skinny<NB, RB, EPI, U, WV>), dim3(gx, n_split), dim3(64 * WV), 0, s, a);
@@ -424,7 +420,7 @@ static int rows_blocks(const SkinnyArgs& a, Epi epi) {
   if (a.M < 16) return 1;
   if (epi == EPI_SILU) return 2;
   if (a.N >= 16384) return 4;
-  return Q3_PARTIAL_RB(epi);
+  return 1;
 }
 
 template <int NB, int EPI>

@@ -48,26 +48,47 @@ class GreedyReport:
     def __init__(self):
         self.steps = 0
         self.near_ties = 0
+        self.ties = []          # (step, gpu token, oracle token, oracle gap, 2 * max logit error)
         self.strict_prefix = None
         self.max_rel = 0.0
 
     def __repr__(self):
         return (f"steps={self.steps} near_ties={self.near_ties} strict_prefix={self.strict_prefix} "
-                f"max_rel={self.max_rel:.3e}")
+                f"max_rel={self.max_rel:.3e} ties={self.ties}")
 
 
 def check_greedy_step(rep: GreedyReport, gpu_token: int, gpu_logits: np.ndarray, oracle_logits: np.ndarray):
     """The GPU token must equal the oracle's argmax, except at a near tie:
-    logit_o[top] - logit_o[gpu] <= 2 * max_v |logit_gpu[v] - logit_o[v]|."""
+    logit_o[top] - logit_o[gpu] <= 2 * max_v |logit_gpu[v] - logit_o[v]|.
+    Near ties are recorded with their gap; the tests assert that their
+    fixed seeds meet none."""
     err = float(np.max(np.abs(gpu_logits.astype(np.float64) - oracle_logits)))
     rel = err / float(np.max(np.abs(oracle_logits)))
     rep.max_rel = max(rep.max_rel, rel)
     assert rel <= REL_TOL, f"step {rep.steps}: logits rel err {rel:.3e}"
     top = int(O.argmax_lowest(oracle_logits)[0])
     if gpu_token != top:
-        gap = oracle_logits[top] - oracle_logits[gpu_token]
+        gap = float(oracle_logits[top] - oracle_logits[gpu_token])
         assert gap <= 2 * err, f"step {rep.steps}: token {gpu_token} vs oracle {top}, gap {gap:.4g} > 2*err {2*err:.4g}"
         rep.near_ties += 1
+        rep.ties.append((rep.steps, gpu_token, top, round(gap, 6), round(2 * err, 6)))
+        log(f"   near tie at step {rep.steps}: gpu {gpu_token}, oracle {top}, oracle gap {gap:.3e}, "
+            f"2 * max logit error {2 * err:.3e}")
         if rep.strict_prefix is None:
             rep.strict_prefix = rep.steps
     rep.steps += 1
+
+
+def oracle_prefill_logged(om, ids, max_seq=None, tag="oracle"):
+    """O.prefill (embed, the layers in order, final logits), one log line per
+    few layers so a long float64 run shows its progress."""
+    ids = np.asarray(ids)
+    b_sz, t_len = ids.shape
+    cache = O.KVCache(om.cfg, len(om.layers), b_sz, max_seq or t_len)
+    x = O.embed(om, ids)
+    for li, w in enumerate(om.layers):
+        x = O.layer_forward(w, x, cache.k[li], cache.v[li], 0, om.cfg)
+        if li % 7 == 6:
+            log(f"   [{tag}] {t_len}-token prefill: layer {li + 1}/{len(om.layers)}")
+    logits = O.final_logits(om, x[:, -1, :])
+    return logits, O.argmax_lowest(logits), cache

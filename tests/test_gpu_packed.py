@@ -62,6 +62,7 @@ def test_packed_prefill_matches_each_sequence_alone(setup, lens):
             log(f"[packed] sequence {s}: last-layer K rows rel err {e:.2e}")
             assert e <= REL_TOL
     log(f"[packed] lengths {lens}: {rep}")
+    assert rep.near_ties == 0, rep
 
 
 def test_packed_chunked_continuation(setup):
@@ -79,3 +80,4 @@ def test_packed_chunked_continuation(setup):
         o_logits, _, _, _ = O.prefill(om, full[s][None, :])
         check_greedy_step(rep, int(nxt[s]), logits[s], o_logits[0])
     log(f"[packed] chunked continuation: {rep}")
+    assert rep.near_ties == 0, rep

@@ -90,6 +90,7 @@ def test_interleaved_rope_model_prefill_and_greedy_steps(lib):
     _, h_logits = O.generate_cached(O.Model(bits), ids, 1)
     assert np.max(np.abs(h_logits[0] - o_logits[0])) > 20 * np.max(np.abs(lgs[0] - o_logits[0]))
     log(f"[variant] greedy report: {rep}")
+    assert rep.near_ties == 0, rep
 
 
 def _expected_with_eos(gen, eos):
@@ -164,7 +165,7 @@ def test_eos_done_mask_in_a_captured_decode_loop(lib):
             g.replay()
             torch.cuda.synchronize()
             got = np.stack([o.cpu().numpy() for o in outs]).astype(np.int64)
-            np.testing.assert_array_equal(got, exp_tok)
+            assert np.array_equal(got, exp_tok), f"eos {eos}, replay {rep}:\n{got.T}\nwant\n{exp_tok.T}"
             np.testing.assert_array_equal(seq.cpu().numpy(), T + exp_len)
             del junk
         log(f"[eos] eos={eos}: stops after {exp_len.tolist()} steps, replays agree")
@@ -189,3 +190,8 @@ def test_eos_done_mask_in_a_captured_decode_loop(lib):
         torch.cuda.synchronize()
         check_greedy_step(rep, int(n1.item()), logits.cpu().numpy()[0], o_logits[i])
     log(f"[eos] sequence 1 up to its stop vs the oracle: {rep}")
+    # One stated deviation on this seed: at step 3 the float64 oracle's two
+    # best tokens are 3.4e-3 apart, below the bf16 path's logit error
+    # (1.8e-2), and the GPU takes the runner-up.  Any other near tie fails.
+    assert [(t[0], t[1], t[2]) for t in rep.ties] == [(3, 87145, 110127)], rep
+    assert rep.ties[0][3] < 5e-3, rep
