@@ -22,7 +22,8 @@ INTER, VOCAB, N_LAYERS, MAX_POS = 3072, 151936, 28, 40960
 QKV_ROWS, GATE_UP_ROWS = 4096, 6144
 
 Q3_OK, Q3_ERR_NULL, Q3_ERR_SHAPE, Q3_ERR_POSITION = 0, -1, -2, -3
-Q3_ERR_ALIGN, Q3_ERR_WORKSPACE, Q3_ERR_HIP = -4, -5, -6
+Q3_ERR_ALIGN, Q3_ERR_WORKSPACE, Q3_ERR_HIP, Q3_ERR_TOO_LARGE = -4, -5, -6, -7
+NOALLOC_MAX_BYTES = 40 << 20
 
 _vp = ctypes.c_void_p
 
@@ -73,6 +74,8 @@ _decode_eos = _sig("q3_decode_step_eos", ctypes.c_int, ctypes.POINTER(q3_model),
 _sample = _sig("q3_sample", ctypes.c_int, _vp, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
 _wsb_sample = _sig("q3_sample_workspace_bytes", _sz, _i32, _i32)
 _wsb_packed = _sig("q3_workspace_bytes_packed", _sz, _i32, _i32)
+_decode_noalloc = _sig("q3_decode_step_noalloc", ctypes.c_int, ctypes.POINTER(q3_model), ctypes.POINTER(q3_kv), _i32,
+                       _vp, _vp, _i32, _i32, _vp, _vp, _vp)
 _prefill_packed = _sig("q3_prefill_packed", ctypes.c_int, ctypes.POINTER(q3_model), ctypes.POINTER(q3_kv), _i32, _i32,
                        _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp)
 
@@ -81,7 +84,8 @@ Q3_EPI_STORE_BF16, Q3_EPI_STORE_F32, Q3_EPI_ADD_F32, Q3_EPI_SILU_GATE = 0, 1, 2,
 EXPORTS = ("q3_status_str", "q3_rope_table_host", "q3_workspace_bytes", "q3_layer_forward",
            "q3_prefill", "q3_decode_step", "q3_argmax", "q3_linear", "q3_attention_prefill",
            "q3_attention_decode", "q3_attention_decode_warm", "q3_rope_interleaved_to_half", "q3_decode_step_eos",
-           "q3_sample", "q3_sample_workspace_bytes", "q3_workspace_bytes_packed", "q3_prefill_packed")
+           "q3_sample", "q3_sample_workspace_bytes", "q3_workspace_bytes_packed", "q3_prefill_packed",
+           "q3_decode_step_noalloc")
 
 
 class Q3Error(RuntimeError):
@@ -246,4 +250,13 @@ def q3_prefill_packed(m: q3_model, kv: q3_kv, n_seqs, n_tokens, ids, cu_seqlens,
                          _ptr(ws), ws_bytes, _stream(stream))
     if check:
         _check(st, "q3_prefill_packed")
+    return st
+
+
+def q3_decode_step_noalloc(m: q3_model, kv: q3_kv, batch, in_ids, seq_lens, max_len_hint, eos_id, logits, out_ids,
+                           stream=None, check=True) -> int:
+    st = _decode_noalloc(ctypes.byref(m), ctypes.byref(kv), batch, _ptr(in_ids), _ptr(seq_lens), max_len_hint, eos_id,
+                         _ptr(logits), _ptr(out_ids), _stream(stream))
+    if check:
+        _check(st, "q3_decode_step_noalloc")
     return st

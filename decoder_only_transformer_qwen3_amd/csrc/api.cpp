@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/q3.h"
 #include "common.hpp"
 #include "launch.hpp"
@@ -262,6 +264,36 @@ inline uint16_t* layer_cache(void* base, int layer, const q3_kv* kv) {
 
 }  // namespace
 
+// Scratch of q3_decode_step_noalloc: the decode step's workspace for up to
+// Q3_NOALLOC_MAX_BYTES, one copy per GPU the library runs on, held until the
+// process ends.  Host code never passes `scratch` itself to a kernel (its
+// host-side name is not a device address): each device's address is looked
+// up once with hipGetSymbolAddress and kept in noalloc_ptr.
+static __device__ __align__(256) unsigned char scratch[Q3_NOALLOC_MAX_BYTES];
+
+namespace {
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex noalloc_mu;
+void* noalloc_ptr[NOALLOC_MAX_DEVICES];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device, with that device current).
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) return Q3_ERR_HIP;
+  std::lock_guard<std::mutex> lock(noalloc_mu);
+  if (!noalloc_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return Q3_ERR_HIP;
+    noalloc_ptr[dev] = p;
+  }
+  *out = noalloc_ptr[dev];
+  return Q3_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* q3_status_str(int status) {
@@ -273,6 +305,7 @@ const char* q3_status_str(int status) {
     case Q3_ERR_ALIGN: return "a pointer is not suitably aligned";
     case Q3_ERR_WORKSPACE: return "workspace smaller than q3_workspace_bytes()";
     case Q3_ERR_HIP: return "a HIP kernel launch failed";
+    case Q3_ERR_TOO_LARGE: return "the call needs more than the fixed scratch of the no-allocation entry point";
     default: return "unknown status";
   }
 }
@@ -468,6 +501,25 @@ int q3_decode_step(const q3_model* m, const q3_kv* kv, int32_t batch, const int3
                    int32_t max_len_hint, float* logits, int32_t* out_ids, void* ws, size_t ws_bytes, void* stream) {
   return q3_decode_step_eos(m, kv, batch, in_ids, seq_lens, max_len_hint, -1, logits, out_ids, ws, ws_bytes,
                             stream);
+}
+
+int q3_decode_step_noalloc(const q3_model* m, const q3_kv* kv, int32_t batch, const int32_t* in_ids,
+                           int32_t* seq_lens, int32_t max_len_hint, int32_t eos_id, float* logits, int32_t* out_ids,
+                           void* stream) {
+  if (batch >= 1 && q3_workspace_bytes(batch, 1) > (size_t)Q3_NOALLOC_MAX_BYTES) return Q3_ERR_TOO_LARGE;
+  const size_t need = batch >= 1 ? q3_workspace_bytes(batch, 1) : 0;
+  // every other argument is validated before the scratch is looked up (the
+  // workspace check is the scratch's own, just passed above)
+  int st = q3v::check_decode_call(m, kv, batch, in_ids, seq_lens, max_len_hint, logits, out_ids,
+                                  reinterpret_cast<const void*>((uintptr_t)256), need);
+  if (st == Q3_OK && (eos_id < -1 || eos_id >= Q3_VOCAB)) st = Q3_ERR_SHAPE;
+  if (st != Q3_OK) return st;
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != Q3_OK) return st;
+  // the kernel chain clears the tickets it uses (first kernel of the step), so
+  // whatever an earlier call left in the scratch is never read
+  return q3_decode_step_eos(m, kv, batch, in_ids, seq_lens, max_len_hint, eos_id, logits, out_ids, ws, need, stream);
 }
 
 int q3_linear(const void* x, const void* w, void* out, int32_t m, int32_t n, int32_t k, int32_t ldo, int32_t epilogue,

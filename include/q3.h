@@ -65,7 +65,8 @@ enum {
   Q3_ERR_POSITION = -3,  /* positions exceed the cache capacity or 40960 */
   Q3_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned */
   Q3_ERR_WORKSPACE = -5, /* workspace smaller than q3_workspace_bytes() */
-  Q3_ERR_HIP = -6        /* a kernel launch failed (hipGetLastError) */
+  Q3_ERR_HIP = -6,       /* a kernel launch failed (hipGetLastError) */
+  Q3_ERR_TOO_LARGE = -7  /* q3_decode_step_noalloc: batch beyond its fixed scratch */
 };
 
 /* One decoder layer ("手写Qwen3-0.6B推理" §打印模型结构 lists the tensors;
@@ -235,6 +236,25 @@ int q3_decode_step(const q3_model *m, const q3_kv *kv, int32_t batch, const int3
 int q3_decode_step_eos(const q3_model *m, const q3_kv *kv, int32_t batch, const int32_t *in_ids,
                        int32_t *seq_lens, int32_t max_len_hint, int32_t eos_id, float *logits,
                        int32_t *out_ids, void *ws, size_t ws_bytes, void *stream);
+
+/* q3_decode_step_eos for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same step with the same results, but the workspace is a
+ * fixed scratch array inside the library, one per GPU, held until the
+ * process ends (Q3_NOALLOC_MAX_BYTES, enough for q3_workspace_bytes(batch,
+ * 1) up to batch 32).  The call itself allocates and frees nothing; its
+ * first call on a device looks up that device's scratch address (with the
+ * device current).  The caller still passes inputs and outputs as for
+ * q3_decode_step_eos; `stream` must belong to the current device.  Every
+ * call on one GPU shares that GPU's scratch, so calls that overlap on one
+ * GPU (different streams, different threads) race: order them.  Nothing in
+ * the scratch needs to start at zero (the step clears its own tickets).
+ * Errors: those of q3_decode_step_eos, and Q3_ERR_TOO_LARGE when
+ * q3_workspace_bytes(batch, 1) exceeds Q3_NOALLOC_MAX_BYTES (batch > 32). */
+#define Q3_NOALLOC_MAX_BYTES (40u << 20)
+int q3_decode_step_noalloc(const q3_model *m, const q3_kv *kv, int32_t batch, const int32_t *in_ids,
+                           int32_t *seq_lens, int32_t max_len_hint, int32_t eos_id, float *logits,
+                           int32_t *out_ids, void *stream);
 
 /* Row-wise greedy argmax ("手写Qwen3-0.6B推理" §推理; "第 3 章" §4.3):
  * out_idx[r] = lowest index v with logits[r*row_stride + v] equal to the

@@ -261,3 +261,14 @@ def test_attention_decode_warm_rejects_partial_or_misaligned_weights(B):
     assert call(0x68000, 0x70000, None, 0x90000) == B.Q3_ERR_NULL
     assert call(None, None, 0x80000, None) == B.Q3_ERR_NULL
     assert call(0x68000, 0x70000, 0x80008, 0x90000) == B.Q3_ERR_ALIGN
+
+
+def test_noalloc_decode_validates_before_touching_the_device(B):
+    """The no-allocation decode step rejects a batch beyond its fixed scratch,
+    and invalid arguments, on the host: no HIP call is made for them."""
+    m, kv = B.q3_model(), B.q3_kv()
+    assert B.q3_decode_step_noalloc(m, kv, 33, 0x1000, 0x2000, 8, -1, None, 0x3000, stream=0,
+                                    check=False) == B.Q3_ERR_TOO_LARGE
+    assert "scratch" in B.q3_status_str(B.Q3_ERR_TOO_LARGE)
+    assert B.q3_decode_step_noalloc(m, kv, 4, 0x1000, 0x2000, 8, -1, None, 0x3000, stream=0,
+                                    check=False) == B.Q3_ERR_NULL
