@@ -22,8 +22,9 @@
 // chunk of the blocked V cache holds for one dim.  O^T += V^T P^T then takes
 // those registers, rounded to bf16, directly as the B operand, and each A
 // operand (8 positions of one dim) is a single 16 B LDS read.
-// K rows are XOR-swizzled in LDS (16 B chunk c of row r at c ^ swz(r)) so
-// the operand reads are free of bank conflicts.
+// K rows are XOR-swizzled in LDS (16 B chunk c of row r at c ^ (r % 16)):
+// an operand read has 16 lanes on 16 different rows of a 16-row group, all
+// reading the same logical chunk, so they hit 16 different bank groups.
 //
 // Softmax works in the log2 domain with the hardware exp2; the running max
 // is raised only when a score exceeds it by more than 8, so most tiles skip
@@ -48,7 +49,7 @@ constexpr int FA_TILE = FA_BK * D;         // bf16 elements of one K or V tile (
 constexpr float FA_RESCALE_SLACK = 8.0f;
 
 // 16 B-chunk swizzle of K row r in LDS
-__device__ __forceinline__ int fa_kswz(int r) { return (r & 3) | ((r >> 1) & 4); }
+__device__ __forceinline__ int fa_kswz(int r) { return r & 15; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
