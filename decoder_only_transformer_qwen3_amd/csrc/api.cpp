@@ -27,7 +27,7 @@ constexpr int GEMV_MAX_ROWS = 8;
 
 struct Ws {
   float* resid;
-  uint16_t *h, *qkv, *qr, *ao, *act, *fh;
+  uint16_t *h, *qkv, *ao, *act, *fh;
   float *part, *tpart, *apart, *logits, *ssq;
   int* tick;  // 64 column-block tickets, then batch * 8 attention tickets
   int n_tick;
@@ -41,7 +41,6 @@ Ws carve_rows(void* base, int32_t batch, int64_t rows, bool one_token) {
   w.resid = reinterpret_cast<float*>(p + L.resid);
   w.h = reinterpret_cast<uint16_t*>(p + L.h);
   w.qkv = reinterpret_cast<uint16_t*>(p + L.qkv);
-  w.qr = reinterpret_cast<uint16_t*>(p + L.qr);
   w.ao = reinterpret_cast<uint16_t*>(p + L.ao);
   w.act = reinterpret_cast<uint16_t*>(p + L.act);
   w.part = reinterpret_cast<float*>(p + L.part);
@@ -183,9 +182,10 @@ void run_layer(const LayerCtx& c) {
                        warm ? w->w_o : nullptr, warm ? w->w_gate_up : nullptr, warm ? w->w_down : nullptr,
                        warm ? next_qkv : nullptr);
   } else {
-    launch_qknorm_rope(c.ws.qkv, U(w->q_norm), U(w->k_norm), c.cos, c.sin, c.ws.qr, c.kl, c.vl, c.sm, c.max_T,
-                       c.max_seq, c.s);
-    launch_attn_prefill(c.ws.qr, c.kl, c.vl, c.ws.ao, c.sm, c.max_T, c.max_seq, c.s);
+    // k norm + RoPE and V into the cache; q is normed and rotated as the attention loads it
+    launch_kv_store(c.ws.qkv, U(w->k_norm), c.cos, c.sin, c.kl, c.vl, c.sm, c.max_T, c.max_seq, c.s);
+    launch_attn_prefill(c.ws.qkv, QKV_N, U(w->q_norm), c.cos, c.sin, c.kl, c.vl, c.ws.ao, c.sm, c.max_T,
+                        c.max_seq, c.s);
   }
   // o_proj + residual, post-attention RMSNorm, gate|up with silu(gate) * up, down + residual
   if (skinny) {
@@ -540,8 +540,8 @@ int q3_attention_prefill(const void* q, const void* k_layer, const void* v_layer
   const int st = q3v::check_attn_prefill_call(q, k_layer, v_layer, batch, n_tokens, start_pos, max_seq, out);
   if (st != Q3_OK) return st;
   const SeqMap sm{nullptr, nullptr, batch, n_tokens, start_pos, batch * n_tokens};
-  launch_attn_prefill(U(q), U(k_layer), U(v_layer), static_cast<uint16_t*>(out), sm, n_tokens, max_seq,
-                      static_cast<hipStream_t>(stream));
+  launch_attn_prefill(U(q), QDIM, nullptr, nullptr, nullptr, U(k_layer), U(v_layer), static_cast<uint16_t*>(out), sm,
+                      n_tokens, max_seq, static_cast<hipStream_t>(stream));
   return launch_status();
 }
 

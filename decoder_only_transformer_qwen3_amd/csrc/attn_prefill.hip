@@ -53,10 +53,11 @@ __device__ __forceinline__ int fa_kswz(int r) { return r & 15; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_prefill(const uint16_t* __restrict__ q,
-                                                         const uint16_t* __restrict__ k_cache,
-                                                         const uint16_t* __restrict__ v_cache,
-                                                         uint16_t* __restrict__ out, SeqMap sm, int max_seq) {
+template <bool QNORM>
+__global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_prefill(
+    const uint16_t* __restrict__ q, int ldq, const uint16_t* __restrict__ q_norm, const float* __restrict__ rope_cos,
+    const float* __restrict__ rope_sin, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
+    uint16_t* __restrict__ out, SeqMap sm, int max_seq) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[FA_NS][2][FA_TILE];
 
   // XCD-aware order: workgroups go round-robin to the 8 XCDs by linear id,
@@ -79,19 +80,10 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int kv_len = start + T;
   const int wg_last = (qt * FA_BQ + FA_BQ - 1) < T ? (qt * FA_BQ + FA_BQ - 1) : T - 1;
   const int n_kt = (start + wg_last) / FA_BK + 1;  // key tiles of the workgroup
+  __builtin_assume(n_kt >= 1);                     // start >= 0 and wg_last >= 0 past the return above
   const int wave_last = (t0 + 31) < T ? (t0 + 31) : T - 1;
   const int wave_kt = t0 < T ? (start + wave_last) / FA_BK + 1 : 0;  // tiles this wave computes
   const int wave_pmin = start + (t0 < T ? t0 : T - 1);
-
-  // ---- Q operand: qreg[s] = dims 16 s + 8 lh .. +7 of query row t0 + lq
-  u32x4 qreg[8];
-  {
-    int tq = t0 + lq;
-    tq = tq < T ? tq : T - 1;
-    const uint16_t* qrow = q + ((size_t)row0 + tq) * QDIM + hq * D + 8 * lh;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qreg[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s);
-  }
 
   const uint16_t* kbase = k_cache + ((size_t)b * HKV + g) * max_seq * D;
   const uint16_t* vbase = v_cache + ((size_t)b * HKV + g) * max_seq * D;
@@ -131,6 +123,75 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int krow = 16 * (lq >> 4) + 8 * ((lq >> 2) & 1) + 4 * ((lq >> 3) & 1) + (lq & 3);
 
   issue(0);
+
+  // ---- Q operand: qreg[s] = dims 16 s + 8 lh .. +7 of query row t0 + lq
+  // (loaded after the first K/V tile's DMA is issued, so the two overlap)
+  u32x4 qreg[8];
+  {
+    int tq = t0 + lq;
+    tq = tq < T ? tq : T - 1;
+    const uint16_t* qrow = q + ((size_t)row0 + tq) * ldq + hq * D + 8 * lh;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qreg[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s);
+    if constexpr (QNORM) {
+      // raw projection: per-head RMSNorm with the q gain, then NeoX RoPE at
+      // position start + tq ("手写Qwen3-0.6B推理" §Attention and §Rope).  The
+      // lane holds 64 of the head's dims, lane l ^ 32 the other 64, and the
+      // RoPE partner of dim d < 64 (qreg[s], s < 4) is d + 64 (qreg[s + 4]).
+      int pc = start + tq;
+      pc = pc < MAXPOS ? pc : MAXPOS - 1;
+      const float* cr = rope_cos + (size_t)pc * ROPE_HALF + 8 * lh;
+      const float* sr = rope_sin + (size_t)pc * ROPE_HALF + 8 * lh;
+      const uint16_t* gq = q_norm + 8 * lh;
+      u32x4 ga[4], gb[4];
+      f32x4 c0[4], c1[4], s0[4], s1[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        ga[s] = *reinterpret_cast<const u32x4*>(gq + 16 * s);
+        gb[s] = *reinterpret_cast<const u32x4*>(gq + 64 + 16 * s);
+        c0[s] = *reinterpret_cast<const f32x4*>(cr + 16 * s);
+        c1[s] = *reinterpret_cast<const f32x4*>(cr + 16 * s + 4);
+        s0[s] = *reinterpret_cast<const f32x4*>(sr + 16 * s);
+        s1[s] = *reinterpret_cast<const f32x4*>(sr + 16 * s + 4);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // all loads in flight before the first wait
+      float ss = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const u32x4 v = qreg[s];
+        ss += bf_lo(v.x) * bf_lo(v.x) + bf_hi(v.x) * bf_hi(v.x) + bf_lo(v.y) * bf_lo(v.y) + bf_hi(v.y) * bf_hi(v.y) +
+              bf_lo(v.z) * bf_lo(v.z) + bf_hi(v.z) * bf_hi(v.z) + bf_lo(v.w) * bf_lo(v.w) + bf_hi(v.w) * bf_hi(v.w);
+      }
+      ss += __shfl_xor(ss, 32, 64);
+      const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + EPS);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 xa = qreg[s], xb = qreg[s + 4];
+        const uint32_t xw[4] = {xa.x, xa.y, xa.z, xa.w}, yw[4] = {xb.x, xb.y, xb.z, xb.w};
+        const uint32_t gaw[4] = {ga[s].x, ga[s].y, ga[s].z, ga[s].w}, gbw[4] = {gb[s].x, gb[s].y, gb[s].z, gb[s].w};
+        const float cs[8] = {c0[s][0], c0[s][1], c0[s][2], c0[s][3], c1[s][0], c1[s][1], c1[s][2], c1[s][3]};
+        const float sn[8] = {s0[s][0], s0[s][1], s0[s][2], s0[s][3], s1[s][0], s1[s][1], s1[s][2], s1[s][3]};
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float o0[2], o1[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float x = h ? bf_hi(xw[e]) : bf_lo(xw[e]), y = h ? bf_hi(yw[e]) : bf_lo(yw[e]);
+            const float a = x * rinv * (h ? bf_hi(gaw[e]) : bf_lo(gaw[e]));
+            const float bb = y * rinv * (h ? bf_hi(gbw[e]) : bf_lo(gbw[e]));
+            o0[h] = a * cs[2 * e + h] - bb * sn[2 * e + h];
+            o1[h] = bb * cs[2 * e + h] + a * sn[2 * e + h];
+          }
+          lo[e] = pack_bf2(o0[0], o0[1]);
+          hi[e] = pack_bf2(o1[0], o1[1]);
+        }
+        qreg[s] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+        qreg[s + 4] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      }
+    }
+  }
+
 
   for (int j = 0; j < n_kt; ++j) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's part of tile j landed
@@ -270,10 +331,16 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   }
 }
 
-void launch_attn_prefill(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out,
+void launch_attn_prefill(const uint16_t* q, int ldq, const uint16_t* q_norm, const float* rope_cos,
+                         const float* rope_sin, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out,
                          const SeqMap& sm, int max_T, int max_seq, hipStream_t s) {
   const dim3 grid(((max_T + FA_BQ - 1) / FA_BQ) * HKV * sm.n);
-  hipLaunchKernelGGL(k_attn_prefill, grid, dim3(256), 0, s, q, k_cache, v_cache, out, sm, max_seq);
+  if (q_norm)
+    hipLaunchKernelGGL(k_attn_prefill<true>, grid, dim3(256), 0, s, q, ldq, q_norm, rope_cos, rope_sin, k_cache,
+                       v_cache, out, sm, max_seq);
+  else
+    hipLaunchKernelGGL(k_attn_prefill<false>, grid, dim3(256), 0, s, q, ldq, q_norm, rope_cos, rope_sin, k_cache,
+                       v_cache, out, sm, max_seq);
 }
 
 }  // namespace q3

@@ -168,118 +168,116 @@ void launch_rmsnorm(float* resid, const float* part, int n_part, int part_rows, 
                      out, n_rows, row_step, row_off);
 }
 
-// ---------------------------------------------------------------- q/k norm + RoPE + KV write
-// Per-head RMSNorm of q and k with a head_dim-long gain shared by all heads
-// ("手写Qwen3-0.6B推理" §Attention, q_norm/k_norm), then NeoX RoPE at the
-// token's absolute position ("手写Qwen3-0.6B推理" §Rope; half-swap pairing
-// per "古法手撕简易LLM推理器" §RoPE的细节):
+// ---------------------------------------------------------------- k norm + RoPE, K/V cache write
+// The new tokens' K and V rows of a multi-token call into the cache.  K gets
+// the per-head RMSNorm with the head_dim-long k_norm gain
+// ("手写Qwen3-0.6B推理" §Attention) and NeoX RoPE at the token's absolute
+// position ("手写Qwen3-0.6B推理" §Rope; half-swap pairing per
+// "古法手撕简易LLM推理器" §RoPE的细节):
 //   y = x / sqrt(mean(x^2) + eps) * gamma
-//   (y_i, y_{i+64}) -> (y_i c - y_{i+64} s, y_{i+64} c + y_i s),  c, s = cos, sin(p * 1e6^(-2i/128)).
-// One wave handles 4 of the 24 q/k heads of one token; 16 lanes per head,
-// lane j holds dims 4j..4j+3 and 64+4j..64+4j+3, so every RoPE pair stays
-// inside the lane and the head's sum of squares is a 16-lane DPP row sum.
-// Rotated K goes to cache row p ("古法手撕简易LLM推理器"
-// §核心计算函数与Transformer层 keeps normed, rotated K in the cache).
-__global__ __launch_bounds__(256) void k_qk_norm_rope(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_norm,
-                                                      const uint16_t* __restrict__ k_norm,
-                                                      const float* __restrict__ rope_cos,
-                                                      const float* __restrict__ rope_sin, uint16_t* __restrict__ q_out,
-                                                      uint16_t* __restrict__ k_cache, SeqMap sm, int max_seq) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * 4 + wave;
-  const int m = gw / 6, hg = gw - m * 6;
-  if (m >= sm.rows) return;
-  const int b = sm_seq(sm, m), t = m - sm_row0(sm, b);
-  const int p = sm_start(sm, b) + t;
-  const int head = hg * 4 + (lane >> 4);  // 0..15 query heads, 16..23 key heads
-  const int j4 = 4 * (lane & 15);
-  const uint16_t* src = qkv + (size_t)m * QKV_N + head * D;
-  const u32x2 lo = *reinterpret_cast<const u32x2*>(src + j4);
-  const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 64 + j4);
-  float x[4] = {bf_lo(lo.x), bf_hi(lo.x), bf_lo(lo.y), bf_hi(lo.y)};
-  float y[4] = {bf_lo(hi.x), bf_hi(hi.x), bf_lo(hi.y), bf_hi(hi.y)};
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) ss += x[i] * x[i] + y[i] * y[i];
-  ss = row16_sum(ss);
-  const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + EPS);
-  const uint16_t* gm = head < HQ ? q_norm : k_norm;
-  const u32x2 g0 = *reinterpret_cast<const u32x2*>(gm + j4);
-  const u32x2 g1 = *reinterpret_cast<const u32x2*>(gm + 64 + j4);
-  const float ga[4] = {bf_lo(g0.x), bf_hi(g0.x), bf_lo(g0.y), bf_hi(g0.y)};
-  const float gb[4] = {bf_lo(g1.x), bf_hi(g1.x), bf_lo(g1.y), bf_hi(g1.y)};
-  const int pc = p < 0 ? 0 : (p >= MAXPOS ? MAXPOS - 1 : p);
-  const f32x4 c = *reinterpret_cast<const f32x4*>(rope_cos + (size_t)pc * ROPE_HALF + j4);
-  const f32x4 sn = *reinterpret_cast<const f32x4*>(rope_sin + (size_t)pc * ROPE_HALF + j4);
-  float o0[4], o1[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float a = x[i] * rinv * ga[i], bb = y[i] * rinv * gb[i];
-    o0[i] = a * c[i] - bb * sn[i];
-    o1[i] = bb * c[i] + a * sn[i];
-  }
-  const u32x2 w0 = {pack_bf2(o0[0], o0[1]), pack_bf2(o0[2], o0[3])};
-  const u32x2 w1 = {pack_bf2(o1[0], o1[1]), pack_bf2(o1[2], o1[3])};
-  uint16_t* dst;
-  if (head < HQ) {
-    dst = q_out + (size_t)m * QDIM + head * D;
-  } else {
-    if (p < 0 || p >= max_seq) return;
-    dst = k_cache + (((size_t)b * HKV + (head - HQ)) * max_seq + p) * D;
-  }
-  *reinterpret_cast<u32x2*>(dst + j4) = w0;
-  *reinterpret_cast<u32x2*>(dst + 64 + j4) = w1;
-}
+//   (y_i, y_{i+64}) -> (y_i c - y_{i+64} s, y_{i+64} c + y_i s),  c, s = cos, sin(p * 1e6^(-2i/128)),
+// and the cache keeps normed, rotated K ("古法手撕简易LLM推理器"
+// §核心计算函数与Transformer层) and raw V.  (q gets the same treatment, with
+// q_norm, where the prefill attention loads it.)
+//
+// One workgroup per (32-position chunk, KV head, sequence); chunks start at
+// multiples of 8 so they hold whole V blocks.  K: 16 lanes per position,
+// lane j holding dims 4j..4j+3 and 64+4j..64+4j+3, so the RoPE pairs stay in
+// the lane and the head's sum of squares is a 16-lane DPP row sum.  V: the
+// chunk's positions are staged in LDS and written to the blocked V cache
+// (8 positions x 128 dims per 2 KB block, dim-major) as position-contiguous
+// 8-byte groups.  Positions of the chunk outside the call's range are left
+// untouched (they may hold earlier tokens).
+constexpr int KVS_POS = 32;  // positions per workgroup
 
-// Raw V of the new tokens into the blocked V cache (8 positions x 128 dims
-// per 2 KB block).  One workgroup per (8-position block, KV head,
-// sequence): the block's tokens are staged in LDS and written back as
-// position-contiguous 8-byte groups; positions outside the call's range are
-// left untouched (they may hold earlier tokens).
-__global__ __launch_bounds__(256) void k_v_store(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ v_cache,
-                                                 SeqMap sm, int max_seq) {
-  __shared__ uint16_t tile[VBLK][D];
+__global__ __launch_bounds__(256) void k_kv_store(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ k_norm,
+                                                  const float* __restrict__ rope_cos,
+                                                  const float* __restrict__ rope_sin, uint16_t* __restrict__ k_cache,
+                                                  uint16_t* __restrict__ v_cache, SeqMap sm, int max_seq) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[KVS_POS][D];
   const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int T = sm_len(sm, b), row0 = sm_row0(sm, b);
   const int p_first = sm_start(sm, b);
-  const int pb = (p_first >> 3) + blockIdx.x;  // position block
-  const int p_lo = p_first > pb * VBLK ? p_first : pb * VBLK;
-  const int p_hi = (p_first + T) < (pb + 1) * VBLK ? (p_first + T) : (pb + 1) * VBLK;
-  if (p_first < 0 || p_lo >= p_hi || pb * VBLK >= max_seq) return;
-  {
-    const int tt = tid >> 5, d4 = 4 * (tid & 31);
-    const int p = pb * VBLK + tt;
-    u32x2 v = {0u, 0u};
-    if (p >= p_lo && p < p_hi) {
-      const size_t m = (size_t)row0 + (p - p_first);
-      v = *reinterpret_cast<const u32x2*>(qkv + m * QKV_N + (HQ + HKV) * D + g * D + d4);
+  const int c0 = (p_first & ~7) + KVS_POS * blockIdx.x;  // first position of the chunk
+  const int p_lo = p_first > c0 ? p_first : c0;
+  int p_hi = (p_first + T) < (c0 + KVS_POS) ? (p_first + T) : (c0 + KVS_POS);
+  p_hi = p_hi < max_seq ? p_hi : max_seq;
+  if (p_first < 0 || p_lo >= p_hi) return;  // whole workgroup
+  const size_t kv_base = ((size_t)b * HKV + g) * max_seq * D;
+  // ---- V rows of the chunk into LDS, 16 B per lane (zeros outside the range, never written back)
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int e = it * 256 + tid, r = e >> 4, c8 = 8 * (e & 15);
+    const int p = c0 + r;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (p >= p_lo && p < p_hi)
+      v = *reinterpret_cast<const u32x4*>(qkv + (size_t)(row0 + p - p_first) * QKV_N + (HQ + HKV + g) * D + c8);
+    *reinterpret_cast<u32x4*>(&tile[r][c8]) = v;
+  }
+  // ---- K rows: 16 positions per pass
+#pragma unroll
+  for (int it = 0; it < KVS_POS / 16; ++it) {
+    const int p = c0 + it * 16 + (tid >> 4), j4 = 4 * (tid & 15);
+    const bool live = p >= p_lo && p < p_hi;
+    float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
+    if (live) {
+      const uint16_t* src = qkv + (size_t)(row0 + p - p_first) * QKV_N + (HQ + g) * D;
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(src + j4);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 64 + j4);
+      x[0] = bf_lo(lo.x), x[1] = bf_hi(lo.x), x[2] = bf_lo(lo.y), x[3] = bf_hi(lo.y);
+      y[0] = bf_lo(hi.x), y[1] = bf_hi(hi.x), y[2] = bf_lo(hi.y), y[3] = bf_hi(hi.y);
     }
-    *reinterpret_cast<u32x2*>(&tile[tt][d4]) = v;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ss += x[i] * x[i] + y[i] * y[i];
+    ss = row16_sum(ss);  // the 16 lanes of one position
+    if (live) {
+      const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + EPS);
+      const u32x2 g0 = *reinterpret_cast<const u32x2*>(k_norm + j4);
+      const u32x2 g1 = *reinterpret_cast<const u32x2*>(k_norm + 64 + j4);
+      const float ga[4] = {bf_lo(g0.x), bf_hi(g0.x), bf_lo(g0.y), bf_hi(g0.y)};
+      const float gb[4] = {bf_lo(g1.x), bf_hi(g1.x), bf_lo(g1.y), bf_hi(g1.y)};
+      const int pc = p >= MAXPOS ? MAXPOS - 1 : p;
+      const f32x4 c = *reinterpret_cast<const f32x4*>(rope_cos + (size_t)pc * ROPE_HALF + j4);
+      const f32x4 sn = *reinterpret_cast<const f32x4*>(rope_sin + (size_t)pc * ROPE_HALF + j4);
+      float o0[4], o1[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = x[i] * rinv * ga[i], bb = y[i] * rinv * gb[i];
+        o0[i] = a * c[i] - bb * sn[i];
+        o1[i] = bb * c[i] + a * sn[i];
+      }
+      uint16_t* dst = k_cache + kv_base + (size_t)p * D;
+      *reinterpret_cast<u32x2*>(dst + j4) = u32x2{pack_bf2(o0[0], o0[1]), pack_bf2(o0[2], o0[3])};
+      *reinterpret_cast<u32x2*>(dst + 64 + j4) = u32x2{pack_bf2(o1[0], o1[1]), pack_bf2(o1[2], o1[3])};
+    }
   }
   __syncthreads();
+  // ---- V blocks: thread (d, half) writes 4 positions of dim d of each block
   const int d = tid >> 1, h4 = 4 * (tid & 1);
-  uint16_t* dst = v_cache + ((size_t)b * HKV + g) * max_seq * D + ((size_t)pb * D + d) * VBLK + h4;
-  const int q0 = pb * VBLK + h4;
-  if (q0 >= p_lo && q0 + 4 <= p_hi) {
-    const u32x2 w = {(uint32_t)tile[h4][d] | ((uint32_t)tile[h4 + 1][d] << 16),
-                     (uint32_t)tile[h4 + 2][d] | ((uint32_t)tile[h4 + 3][d] << 16)};
-    *reinterpret_cast<u32x2*>(dst) = w;
-  } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (q0 + i >= p_lo && q0 + i < p_hi) dst[i] = tile[h4 + i][d];
+  for (int blk = 0; blk < KVS_POS / VBLK; ++blk) {
+    const int q0 = c0 + blk * VBLK + h4, r0 = blk * VBLK + h4;
+    uint16_t* dst = v_cache + kv_base + ((size_t)((c0 >> 3) + blk) * D + d) * VBLK + h4;
+    if (q0 >= p_lo && q0 + 4 <= p_hi) {
+      const u32x2 w = {(uint32_t)tile[r0][d] | ((uint32_t)tile[r0 + 1][d] << 16),
+                       (uint32_t)tile[r0 + 2][d] | ((uint32_t)tile[r0 + 3][d] << 16)};
+      *reinterpret_cast<u32x2*>(dst) = w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (q0 + i >= p_lo && q0 + i < p_hi) dst[i] = tile[r0 + i][d];
+    }
   }
 }
 
-void launch_qknorm_rope(const uint16_t* qkv, const uint16_t* q_norm, const uint16_t* k_norm,
-                        const float* rope_cos, const float* rope_sin, uint16_t* q_out, uint16_t* k_cache,
-                        uint16_t* v_cache, const SeqMap& sm, int max_T, int max_seq, hipStream_t s) {
-  const int waves = sm.rows * 6;
-  hipLaunchKernelGGL(k_qk_norm_rope, dim3((waves + 3) / 4), dim3(256), 0, s, qkv, q_norm, k_norm, rope_cos, rope_sin,
-                     q_out, k_cache, sm, max_seq);
-  // an unaligned run of up to max_T positions touches at most max_T/8 + 2 blocks
-  const int nblk = max_T / VBLK + 2;
-  hipLaunchKernelGGL(k_v_store, dim3(nblk, HKV, sm.n), dim3(256), 0, s, qkv, v_cache, sm, max_seq);
+void launch_kv_store(const uint16_t* qkv, const uint16_t* k_norm, const float* rope_cos, const float* rope_sin,
+                     uint16_t* k_cache, uint16_t* v_cache, const SeqMap& sm, int max_T, int max_seq, hipStream_t s) {
+  // a run of up to max_T positions from an unaligned start spans at most max_T + 7 positions
+  // from the 8-aligned position below its start
+  const int n_chunks = (max_T + 7 + KVS_POS - 1) / KVS_POS;
+  hipLaunchKernelGGL(k_kv_store, dim3(n_chunks, HKV, sm.n), dim3(256), 0, s, qkv, k_norm, rope_cos, rope_sin, k_cache,
+                     v_cache, sm, max_seq);
 }
 
 // ---------------------------------------------------------------- argmax

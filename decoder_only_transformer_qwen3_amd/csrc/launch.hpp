@@ -38,12 +38,11 @@ void launch_norm_operand(const float* resid, int n_rows, int row_step, int row_o
 void launch_rmsnorm(float* resid, const float* part, int n_part, int part_rows, const uint16_t* gamma,
                     uint16_t* out, int n_rows, int row_step, int row_off, hipStream_t s);
 
-// Per-head q/k RMSNorm + NeoX RoPE + KV-cache write for the sm.rows rows of
-// the merged qkv projection, each at its sequence and position (SeqMap);
-// max_T bounds the rows of one sequence.
-void launch_qknorm_rope(const uint16_t* qkv, const uint16_t* q_norm, const uint16_t* k_norm,
-                        const float* rope_cos, const float* rope_sin, uint16_t* q_out, uint16_t* k_cache,
-                        uint16_t* v_cache, const SeqMap& sm, int max_T, int max_seq, hipStream_t s);
+// K rows (per-head k RMSNorm + NeoX RoPE) and raw V rows of the merged qkv
+// projection [rows][4096] into the cache, each row at its sequence and
+// position (SeqMap); max_T bounds the rows of one sequence.
+void launch_kv_store(const uint16_t* qkv, const uint16_t* k_norm, const float* rope_cos, const float* rope_sin,
+                     uint16_t* k_cache, uint16_t* v_cache, const SeqMap& sm, int max_T, int max_seq, hipStream_t s);
 
 // MFMA tiled GEMM, out = X[M,K] * W[N,K]^T with the chosen epilogue.
 // Requires N % 128 == 0 (EPI_SILU: N = 2*ldo-columns, (N/2) % 64 == 0), K % 64 == 0.
@@ -103,8 +102,11 @@ void launch_sample(const float* logits, int rows, int vocab, int64_t stride, con
 
 // Causal GQA flash attention over the cache for the rows of a multi-token
 // call: the rows of sequence s at positions start_s .. start_s + T_s - 1
-// (SeqMap); max_T bounds T_s.
-void launch_attn_prefill(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out,
+// (SeqMap); max_T bounds T_s.  Query row m is q + m * ldq (16 heads of 128).
+// With q_norm, the query rows are the raw projection: each head gets the
+// q RMSNorm and NeoX RoPE at its position as it is loaded.
+void launch_attn_prefill(const uint16_t* q, int ldq, const uint16_t* q_norm, const float* rope_cos,
+                         const float* rope_sin, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out,
                          const SeqMap& sm, int max_T, int max_seq, hipStream_t s);
 
 // Split-K decode attention for one new token per sequence, from the raw

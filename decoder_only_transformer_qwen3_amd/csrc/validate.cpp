@@ -28,7 +28,6 @@ WsLayout ws_layout_rows(int32_t batch, int64_t rows, bool one_token) {
   L.resid = take(M * Q3_HIDDEN * 4);
   L.h = take(M * Q3_HIDDEN * 2);
   L.qkv = take(M * Q3_QKV_ROWS * 2);
-  L.qr = take(M * Q3_N_HEADS * Q3_HEAD_DIM * 2);
   L.ao = take(M * Q3_N_HEADS * Q3_HEAD_DIM * 2);
   L.act = take(M * Q3_INTER * 2);
   L.part = take(M <= (size_t)SKINNY_MAX_ROWS ? (size_t)PART_MAX_SPLIT * M * Q3_HIDDEN * 4 : 0);

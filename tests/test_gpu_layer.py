@@ -104,6 +104,8 @@ def run_layer_case(lib, layer0, rope, batch, T, start, max_seq, check_seqs=None,
     (97, 2, 10, 16),      # 194 rows over 97 sequences: two row tiles, K split
     (1, 1, 40959, 40960), # decode at the last position of the rotary table
     (1, 64, 40896, 40960),  # a prefill chunk ending at the position limit
+    (3, 777, 100, 896),   # 2331 rows at an offset: the persistent GEMMs, q/k norm + RoPE in the
+                          # q|k|v epilogue, a ragged last row tile of 27 rows
 ])
 def test_layer_forward_parity(lib, layer0, rope, batch, T, start, max_seq):
     run_layer_case(lib, layer0, rope, batch, T, start, max_seq)

@@ -1,7 +1,8 @@
 """GPU parity of q3_prefill_packed: ragged prompts packed into one token
 array (the engine layout "第 3 章" §3.1 describes, logits only at each
 sequence's last position, §4.1), against the oracle run on each sequence
-alone.  Covers the tiled-GEMM row counts, the skinny ones, query blocks
+alone.  Covers the tiled-GEMM row counts, the skinny ones, the persistent
+GEMMs (over 2048 rows, q/k norm + RoPE in the q|k|v epilogue), query blocks
 that straddle sequences, and a chunked continuation (start positions > 0)."""
 import numpy as np
 import pytest
@@ -45,6 +46,7 @@ def _packed_call(B, dev, dm, kv, seqs, starts=None):
 @pytest.mark.parametrize("lens", [
     [1, 7, 64, 130, 300],   # 502 rows: tiled GEMMs; query blocks of 64 cross every sequence boundary
     [3, 1, 9],              # 13 rows: skinny GEMMs
+    [1100, 3, 950],         # 2053 rows: persistent GEMMs, q/k norm + RoPE through the row map
 ])
 def test_packed_prefill_matches_each_sequence_alone(setup, lens):
     B, dev, dm, om = setup
