@@ -64,6 +64,8 @@ _decode = _sig("q3_decode_step", ctypes.c_int, ctypes.POINTER(q3_model), ctypes.
 _argmax = _sig("q3_argmax", ctypes.c_int, _vp, _i32, _i32, _i64, _vp, _vp)
 _linear = _sig("q3_linear", ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp)
 _attn_prefill = _sig("q3_attention_prefill", ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp)
+_attn_prefill_qkv = _sig("q3_attention_prefill_qkv", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                         _i32, _i32, _i32, _vp, _vp)
 _attn_decode = _sig("q3_attention_decode", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
                     _i32, _vp, _vp, _sz, _vp)
 _attn_decode_warm = _sig("q3_attention_decode_warm", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
@@ -85,7 +87,7 @@ EXPORTS = ("q3_status_str", "q3_rope_table_host", "q3_workspace_bytes", "q3_laye
            "q3_prefill", "q3_decode_step", "q3_argmax", "q3_linear", "q3_attention_prefill",
            "q3_attention_decode", "q3_attention_decode_warm", "q3_rope_interleaved_to_half", "q3_decode_step_eos",
            "q3_sample", "q3_sample_workspace_bytes", "q3_workspace_bytes_packed", "q3_prefill_packed",
-           "q3_decode_step_noalloc")
+           "q3_decode_step_noalloc", "q3_attention_prefill_qkv")
 
 
 class Q3Error(RuntimeError):
@@ -184,6 +186,16 @@ def q3_attention_prefill(q, k_layer, v_layer, batch, n_tokens, start_pos, max_se
                        _stream(stream))
     if check:
         _check(st, "q3_attention_prefill")
+    return st
+
+
+def q3_attention_prefill_qkv(qkv, q_norm, k_norm, rope_cos, rope_sin, k_layer, v_layer, batch, n_tokens, start_pos,
+                             max_seq, write_kv, out, stream=None, check=True) -> int:
+    st = _attn_prefill_qkv(_ptr(qkv), _ptr(q_norm), _ptr(k_norm), _ptr(rope_cos), _ptr(rope_sin), _ptr(k_layer),
+                           _ptr(v_layer), batch, n_tokens, start_pos, max_seq, int(write_kv), _ptr(out),
+                           _stream(stream))
+    if check:
+        _check(st, "q3_attention_prefill_qkv")
     return st
 
 

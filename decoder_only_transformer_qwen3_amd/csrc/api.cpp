@@ -545,6 +545,22 @@ int q3_attention_prefill(const void* q, const void* k_layer, const void* v_layer
   return launch_status();
 }
 
+int q3_attention_prefill_qkv(const void* qkv, const void* q_norm, const void* k_norm, const float* rope_cos,
+                             const float* rope_sin, void* k_layer, void* v_layer, int32_t batch, int32_t n_tokens,
+                             int32_t start_pos, int32_t max_seq, int32_t write_kv, void* out, void* stream) {
+  const int st = q3v::check_attn_prefill_qkv_call(qkv, q_norm, k_norm, rope_cos, rope_sin, k_layer, v_layer, batch,
+                                                  n_tokens, start_pos, max_seq, write_kv, out);
+  if (st != Q3_OK) return st;
+  const SeqMap sm{nullptr, nullptr, batch, n_tokens, start_pos, batch * n_tokens};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* kl = static_cast<uint16_t*>(k_layer);
+  uint16_t* vl = static_cast<uint16_t*>(v_layer);
+  if (write_kv) launch_kv_store(U(qkv), U(k_norm), rope_cos, rope_sin, kl, vl, sm, n_tokens, max_seq, s);
+  launch_attn_prefill(U(qkv), QKV_N, U(q_norm), rope_cos, rope_sin, kl, vl, static_cast<uint16_t*>(out), sm, n_tokens,
+                      max_seq, s);
+  return launch_status();
+}
+
 int q3_attention_decode_warm(const void* qkv, const void* q_norm, const void* k_norm, const float* rope_cos,
                              const float* rope_sin, void* k_layer, void* v_layer, int32_t batch, int32_t max_seq,
                              const int32_t* positions, int32_t max_len_hint, void* out, void* ws, size_t ws_bytes,

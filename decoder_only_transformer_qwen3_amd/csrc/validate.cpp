@@ -230,6 +230,18 @@ int check_attn_prefill_call(const void* q, const void* k_layer, const void* v_la
   return Q3_OK;
 }
 
+int check_attn_prefill_qkv_call(const void* qkv, const void* q_norm, const void* k_norm, const float* rope_cos,
+                                const float* rope_sin, const void* k_layer, const void* v_layer, int32_t batch,
+                                int32_t n_tokens, int32_t start_pos, int32_t max_seq, int32_t write_kv,
+                                const void* out) {
+  if (!q_norm || !k_norm || !rope_cos || !rope_sin) return Q3_ERR_NULL;
+  const int st = check_attn_prefill_call(qkv, k_layer, v_layer, batch, n_tokens, start_pos, max_seq, out);
+  if (st != Q3_OK) return st;
+  if (write_kv != 0 && write_kv != 1) return Q3_ERR_SHAPE;
+  if (!al16(q_norm) || !al16(k_norm) || !al16(rope_cos) || !al16(rope_sin)) return Q3_ERR_ALIGN;
+  return Q3_OK;
+}
+
 int check_attn_decode_call(const void* qkv, const void* q_norm, const void* k_norm, const float* rope_cos,
                            const float* rope_sin, const void* k_layer, const void* v_layer, int32_t batch,
                            int32_t max_seq, const int32_t* positions, int32_t max_len_hint, const void* out,

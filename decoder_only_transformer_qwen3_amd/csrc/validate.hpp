@@ -112,6 +112,10 @@ int check_linear_call(const void* x, const void* w, const void* out, int32_t m, 
 
 int check_attn_prefill_call(const void* q, const void* k_layer, const void* v_layer, int32_t batch, int32_t n_tokens,
                             int32_t start_pos, int32_t max_seq, const void* out);
+int check_attn_prefill_qkv_call(const void* qkv, const void* q_norm, const void* k_norm, const float* rope_cos,
+                                const float* rope_sin, const void* k_layer, const void* v_layer, int32_t batch,
+                                int32_t n_tokens, int32_t start_pos, int32_t max_seq, int32_t write_kv,
+                                const void* out);
 
 int check_attn_decode_call(const void* qkv, const void* q_norm, const void* k_norm, const float* rope_cos,
                            const float* rope_sin, const void* k_layer, const void* v_layer, int32_t batch,

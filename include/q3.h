@@ -339,6 +339,28 @@ int q3_linear(const void *x, const void *w, void *out, int32_t m, int32_t n, int
 int q3_attention_prefill(const void *q, const void *k_layer, const void *v_layer, int32_t batch,
                          int32_t n_tokens, int32_t start_pos, int32_t max_seq, void *out, void *stream);
 
+/* Helper: the attention half of a multi-token call as q3_layer_forward and
+ * q3_prefill run it ("古法手撕简易LLM推理器" §prefill与predict): for a chunk
+ * of n_tokens rows per sequence at positions p = start_pos .. start_pos +
+ * n_tokens - 1, from the raw projection rows, the per-head k RMSNorm and
+ * RoPE at p write the rotated K and the raw V into cache row p, then each
+ * query head gets the q RMSNorm and RoPE at its position as the attention
+ * loads it, and attends over rows 0..p as in q3_attention_prefill.
+ *   qkv       bf16 [batch, n_tokens, 4096] raw q|k|v rows (as
+ *             q3_layer_weights.w_qkv orders them);
+ *   q_norm, k_norm  bf16 [128] gains; rope_cos, rope_sin as in q3_model;
+ *   k_layer, v_layer  one layer of a KV cache of capacity max_seq;
+ *   write_kv  1: write the chunk's K and V rows first; 0: those rows
+ *             already hold them (an earlier call with 1) and only the
+ *             attention runs;
+ *   out       bf16 [batch, n_tokens, 2048].
+ * Errors: Q3_ERR_NULL, Q3_ERR_SHAPE (as q3_attention_prefill, or write_kv
+ * not 0 or 1), Q3_ERR_POSITION (start_pos < 0 or start_pos + n_tokens >
+ * max_seq), Q3_ERR_ALIGN (16 B), Q3_ERR_HIP. */
+int q3_attention_prefill_qkv(const void *qkv, const void *q_norm, const void *k_norm, const float *rope_cos,
+                             const float *rope_sin, void *k_layer, void *v_layer, int32_t batch, int32_t n_tokens,
+                             int32_t start_pos, int32_t max_seq, int32_t write_kv, void *out, void *stream);
+
 /* Helper: the attention half of one decode step for one new token per
  * sequence, as q3_decode_step runs it ("古法手撕简易LLM推理器"
  * §prefill与predict): from the raw projection rows of the new tokens it

@@ -46,7 +46,7 @@ int main() {
   EXPECT_EQ(L2.apart < L2.logits, 1);          // decode partials present for one-token calls
   EXPECT_EQ(L3.part, L3.apart);                // no skinny partials above 64 rows
   EXPECT_EQ(L1.resid % 256, 0); EXPECT_EQ(L1.h % 256, 0); EXPECT_EQ(L1.fh % 256, 0);
-  EXPECT_EQ(L3.total >= (size_t)8 * 4096 * (1024 * 4 + 1024 * 2 + 4096 * 2 + 2048 * 4 + 3072 * 2), 1);
+  EXPECT_EQ(L3.total >= (size_t)8 * 4096 * (1024 * 4 + 1024 * 2 + 4096 * 2 + 2048 * 2 + 3072 * 2), 1);
   // ---- decode splits
   EXPECT_EQ(decode_streaming(1, 192), 0);     // 22 MB of caches: stays in the last-level cache
   EXPECT_EQ(decode_streaming(32, 2176), 1);

@@ -162,6 +162,21 @@ def test_attention_helpers_reject_bad_arguments(B):
     assert pf(0x1000, 0x2000, 0x3000, 2, 16, 49, 64, 0x4000) == B.Q3_ERR_POSITION
     assert pf(0x1000, 0x2000, 0x3000, 2, 16, -1, 64, 0x4000) == B.Q3_ERR_POSITION
     assert pf(0x1000, 0x2008, 0x3000, 2, 16, 0, 64, 0x4000) == B.Q3_ERR_ALIGN
+    pq = [0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000, 2, 16, 0, 64, 1, 0x8000]
+
+    def pqkv(i, value):
+        a = list(pq)
+        a[i] = value
+        return B.q3_attention_prefill_qkv(*a, stream=0, check=False)
+
+    assert pqkv(1, None) == B.Q3_ERR_NULL        # q gain
+    assert pqkv(4, None) == B.Q3_ERR_NULL        # sin table
+    assert pqkv(0, None) == B.Q3_ERR_NULL        # projection rows
+    assert pqkv(11, 2) == B.Q3_ERR_SHAPE         # write_kv
+    assert pqkv(7, 0) == B.Q3_ERR_SHAPE
+    assert pqkv(9, 49) == B.Q3_ERR_POSITION
+    assert pqkv(2, 0x3008) == B.Q3_ERR_ALIGN     # k gain
+    assert pqkv(3, 0x4004) == B.Q3_ERR_ALIGN     # cos table
     need = B.q3_workspace_bytes(3, 1)
     base = [0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000, 3, 64, 0x8000, 64, 0x9000, 0xA000, need]
 

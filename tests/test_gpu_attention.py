@@ -1,7 +1,7 @@
 """GPU parity of the attention kernels on their own, through the helper
-entry points q3_attention_prefill and q3_attention_decode, against the
-float64 oracle's attention (plus its RMSNorm and RoPE for the decode helper,
-which starts from the raw projection rows).
+entry points q3_attention_prefill, q3_attention_prefill_qkv and
+q3_attention_decode, against the float64 oracle's attention (plus its
+RMSNorm and RoPE for the helpers that start from the raw projection rows).
 
 Covers ragged query tiles, a chunk at an offset, single keys, the cache
 capacity edge, and the full benchmark sizes (8 x 4096 prefill; batch 32
@@ -92,6 +92,67 @@ def test_attention_prefill_8x4096_sampled(lib):
         e = rel_err(got[b, rows], ref)
         log(f"   seq {b}: rel={e:.3e}")
         assert e <= REL_TOL
+
+
+def _prefill_qkv_case(lib, rope, batch, T, start, max_seq, rows=None, seed=71):
+    """q3_attention_prefill_qkv from raw projection rows: K/V rows written
+    into the cache (rows before the chunk untouched), q normed and rotated
+    in the attention; then the same call with write_kv = 0 reproduces the
+    output bit for bit."""
+    B, dev = lib
+    log(f"[attn-prefill-qkv] batch={batch} T={T} start={start} max_seq={max_seq}")
+    kb, vb, _, _ = _caches(B, dev, batch, max_seq, start, seed)
+    kb[:, :, start + T:] = 0x7FC0   # NaN bits past the chunk: never read
+    vb[:, :, start + T:] = 0x7FC0
+    kc, vc = dev.to_device_bf16(kb), dev.to_device_bf16(v_dense_to_blocked(vb))
+    qkv = I.normal_bf16(seed + 2, "attn_qkv_prefill", (batch, T, B.QKV_ROWS), std=1.0)
+    qn = I.normal_bf16(seed + 3, "attn_qn", (B.HEAD_DIM,), std=0.02, mean=1.0)
+    kn = I.normal_bf16(seed + 4, "attn_kn", (B.HEAD_DIM,), std=0.02, mean=1.0)
+    qkv_d, qn_d, kn_d = dev.to_device_bf16(qkv), dev.to_device_bf16(qn), dev.to_device_bf16(kn)
+    out = torch.empty((batch, T, B.N_HEADS * B.HEAD_DIM), dtype=torch.bfloat16, device="cuda")
+    B.q3_attention_prefill_qkv(qkv_d, qn_d, kn_d, rope[0], rope[1], kc, vc, batch, T, start, max_seq, 1, out)
+    torch.cuda.synchronize()
+    got = bf16_tensor_to_f64(out).reshape(batch, T, B.N_HEADS, B.HEAD_DIM)
+    kg = bf16_tensor_to_f64(kc)
+    vg = v_blocked_to_dense(bf16_tensor_to_f64(vc))
+    out2 = torch.empty_like(out)
+    B.q3_attention_prefill_qkv(qkv_d, qn_d, kn_d, rope[0], rope[1], kc, vc, batch, T, start, max_seq, 0, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    x = O.widen_bf16(qkv)
+    pos = np.arange(start, start + T)
+    sel = np.arange(T) if rows is None else np.asarray(rows)
+    for b in range(batch):
+        k = O.rope(O.rmsnorm(x[b, :, 2048:3072].reshape(T, B.N_KV_HEADS, B.HEAD_DIM), O.widen_bf16(kn)), pos, 1e6)
+        v = x[b, :, 3072:].reshape(T, B.N_KV_HEADS, B.HEAD_DIM)
+        q = O.rope(O.rmsnorm(x[b, sel, :2048].reshape(len(sel), B.N_HEADS, B.HEAD_DIM), O.widen_bf16(qn)),
+                   pos[sel], 1e6)
+        kk = np.concatenate([O.widen_bf16(kb[b, :, :start]), k.transpose(1, 0, 2)], axis=1)
+        vv = np.concatenate([O.widen_bf16(vb[b, :, :start]), v.transpose(1, 0, 2)], axis=1)
+        ref = O.attention(q.transpose(1, 0, 2), kk, vv, pos[sel]).transpose(1, 0, 2)
+        e = rel_err(got[b, sel], ref)
+        ek = rel_err(kg[b, :, start:start + T], k.transpose(1, 0, 2))
+        np.testing.assert_array_equal(vg[b, :, start:start + T], v.transpose(1, 0, 2))  # raw V stored exactly
+        np.testing.assert_array_equal(kg[b, :, :start], O.widen_bf16(kb[b, :, :start]))
+        np.testing.assert_array_equal(vg[b, :, :start], O.widen_bf16(vb[b, :, :start]))
+        log(f"   seq {b}: out rel={e:.3e} K rows rel={ek:.3e}")
+        assert e <= REL_TOL and ek <= REL_TOL
+
+
+@pytest.mark.parametrize("batch,T,start,max_seq", [
+    (1, 16, 0, 16),
+    (2, 100, 50, 160),   # ragged tile, chunk at an offset, unaligned V blocks
+    (3, 13, 3, 24),
+    (2, 77, 61, 256),    # NaN rows past the chunk must stay unread
+])
+def test_attention_prefill_qkv_parity(lib, rope, batch, T, start, max_seq):
+    _prefill_qkv_case(lib, rope, batch, T, start, max_seq)
+
+
+def test_attention_prefill_qkv_8x4096_sampled(lib, rope):
+    """The in-step form of the 8 x 4096 attention (raw projection rows);
+    every K/V row checked, outputs on rows sampled across tiles."""
+    _prefill_qkv_case(lib, rope, 8, 4096, 0, 4096, rows=[0, 1, 63, 64, 127, 128, 1000, 2047, 2048, 4094, 4095])
 
 
 def _decode_case(lib, rope, batch, max_seq, positions, check_seqs=None, seed=51):
