@@ -37,6 +37,8 @@
 // C column l%32, rows 8*(i/4) + 4*(l/32) + (i%4).
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -89,17 +91,36 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const uint16_t* vbase = v_cache + ((size_t)b * HKV + g) * max_seq * D;
   const int last_key = kv_len - 1, last_blk = (kv_len - 1) & ~7;
 
-  // DMA of key tile j into its stage: 8 instructions per thread (4 for K, 4 for V)
+  // DMA of key tile j into its stage: 8 instructions per thread (4 for K, 4 for V).
+  // Lane offsets are fixed; every tile but the last adds a uniform base
+  // (j * 64 rows), and only the last clamps its rows to the cache range.
+  const int kr_lane = 4 * w + (l >> 4);  // K row within each 16-row quarter
+  const int koff = kr_lane * D + 8 * ((l & 15) ^ fa_kswz(kr_lane));
   auto issue = [&](int j) {
     uint16_t* ks = lds[j % FA_NS][0];
     uint16_t* vs = lds[j % FA_NS][1];
+    if (j + 1 < n_kt) {
+      const uint16_t* kt = kbase + (size_t)j * FA_BK * D;
+      const uint16_t* vt = vbase + (size_t)j * FA_BK * D;
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        __builtin_amdgcn_global_load_lds((const void*)(kt + 16 * rq * D + koff),
+                                         (lds_ptr_t)(ks + (16 * rq + 4 * w) * D), 16, 0, 0);
+      }
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int ch = 4 * rq + w;
+        __builtin_amdgcn_global_load_lds((const void*)(vt + 8 * (ch >> 1) * D + (ch & 1) * 512 + 8 * l),
+                                         (lds_ptr_t)(vs + ch * 512), 16, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {  // K rows 16 rq + 4 w .. +3, one row per 16 lanes
-      const int r = 16 * rq + 4 * w + (l >> 4);
-      const int c = (l & 15) ^ fa_kswz(r);
+      const int r = 16 * rq + kr_lane;
       int key = j * FA_BK + r;
       key = key < last_key ? key : last_key;
-      __builtin_amdgcn_global_load_lds((const void*)(kbase + (size_t)key * D + 8 * c),
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + (size_t)key * D + (koff - kr_lane * D)),
                                        (lds_ptr_t)(ks + (16 * rq + 4 * w) * D), 16, 0, 0);
     }
 #pragma unroll
@@ -193,12 +214,27 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   }
 
 
-  for (int j = 0; j < n_kt; ++j) {
+  // LDS read offsets (bytes) of this lane, fixed for the whole loop: K operand
+  // of dim step s in 32-key block 0 (block 1 is 32 rows further), V operand
+  // of step 0 (the other steps are constant offsets)
+  uint32_t kofs[8];
+  {
+    const int sw = fa_kswz(krow);  // equal for rows krow and 32 + krow
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) kofs[s8] = 2u * (uint32_t)(krow * D + 8 * ((2 * s8 + lh) ^ sw));
+  }
+  const uint32_t vofs = 2u * (uint32_t)(lh * (D * VBLK) + lq * VBLK);
+  const char* lds_b = reinterpret_cast<const char*>(&lds[0][0][0]);
+
+  // tile j in stage ST = j % 2 (a compile-time constant, so the stage offset
+  // folds into the LDS instructions' immediate offsets)
+  auto tile = [&](int j, auto stage_c) {
+    constexpr int ST = decltype(stage_c)::value;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's part of tile j landed
     __builtin_amdgcn_s_barrier();        // all of tile j is in LDS; stage (j+1)%2 is free
     if (j + 1 < n_kt) issue(j + 1);
     if (j == n_kt - 1 && n_kt * FA_BK > kv_len) {  // zero the V positions past the end, once
-      uint16_t* vz = lds[j % FA_NS][1];
+      uint16_t* vz = lds[ST][1];
       const int first = kv_len - j * FA_BK;
       for (int e = tid; e < (FA_BK - first) * D; e += 256) {
         const int p = first + e / D, d = e % D;
@@ -206,10 +242,10 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       }
       __syncthreads();
     }
-    if (j >= wave_kt) continue;          // past this wave's causal range (wave-uniform)
+    if (j >= wave_kt) return;            // past this wave's causal range (wave-uniform)
 
-    const uint16_t* ks = lds[j % FA_NS][0];
-    const uint16_t* vs = lds[j % FA_NS][1];
+    const char* ks = lds_b + ST * (2 * FA_TILE * 2);
+    const char* vs = ks + FA_TILE * 2;
     // ---- S^T = K Q^T: sacc[kb] for keys j*64 + 32 kb + (row order above)
     f32x16 sacc[2];
 #pragma unroll
@@ -219,21 +255,21 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     {
       // 16 K operand reads (2 key blocks x 8 dim steps) in a ring four reads
       // ahead of the MFMAs
-      const uint16_t* kr0 = ks + krow * D;
-      const uint16_t* kr1 = ks + (32 + krow) * D;
-      const int sw = fa_kswz(krow);  // equal for rows krow and 32 + krow
       auto kread = [&](int x) {
-        return *reinterpret_cast<const u32x4*>(((x >> 3) ? kr1 : kr0) + 8 * ((2 * (x & 7) + lh) ^ sw));
+        return *reinterpret_cast<const u32x4*>(ks + kofs[x & 7] + (x >> 3) * (32 * D * 2));
       };
+      // step y: key block y % 2, dim step y / 2, so consecutive MFMAs go to
+      // different accumulators
+      auto kx = [](int y) { return 8 * (y & 1) + (y >> 1); };
       u32x4 ka[4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) ka[x] = kread(x);
+      for (int y = 0; y < 4; ++y) ka[y] = kread(kx(y));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        sacc[x >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[x & 3]), as_bf16x8(qreg[x & 7]),
-                                                               sacc[x >> 3], 0, 0, 0);
-        if (x + 4 < 16) ka[x & 3] = kread(x + 4);
+      for (int y = 0; y < 16; ++y) {
+        sacc[y & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[y & 3]), as_bf16x8(qreg[y >> 1]),
+                                                              sacc[y & 1], 0, 0, 0);
+        if (y + 4 < 16) ka[y & 3] = kread(kx(y + 4));
         __builtin_amdgcn_sched_barrier(0);  // keep each read four steps ahead of its MFMA
       }
     }
@@ -263,7 +299,10 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       float mx = sv[0];
 #pragma unroll
       for (int i = 1; i < 32; ++i) mx = fmaxf(mx, sv[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+      {  // with the partner lane l ^ 32 (same query), through a lane swap instead of the LDS crossbar
+        const auto sw32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw32[0]), __uint_as_float(sw32[1])) * sl2;
+      }
       const bool raise = mx > m_run + FA_RESCALE_SLACK;
       if (__ballot(raise)) {
         const float m_new = raise ? mx : m_run;
@@ -292,9 +331,8 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     // ---- O^T += V^T P^T, 16 keys per MFMA step; A = 8 positions of one dim
     {
       // 16 V operand reads (4 key steps x 4 dim blocks) in a ring four reads ahead
-      const uint16_t* vb0 = vs + lh * (D * VBLK) + lq * VBLK;
       auto vread = [&](int x) {
-        return *reinterpret_cast<const u32x4*>(vb0 + 2 * (x >> 2) * (D * VBLK) + 32 * (x & 3) * VBLK);
+        return *reinterpret_cast<const u32x4*>(vs + vofs + 2 * (2 * (x >> 2) * (D * VBLK) + 32 * (x & 3) * VBLK));
       };
       u32x4 va[4];
 #pragma unroll
@@ -309,6 +347,10 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+  for (int j = 0; j < n_kt; j += 2) {
+    tile(j, std::integral_constant<int, 0>{});
+    if (j + 1 < n_kt) tile(j + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- normalise and store: lane holds dims db*32 + 8*(i/4) + 4*lh + (i%4) of its query
