@@ -233,13 +233,14 @@ __global__ __launch_bounds__(256, (WN * WM > 4) ? 1 : 2) void k_gemm_tiled(
 // ---------------------------------------------------------------------------
 // Large-M variant: persistent workgroups fed by direct-to-LDS loads
 // (global_load_lds_dwordx4).  One workgroup per CU walks a list of 256 x 256
-// tiles; a 4-stage LDS ring of K = 32 slices runs continuously across tile
-// boundaries (three slices in flight while one is consumed), so the next
-// tile's first loads overlap the current tile's epilogue and no registers
-// are spent on staging.  Each DMA instruction fills 1 KB of LDS
-// contiguously (lane i -> bytes 16 i), so rows are not padded; instead the
-// four 16-byte chunks of each 64-byte row are XOR-swizzled by (row / 4) % 4,
-// which keeps the 32-row MFMA operand reads free of bank conflicts.
+// tiles; a 2-stage LDS ring of K = 64 slices runs continuously across tile
+// boundaries (one slice in flight while the other is consumed, one barrier
+// per 4 MFMA k-steps), so the next tile's first loads overlap the current
+// tile's epilogue and no registers are spent on staging.  Each DMA
+// instruction fills 1 KB of LDS contiguously (lane i -> bytes 16 i), so rows
+// are not padded; instead the eight 16-byte chunks of each 128-byte row are
+// XOR-swizzled by (row / 2) % 8, which keeps the 32-row MFMA operand reads
+// free of bank conflicts (16 lanes on 16 rows hit 16 different bank groups).
 //
 // 8 waves as 2 (features) x 4 (tokens), each owning 4 x 2 MFMA blocks of
 // 32 x 32 (128 features of 64 tokens), i.e. two waves per SIMD.  A wave's
@@ -248,13 +249,14 @@ __global__ __launch_bounds__(256, (WN * WM > 4) ? 1 : 2) void k_gemm_tiled(
 // (same operand reads and MFMAs per k-step).  Tiles are dealt out XCD-contiguously:
 // the 32 workgroups on one XCD process consecutive tiles in the grouped
 // order, which keeps their X and W panels in that XCD's L2.
-constexpr int DK = 32;        // K per stage
-constexpr int DSTAGES = 4;
+constexpr int DK = 64;        // K per stage
+constexpr int DSTAGES = 2;
+constexpr int DKS = DK / 16;  // MFMA k-steps per stage
 constexpr int DROWS = 256;    // rows per operand tile
-constexpr int DSTAGE_ELEMS = DROWS * DK;  // bf16 per operand per stage (16 KB)
+constexpr int DSTAGE_ELEMS = DROWS * DK;  // bf16 per operand per stage (32 KB)
 constexpr int PWG_XCD = 32;   // persistent workgroups per XCD (one per CU)
 
-__device__ __forceinline__ int dswz(int row, int chunk) { return row * DK + ((chunk ^ ((row >> 2) & 3)) << 3); }
+__device__ __forceinline__ int dswz(int row, int chunk) { return row * DK + ((chunk ^ ((row >> 1) & 7)) << 3); }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
   // silu(g) * u = g * u / (1 + e^-g), with the hardware exp2 and reciprocal
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_persist(const uint16_t* __restr
   constexpr int WGN = 2, WGM = 4, NWAVES = 8;
   constexpr int BN = 256, BM = 256;
   constexpr int WN = BN / 32 / WGN, WM = BM / 32 / WGM;  // 4 x 2 blocks per wave
-  constexpr int DMA_PER_WAVE = 16 / NWAVES;              // 1 KB DMAs per operand per stage per wave
+  constexpr int DMA_PER_WAVE = (DSTAGE_ELEMS * 2 / 1024) / NWAVES;  // 1 KB DMAs per operand per stage per wave
   __shared__ __attribute__((aligned(1024))) uint16_t Ls[DSTAGES][2][DSTAGE_ELEMS];  // [stage][W, X]
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lq = l & 31, lh = l >> 5;
@@ -293,15 +295,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_persist(const uint16_t* __restr
     tm = first_m + within % gm;
     tn = within / gm;
   };
-  // DMA sources of this lane: wave w, instruction i fills LDS rows 16 (2 w + i) .. +15;
-  // lane l writes row 16 (.) + l / 4, slot l % 4, which holds logical chunk (l % 4) ^ swizzle.
+  // DMA sources of this lane: wave w, instruction i fills LDS rows 8 (4 w + i) .. +7;
+  // lane l writes row 8 (.) + l / 8, slot l % 8, which holds logical chunk (l % 8) ^ swizzle.
   auto set_src = [&](int i_tile, const uint16_t* (&ws)[DMA_PER_WAVE], const uint16_t* (&xs)[DMA_PER_WAVE]) {
     int tm, tn;
     tile_coords(i_tile, tm, tn);
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      const int row = 16 * (DMA_PER_WAVE * w + i) + (l >> 2);
-      const int chunk = (l & 3) ^ ((row >> 2) & 3);
+      const int row = 8 * (DMA_PER_WAVE * w + i) + (l >> 3);
+      const int chunk = (l & 7) ^ ((row >> 1) & 7);
       int wrow;
       if constexpr (EPI == EPI_SILU) {
         const int half = N >> 1;
@@ -414,36 +416,47 @@ __global__ __launch_bounds__(512, 1) void k_gemm_persist(const uint16_t* __restr
     }
   };
 
-  // Prologue: stages 0..2, then wait for stage 0 (the two later stages, 4 DMAs
-  // per wave each, may still be in flight) and a plain barrier: no fence,
-  // since each wave has waited for its own DMA writes and a fenced
+  // Prologue: stages 0 and 1 into both buffers, then wait for stage 0 (stage
+  // 1's 8 DMAs per wave may still be in flight) and a plain barrier: no
+  // fence, since each wave has waited for its own DMA writes and a fenced
   // __syncthreads would wait for every stage in flight.
-  for (int p = 0; p < DSTAGES - 1; ++p) issue_next();
+  for (int p = 0; p < DSTAGES; ++p) issue_next();
+  static_assert(2 * DMA_PER_WAVE == 8, "wait count below");
   __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
   __builtin_amdgcn_s_barrier();
   zero_acc();
   rd(0, 0, ra0, rb0);
   int kt = 0, tile = 0;
-  // steady state: every stage has a successor, so the body is branch-free
-  // apart from the tile epilogue and the LDS wait counts stay exact
+  auto stage_body = [&](int g) {
+    // k-steps 0 .. DKS-2 of stage g, each with the next step's operand reads in flight
+#pragma unroll
+    for (int ks = 1; ks < DKS; ++ks) {
+      if (ks & 1) {
+        rd(g, ks, ra1, rb1);
+        mm(ra0, rb0);
+      } else {
+        rd(g, ks, ra0, rb0);
+        mm(ra1, rb1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, WN + WM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, WN * WM - 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   for (int g = 0; g + 1 < n_stages; ++g) {
-    rd(g, 1, ra1, rb1);
-    mm(ra0, rb0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // 1 MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, WN + WM, 0);            // next k-step's LDS reads
-    __builtin_amdgcn_sched_group_barrier(0x008, WN * WM - 1, 0);        // remaining MFMAs
-    __builtin_amdgcn_sched_barrier(0);
-    // stage g+1 landed (stage g+2, 4 DMAs per wave, may be in flight); epilogue
-    // stores of the previous tile may still be outstanding too, which only makes this wait longer
-    __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+    stage_body(g);
+    // stage g+1 landed; every wave's reads of stage g have returned before the
+    // barrier, so the DMA below may refill its buffer
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     issue_next();
     rd(g + 1, 0, ra0, rb0);
-    mm(ra1, rb1);
-    __builtin_amdgcn_sched_group_barrier(0x020, 2 * DMA_PER_WAVE, 1);   // DMA issues
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);                  // 1 MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, WN + WM, 1);            // next stage's LDS reads
-    __builtin_amdgcn_sched_group_barrier(0x008, WN * WM - 1, 1);        // remaining MFMAs
+    mm(ra1, rb1);  // k-step DKS-1 of stage g (DKS even)
+    __builtin_amdgcn_sched_group_barrier(0x020, 2 * DMA_PER_WAVE, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, WN + WM, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, WN * WM - 1, 1);
     __builtin_amdgcn_sched_barrier(0);
     if (++kt == nk) {
       epilogue(tile);
@@ -453,8 +466,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_persist(const uint16_t* __restr
     }
   }
   // last stage
-  rd(n_stages - 1, 1, ra1, rb1);
-  mm(ra0, rb0);
+  stage_body(n_stages - 1);
   mm(ra1, rb1);
   epilogue(tile);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no DMA may still target LDS at exit
