@@ -3,8 +3,10 @@
 // Both operands are K-contiguous ([rows][K] row-major), which is the native
 // operand order of the MFMA unit.  The kernel forms C^T = W X^T so that the
 // accumulator of v_mfma_f32_32x32x16_bf16 holds, per lane, 4 consecutive
-// output features of one token; the epilogue then writes 8 B (bf16) or
-// 16 B (f32) vectors.
+// output features of one token.  The bf16 epilogues trade groups between
+// the two half-waves (lane l and l + 32 hold adjacent groups of the same
+// token) and write 16 B per lane; the fp32 residual add reads a batch of
+// rows before it writes any of them.
 //
 // Lane layout of the 32x32x16 MFMA (lane l, element j of the 8-wide operand):
 //   A: row l%32, k-slot (l/32, j);  B: column l%32, k-slot (l/32, j);
@@ -13,11 +15,8 @@
 //
 // Tile: 4 waves as 2 x 2; each wave owns WN x WM MFMA blocks of 32 x 32
 // (features x tokens), so the workgroup tile is 64 WN x 64 WM with K steps
-// of 64.  The large variant (WN = WM = 4: 256 x 256 per workgroup, 128 x 128
-// per wave, 256 accumulator registers) halves the LDS bytes read per MFMA
-// compared with 64 x 64 per wave, which would otherwise saturate LDS
-// bandwidth at MFMA peak; it runs one wave per SIMD.  Global -> register ->
-// LDS double buffering, one barrier per K step, LDS rows padded by 16 B.
+// of 64 (launched with WN = WM = 2).  Global -> register -> LDS double
+// buffering, one barrier per K step, LDS rows padded by 16 B.
 //
 // Workgroup order: consecutive workgroup ids land on different XCDs (round
 // robin over 8), so ids are remapped to give each XCD a contiguous range of
@@ -27,6 +26,62 @@
 #include "launch.hpp"
 
 namespace q3 {
+
+// Epilogue helpers for the C^T = W X^T accumulator layout: in a 32 x 32 block,
+// lane (r, h) = (l % 32, l / 32) holds features 8 j + 4 h .. + 3 (group j =
+// 0..3, elements 4 j .. 4 j + 3) of token r.
+
+// 16-byte store of 8 consecutive bf16 features from groups j = 2 p (lo) and
+// 2 p + 1 (hi): one swap between the half-waves gives lane h = 0 features
+// 16 p .. 16 p + 7 and lane h = 1 features 16 p + 8 .. 16 p + 15, both of
+// token r.  dst is the address of the lane's 8 features; the lane and its
+// partner l ^ 32 must both be active.
+__device__ __forceinline__ void store_pair16(uint16_t* dst, u32x2 lo, u32x2 hi) {
+  const auto x = __builtin_amdgcn_permlane32_swap(lo.x, hi.x, false, false);
+  const auto y = __builtin_amdgcn_permlane32_swap(lo.y, hi.y, false, false);
+  u32x4 v;
+  v.x = x[0];
+  v.y = y[0];
+  v.z = x[1];
+  v.w = y[1];
+  *reinterpret_cast<u32x4*>(dst) = v;
+}
+
+// bf16 features 16 p + 8 h .. + 7 of one block (feature 0 of the block at row + 0).
+__device__ __forceinline__ void store_block_bf16(uint16_t* row, const f32x16& a, int lh) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    u32x2 o[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int g = 2 * p + h;
+      o[h].x = pack_bf2(a[4 * g], a[4 * g + 1]);
+      o[h].y = pack_bf2(a[4 * g + 2], a[4 * g + 3]);
+    }
+    store_pair16(row + 16 * p + 8 * lh, o[0], o[1]);
+  }
+}
+
+// row[b * 32 + 8 j + 4 h .. + 3] += group j of block(b) for NB blocks.  All
+// loads are issued before the first store: the compiler keeps the program
+// order of accesses that may alias, so interleaved load-add-store would wait
+// a full memory round trip per 16 bytes.
+template <int NB, typename Block>
+__device__ __forceinline__ void add_blocks_f32(float* row, Block block, int lh) {
+  f32x4 r[NB][4];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) r[b][g] = *reinterpret_cast<const f32x4*>(row + b * 32 + 8 * g + 4 * lh);
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x16& a = block(b);
+      r[b][g] += f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+      *reinterpret_cast<f32x4*>(row + b * 32 + 8 * g + 4 * lh) = r[b][g];
+    }
+}
 
 constexpr int TB_K = 64;
 constexpr int T_LDS = TB_K + 8;  // padded row, bf16 elements (144 B)
@@ -192,40 +247,34 @@ __global__ __launch_bounds__(256, (WN * WM > 4) ? 1 : 2) void k_gemm_tiled(
     if (m >= M) continue;
     if constexpr (EPI == EPI_SILU) {
 #pragma unroll
-      for (int nb = 0; nb < WN / 2; ++nb)
+      for (int nb = 0; nb < WN / 2; ++nb) {
+        f32x16 v;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float v[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float gt = acc[nb][mb][4 * g + i], up = acc[nb + WN / 2][mb][4 * g + i];
-            v[i] = gt / (1.0f + __expf(-gt)) * up;
-          }
-          const int n = tile_n * (BN / 2) + wn * (16 * WN) + nb * 32 + 8 * g + 4 * lh;
-          u32x2 o;
-          o.x = pack_bf2(v[0], v[1]);
-          o.y = pack_bf2(v[2], v[3]);
-          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + (size_t)m * ldo + n) = o;
+        for (int i = 0; i < 16; ++i) {
+          const float gt = acc[nb][mb][i], up = acc[nb + WN / 2][mb][i];
+          v[i] = gt / (1.0f + __expf(-gt)) * up;
         }
-    } else {
+        store_block_bf16(reinterpret_cast<uint16_t*>(out) + (size_t)m * ldo + tile_n * (BN / 2) + wn * (16 * WN) +
+                             nb * 32,
+                         v, lh);
+      }
+    } else if constexpr (EPI == EPI_BF16) {
+#pragma unroll
+      for (int nb = 0; nb < WN; ++nb)
+        store_block_bf16(reinterpret_cast<uint16_t*>(out) + (size_t)m * ldo + tile_n * BN + wn * 32 * WN + nb * 32,
+                         acc[nb][mb], lh);
+    } else if constexpr (EPI == EPI_F32) {
 #pragma unroll
       for (int nb = 0; nb < WN; ++nb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int n = tile_n * BN + wn * 32 * WN + nb * 32 + 8 * g + 4 * lh;
-          f32x4 v = {acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2], acc[nb][mb][4 * g + 3]};
-          if constexpr (EPI == EPI_BF16) {
-            u32x2 o;
-            o.x = pack_bf2(v[0], v[1]);
-            o.y = pack_bf2(v[2], v[3]);
-            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + (size_t)m * ldo + n) = o;
-          } else if constexpr (EPI == EPI_F32) {
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)m * ldo + n) = v;
-          } else {  // EPI_ADD_F32
-            f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)m * ldo + n);
-            *dst = *dst + v;
-          }
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)m * ldo + n) =
+              f32x4{acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2], acc[nb][mb][4 * g + 3]};
         }
+    } else {  // EPI_ADD_F32
+      add_blocks_f32<WN>(reinterpret_cast<float*>(out) + (size_t)m * ldo + tile_n * BN + wn * 32 * WN,
+                         [&](int b) -> const f32x16& { return acc[b][mb]; }, lh);
     }
   }
 }
@@ -382,36 +431,36 @@ __global__ __launch_bounds__(512, 1) void k_gemm_persist(const uint16_t* __restr
       if (m >= M) continue;
       if constexpr (EPI == EPI_SILU) {
 #pragma unroll
-        for (int nb = 0; nb < WN / 2; ++nb)
+        for (int nb = 0; nb < WN / 2; ++nb) {
+          const f32x16& ga = acc[nb][mb];
+          const f32x16& ua = acc[nb + WN / 2][mb];
+          f32x16 v;
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x16& ga = acc[nb][mb];
-            const f32x16& ua = acc[nb + WN / 2][mb];
-            const int n = tn * (BN / 2) + wn * (16 * WN) + nb * 32 + 8 * g + 4 * lh;
-            u32x2 o;
-            o.x = pack_bf2(silu_mul(ga[4 * g], ua[4 * g]), silu_mul(ga[4 * g + 1], ua[4 * g + 1]));
-            o.y = pack_bf2(silu_mul(ga[4 * g + 2], ua[4 * g + 2]), silu_mul(ga[4 * g + 3], ua[4 * g + 3]));
-            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + (size_t)m * ldo + n) = o;
-          }
-      } else {
+          for (int i = 0; i < 16; ++i) v[i] = silu_mul(ga[i], ua[i]);
+          store_block_bf16(reinterpret_cast<uint16_t*>(out) + (size_t)m * ldo + tn * (BN / 2) + wn * (16 * WN) +
+                               nb * 32,
+                           v, lh);
+        }
+      } else if constexpr (EPI == EPI_BF16) {
+#pragma unroll
+        for (int nb = 0; nb < WN; ++nb)
+          store_block_bf16(reinterpret_cast<uint16_t*>(out) + (size_t)m * ldo + tn * BN + wn * 32 * WN + nb * 32,
+                           acc[nb][mb], lh);
+      } else if constexpr (EPI == EPI_F32) {
 #pragma unroll
         for (int nb = 0; nb < WN; ++nb)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int n = tn * BN + wn * 32 * WN + nb * 32 + 8 * g + 4 * lh;
-            f32x4 v = {acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2], acc[nb][mb][4 * g + 3]};
-            if constexpr (EPI == EPI_BF16) {
-              u32x2 o;
-              o.x = pack_bf2(v[0], v[1]);
-              o.y = pack_bf2(v[2], v[3]);
-              *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + (size_t)m * ldo + n) = o;
-            } else if constexpr (EPI == EPI_F32) {
-              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)m * ldo + n) = v;
-            } else {  // EPI_ADD_F32
-              f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)m * ldo + n);
-              *dst = *dst + v;
-            }
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)m * ldo + n) =
+                f32x4{acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2], acc[nb][mb][4 * g + 3]};
           }
+      } else {  // EPI_ADD_F32: two blocks (32 registers of residual) per batch
+        float* row = reinterpret_cast<float*>(out) + (size_t)m * ldo + tn * BN + wn * 32 * WN;
+#pragma unroll
+        for (int q = 0; q < WN / 2; ++q) {
+          add_blocks_f32<2>(row + 64 * q, [&](int b) -> const f32x16& { return acc[2 * q + b][mb]; }, lh);
+        }
       }
     }
   };
