@@ -361,14 +361,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       const float inv = 1.0f / l_tot;
       uint16_t* orow = out + ((size_t)row0 + tq) * QDIM + hq * D;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          u32x2 o;
-          o.x = pack_bf2(oacc[db][4 * gq] * inv, oacc[db][4 * gq + 1] * inv);
-          o.y = pack_bf2(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * gq + 4 * lh) = o;
-        }
+      for (int db = 0; db < 4; ++db) store_block_bf16(orow + db * 32, oacc[db] * inv, lh);
     }
   }
 }

@@ -90,6 +90,42 @@ __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70);
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Stores from the accumulator layout of v_mfma_f32_32x32x16_bf16 with the
+// output row along B: in a 32 x 32 block, lane (r, h) = (l % 32, l / 32)
+// holds columns 8 j + 4 h .. + 3 (group j = 0..3, elements 4 j .. 4 j + 3)
+// of row r.
+
+// 16-byte store of 8 consecutive bf16 columns from groups j = 2 p (lo) and
+// 2 p + 1 (hi): one swap between the half-waves gives lane h = 0 columns
+// 16 p .. 16 p + 7 and lane h = 1 columns 16 p + 8 .. 16 p + 15, both of
+// row r.  dst is the address of the lane's 8 columns; the lane and its
+// partner l ^ 32 must both be active.
+__device__ __forceinline__ void store_pair16(uint16_t* dst, u32x2 lo, u32x2 hi) {
+  const auto x = __builtin_amdgcn_permlane32_swap(lo.x, hi.x, false, false);
+  const auto y = __builtin_amdgcn_permlane32_swap(lo.y, hi.y, false, false);
+  u32x4 v;
+  v.x = x[0];
+  v.y = y[0];
+  v.z = x[1];
+  v.w = y[1];
+  *reinterpret_cast<u32x4*>(dst) = v;
+}
+
+// bf16 columns 16 p + 8 h .. + 7 of one block (column 0 of the block at row + 0).
+__device__ __forceinline__ void store_block_bf16(uint16_t* row, const f32x16& a, int lh) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    u32x2 o[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int g = 2 * p + h;
+      o[h].x = pack_bf2(a[4 * g], a[4 * g + 1]);
+      o[h].y = pack_bf2(a[4 * g + 2], a[4 * g + 3]);
+    }
+    store_pair16(row + 16 * p + 8 * lh, o[0], o[1]);
+  }
+}
+
 // Rows of a multi-token call and the (sequence, position) each belongs to.
 // Uniform: n sequences of T rows, row m = s*T + t at position
 // (pos ? pos[s] : start) + t.  Packed (off != null): sequence s owns rows

@@ -27,41 +27,6 @@
 
 namespace q3 {
 
-// Epilogue helpers for the C^T = W X^T accumulator layout: in a 32 x 32 block,
-// lane (r, h) = (l % 32, l / 32) holds features 8 j + 4 h .. + 3 (group j =
-// 0..3, elements 4 j .. 4 j + 3) of token r.
-
-// 16-byte store of 8 consecutive bf16 features from groups j = 2 p (lo) and
-// 2 p + 1 (hi): one swap between the half-waves gives lane h = 0 features
-// 16 p .. 16 p + 7 and lane h = 1 features 16 p + 8 .. 16 p + 15, both of
-// token r.  dst is the address of the lane's 8 features; the lane and its
-// partner l ^ 32 must both be active.
-__device__ __forceinline__ void store_pair16(uint16_t* dst, u32x2 lo, u32x2 hi) {
-  const auto x = __builtin_amdgcn_permlane32_swap(lo.x, hi.x, false, false);
-  const auto y = __builtin_amdgcn_permlane32_swap(lo.y, hi.y, false, false);
-  u32x4 v;
-  v.x = x[0];
-  v.y = y[0];
-  v.z = x[1];
-  v.w = y[1];
-  *reinterpret_cast<u32x4*>(dst) = v;
-}
-
-// bf16 features 16 p + 8 h .. + 7 of one block (feature 0 of the block at row + 0).
-__device__ __forceinline__ void store_block_bf16(uint16_t* row, const f32x16& a, int lh) {
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    u32x2 o[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int g = 2 * p + h;
-      o[h].x = pack_bf2(a[4 * g], a[4 * g + 1]);
-      o[h].y = pack_bf2(a[4 * g + 2], a[4 * g + 3]);
-    }
-    store_pair16(row + 16 * p + 8 * lh, o[0], o[1]);
-  }
-}
-
 // row[b * 32 + 8 j + 4 h .. + 3] += group j of block(b) for NB blocks.  All
 // loads are issued before the first store: the compiler keeps the program
 // order of accesses that may alias, so interleaved load-add-store would wait
