@@ -181,7 +181,10 @@ void launch_rmsnorm(float* resid, const float* part, int n_part, int part_rows, 
 // q_norm, where the prefill attention loads it.)
 //
 // One workgroup per (32-position chunk, KV head, sequence); chunks start at
-// multiples of 8 so they hold whole V blocks.  K: 16 lanes per position,
+// multiples of 8 so they hold whole V blocks.  The 8 KV heads of a chunk run
+// as consecutive workgroups on one XCD (workgroup ids are dealt to the 8
+// XCDs in turn), so the chunk's rotary-table rows come from HBM once and
+// the other heads read them from that XCD's L2.  K: 16 lanes per position,
 // lane j holding dims 4j..4j+3 and 64+4j..64+4j+3, so the RoPE pairs stay in
 // the lane and the head's sum of squares is a 16-lane DPP row sum.  V: the
 // chunk's positions are staged in LDS and written to the blocked V cache
@@ -193,59 +196,79 @@ constexpr int KVS_POS = 32;  // positions per workgroup
 __global__ __launch_bounds__(256) void k_kv_store(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ k_norm,
                                                   const float* __restrict__ rope_cos,
                                                   const float* __restrict__ rope_sin, uint16_t* __restrict__ k_cache,
-                                                  uint16_t* __restrict__ v_cache, SeqMap sm, int max_seq) {
+                                                  uint16_t* __restrict__ v_cache, SeqMap sm, int max_seq,
+                                                  int n_chunks) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[KVS_POS][D];
-  const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  // workgroup L: XCD L % 8, slot L / 8; head g = slot % 8 of unit 8 (slot / 8) + L % 8
+  const int slot = blockIdx.x >> 3, g = slot & 7;
+  const int unit = (slot >> 3) * 8 + (blockIdx.x & 7);
+  if (unit >= n_chunks * sm.n) return;  // whole workgroup
+  const int b = unit / n_chunks, chunk = unit - b * n_chunks, tid = threadIdx.x;
   const int T = sm_len(sm, b), row0 = sm_row0(sm, b);
   const int p_first = sm_start(sm, b);
-  const int c0 = (p_first & ~7) + KVS_POS * blockIdx.x;  // first position of the chunk
+  const int c0 = (p_first & ~7) + KVS_POS * chunk;  // first position of the chunk
   const int p_lo = p_first > c0 ? p_first : c0;
   int p_hi = (p_first + T) < (c0 + KVS_POS) ? (p_first + T) : (c0 + KVS_POS);
   p_hi = p_hi < max_seq ? p_hi : max_seq;
   if (p_first < 0 || p_lo >= p_hi) return;  // whole workgroup
   const size_t kv_base = ((size_t)b * HKV + g) * max_seq * D;
-  // ---- V rows of the chunk into LDS, 16 B per lane (zeros outside the range, never written back)
+  // Every load of the workgroup is issued before the first is used, with no
+  // branch between them: positions outside the range read a row of the range
+  // instead (their values are dropped), since a conditional load would make
+  // the compiler wait for each one before issuing the next.
+  auto clamp_p = [&](int p) { return p < p_lo ? p_lo : (p >= p_hi ? p_hi - 1 : p); };
+  const uint16_t* rows = qkv + (size_t)(row0 - p_first) * QKV_N;  // row of position p at rows + p * QKV_N
+  u32x4 vv[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int e = it * 256 + tid;
+    vv[it] = *reinterpret_cast<const u32x4*>(rows + (size_t)clamp_p(c0 + (e >> 4)) * QKV_N + (HQ + HKV + g) * D +
+                                             8 * (e & 15));
+  }
+  constexpr int KIT = KVS_POS / 16;  // K passes of 16 positions
+  const int j4 = 4 * (tid & 15);
+  u32x2 klo[KIT], khi[KIT];
+  f32x4 cs[KIT], sn[KIT];
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) {
+    const int pc = clamp_p(c0 + it * 16 + (tid >> 4));
+    const uint16_t* src = rows + (size_t)pc * QKV_N + (HQ + g) * D;
+    klo[it] = *reinterpret_cast<const u32x2*>(src + j4);
+    khi[it] = *reinterpret_cast<const u32x2*>(src + 64 + j4);
+    const int pr = pc >= MAXPOS ? MAXPOS - 1 : pc;
+    cs[it] = *reinterpret_cast<const f32x4*>(rope_cos + (size_t)pr * ROPE_HALF + j4);
+    sn[it] = *reinterpret_cast<const f32x4*>(rope_sin + (size_t)pr * ROPE_HALF + j4);
+  }
+  const u32x2 g0 = *reinterpret_cast<const u32x2*>(k_norm + j4);
+  const u32x2 g1 = *reinterpret_cast<const u32x2*>(k_norm + 64 + j4);
+  // ---- V rows of the chunk into LDS (zeros outside the range, never written back)
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int e = it * 256 + tid, r = e >> 4, c8 = 8 * (e & 15);
     const int p = c0 + r;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (p >= p_lo && p < p_hi)
-      v = *reinterpret_cast<const u32x4*>(qkv + (size_t)(row0 + p - p_first) * QKV_N + (HQ + HKV + g) * D + c8);
+    const u32x4 v = (p >= p_lo && p < p_hi) ? vv[it] : u32x4{0u, 0u, 0u, 0u};
     *reinterpret_cast<u32x4*>(&tile[r][c8]) = v;
   }
-  // ---- K rows: 16 positions per pass
+  // ---- K rows: 16 positions per pass, 16 lanes per position
+  const float ga[4] = {bf_lo(g0.x), bf_hi(g0.x), bf_lo(g0.y), bf_hi(g0.y)};
+  const float gb[4] = {bf_lo(g1.x), bf_hi(g1.x), bf_lo(g1.y), bf_hi(g1.y)};
 #pragma unroll
-  for (int it = 0; it < KVS_POS / 16; ++it) {
-    const int p = c0 + it * 16 + (tid >> 4), j4 = 4 * (tid & 15);
-    const bool live = p >= p_lo && p < p_hi;
-    float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
-    if (live) {
-      const uint16_t* src = qkv + (size_t)(row0 + p - p_first) * QKV_N + (HQ + g) * D;
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(src + j4);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 64 + j4);
-      x[0] = bf_lo(lo.x), x[1] = bf_hi(lo.x), x[2] = bf_lo(lo.y), x[3] = bf_hi(lo.y);
-      y[0] = bf_lo(hi.x), y[1] = bf_hi(hi.x), y[2] = bf_lo(hi.y), y[3] = bf_hi(hi.y);
-    }
+  for (int it = 0; it < KIT; ++it) {
+    const int p = c0 + it * 16 + (tid >> 4);
+    const float x[4] = {bf_lo(klo[it].x), bf_hi(klo[it].x), bf_lo(klo[it].y), bf_hi(klo[it].y)};
+    const float y[4] = {bf_lo(khi[it].x), bf_hi(khi[it].x), bf_lo(khi[it].y), bf_hi(khi[it].y)};
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) ss += x[i] * x[i] + y[i] * y[i];
     ss = row16_sum(ss);  // the 16 lanes of one position
-    if (live) {
+    if (p >= p_lo && p < p_hi) {
       const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + EPS);
-      const u32x2 g0 = *reinterpret_cast<const u32x2*>(k_norm + j4);
-      const u32x2 g1 = *reinterpret_cast<const u32x2*>(k_norm + 64 + j4);
-      const float ga[4] = {bf_lo(g0.x), bf_hi(g0.x), bf_lo(g0.y), bf_hi(g0.y)};
-      const float gb[4] = {bf_lo(g1.x), bf_hi(g1.x), bf_lo(g1.y), bf_hi(g1.y)};
-      const int pc = p >= MAXPOS ? MAXPOS - 1 : p;
-      const f32x4 c = *reinterpret_cast<const f32x4*>(rope_cos + (size_t)pc * ROPE_HALF + j4);
-      const f32x4 sn = *reinterpret_cast<const f32x4*>(rope_sin + (size_t)pc * ROPE_HALF + j4);
       float o0[4], o1[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float a = x[i] * rinv * ga[i], bb = y[i] * rinv * gb[i];
-        o0[i] = a * c[i] - bb * sn[i];
-        o1[i] = bb * c[i] + a * sn[i];
+        o0[i] = a * cs[it][i] - bb * sn[it][i];
+        o1[i] = bb * cs[it][i] + a * sn[it][i];
       }
       uint16_t* dst = k_cache + kv_base + (size_t)p * D;
       *reinterpret_cast<u32x2*>(dst + j4) = u32x2{pack_bf2(o0[0], o0[1]), pack_bf2(o0[2], o0[3])};
@@ -276,8 +299,10 @@ void launch_kv_store(const uint16_t* qkv, const uint16_t* k_norm, const float* r
   // a run of up to max_T positions from an unaligned start spans at most max_T + 7 positions
   // from the 8-aligned position below its start
   const int n_chunks = (max_T + 7 + KVS_POS - 1) / KVS_POS;
-  hipLaunchKernelGGL(k_kv_store, dim3(n_chunks, HKV, sm.n), dim3(256), 0, s, qkv, k_norm, rope_cos, rope_sin, k_cache,
-                     v_cache, sm, max_seq);
+  static_assert(HKV == 8, "one head per slot of an 8-slot group");
+  const int n_groups = (n_chunks * sm.n + 7) / 8;
+  hipLaunchKernelGGL(k_kv_store, dim3(n_groups * 64), dim3(256), 0, s, qkv, k_norm, rope_cos, rope_sin, k_cache,
+                     v_cache, sm, max_seq, n_chunks);
 }
 
 // ---------------------------------------------------------------- argmax
