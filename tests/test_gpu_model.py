@@ -4,8 +4,13 @@ against the float64 oracle, through the C ABI.
 Greedy tokens follow the protocol in gpu_common.check_greedy_step: the GPU
 runs free, the oracle is teacher-forced on the GPU's tokens, every step's
 logits must be within the relative tolerance, and a token may differ from
-the oracle's argmax only at a near tie inside the measured error.
+the oracle's argmax only at a near tie inside the measured error.  (The
+long-context case compares with stored oracle logits, so there the GPU is
+fed the oracle's tokens instead.)
 """
+import json
+import os
+
 import numpy as np
 import pytest
 
@@ -194,6 +199,58 @@ def test_decode_b32_ctx2048_vs_oracle(lib, models):
             check_greedy_step(rep, forced[i], lgs[i][b], o_logits[i])
         log(f"   seq {b}: tokens {forced}")
     log(f"[model] batch 32 x 2048: {rep}")
+    assert rep.near_ties == 0, rep
+
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.mark.timeout(600)
+def test_long_context_b4_ctx32768_vs_oracle(lib, models):
+    """The long-context workload's shape: batch 4 prompts of 32768 uniform
+    random ids (drawn as the benchmark draws them), prefill, then two decode
+    steps at positions 32768 and 32769.  Sequence 0 against the float64
+    oracle's logits, stored by tests/golden/make_long_context.py (a float64
+    prefill of this length takes about an hour, too long to run here).  The
+    stored run is greedy on the oracle's own tokens, so sequence 0 is fed
+    those tokens here (the other sequences run free); every step's logits
+    must be within the tolerance and the GPU's token must be the oracle's."""
+    B, dev = lib
+    dm, _ = models
+    path = os.path.join(GOLDEN, "long_context_b4_ctx32768_seq0.npz")
+    if not os.path.exists(path):
+        pytest.skip("stored oracle logits not generated yet (tests/golden/make_long_context.py)")
+    z = np.load(path)
+    meta = json.loads(str(z["meta"]))
+    Bn, T, steps = meta["batch"], meta["prompt_len"], meta["steps"]
+    assert meta["weight_seed"] == 0 and meta["sequence"] == 0
+    o_logits = z["logits"].astype(np.float64)
+    o_tokens = [int(t) for t in z["tokens"]]
+    assert o_tokens == [int(O.argmax_lowest(l[None])[0]) for l in o_logits]
+    ids = I.token_ids(meta["id_seed"], (Bn, T))
+    kv = dev.DeviceKV(Bn, T + 8)
+    ws, nb = dev.workspace(Bn, T)
+    logits = torch.empty((Bn, B.VOCAB), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(Bn, dtype=torch.int32, device="cuda")
+    seq = torch.empty(Bn, dtype=torch.int32, device="cuda")
+    log(f"[model] prefill {Bn} x {T}")
+    B.q3_prefill(dm.struct, kv.struct, Bn, T, torch.from_numpy(ids).cuda(), logits, nxt, seq, ws, nb)
+    torch.cuda.synchronize()
+    del ws
+    lgs, toks = [logits[0].cpu().numpy().copy()], [int(nxt[0].item())]
+    wsd, nbd = dev.workspace(Bn, 1)
+    for i in range(steps):
+        nxt[0] = o_tokens[i]
+        B.q3_decode_step(dm.struct, kv.struct, Bn, nxt, seq, T + steps, logits, nxt, wsd, nbd)
+        torch.cuda.synchronize()
+        lgs.append(logits[0].cpu().numpy().copy())
+        toks.append(int(nxt[0].item()))
+    assert seq.cpu().numpy().tolist() == [T + steps] * Bn
+    rep = GreedyReport()
+    for i in range(steps + 1):
+        check_greedy_step(rep, toks[i], lgs[i], o_logits[i])
+        log(f"   step {i}: token {toks[i]} (oracle {o_tokens[i]}), logits rel={rel_err(lgs[i], o_logits[i]):.3e}")
+    log(f"[model] batch 4 x 32768, sequence 0: {rep}")
     assert rep.near_ties == 0, rep
 
 
