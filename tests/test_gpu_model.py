@@ -217,10 +217,7 @@ def test_long_context_b4_ctx32768_vs_oracle(lib, models):
     must be within the tolerance and the GPU's token must be the oracle's."""
     B, dev = lib
     dm, _ = models
-    path = os.path.join(GOLDEN, "long_context_b4_ctx32768_seq0.npz")
-    if not os.path.exists(path):
-        pytest.skip("stored oracle logits not generated yet (tests/golden/make_long_context.py)")
-    z = np.load(path)
+    z = np.load(os.path.join(GOLDEN, "long_context_b4_ctx32768_seq0.npz"))
     meta = json.loads(str(z["meta"]))
     Bn, T, steps = meta["batch"], meta["prompt_len"], meta["steps"]
     assert meta["weight_seed"] == 0 and meta["sequence"] == 0
