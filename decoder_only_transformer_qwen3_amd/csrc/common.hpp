@@ -153,19 +153,6 @@ __device__ __forceinline__ int sm_len(const SeqMap& sm, int s) {
 __device__ __forceinline__ int sm_start(const SeqMap& sm, int s) {
   return sm.pos ? sm.pos[s] : (sm.off ? 0 : sm.start);
 }
-// the sequence holding row m: the last s with off[s] <= m (binary search)
-__device__ __forceinline__ int sm_seq(const SeqMap& sm, int m) {
-  if (!sm.off) return m / sm.T;
-  int lo = 0, hi = sm.n - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (sm.off[mid] <= m)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return lo;
-}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -191,11 +178,6 @@ __device__ __forceinline__ float group_sum_dpp(float v) {
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false));  // half-row mirror
   if constexpr (G >= 16)
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false));  // row mirror
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
 
