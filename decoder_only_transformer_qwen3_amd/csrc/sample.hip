@@ -35,6 +35,12 @@
 //   8..11  draw digits
 //   12     the j-th index among equal keys (only when j > 0)
 // A pass that does not apply to a row returns at once for that row.
+// Fast path: when the top-k select leaves at most min(SP_FAST_CAP, 256 G)
+// candidates (ties included), one launch gathers them into the row's mass
+// histograms (unused until pass 4, which such a row skips) and a second
+// sorts them in one workgroup per row and makes the top-p cut and the draw
+// with the same fixed-point arithmetic as the passes (same token); passes
+// 4-12 then return at once for that row.
 #include <math.h>
 
 #include "common.hpp"
@@ -50,6 +56,7 @@ constexpr int SP_PAD = SP_BINS + 1;
 constexpr int SP_PASSES = 13;
 constexpr int SP_MAX_G = 32;   // chunks per row at most (q3v::sample_chunks)
 constexpr float SP_FIX = 1099511627776.0f;  // 2^40: mass fixed point
+constexpr int SP_FAST_CAP = 1024;            // most candidates the fast path sorts (one workgroup)
 
 // Per-row state, written by the initialising launch and by each pass's
 // finishing workgroup, read by the next launch.
@@ -68,6 +75,9 @@ struct alignas(64) SampRow {
   uint64_t need;      // the running select's remaining count / mass to reach
   uint64_t above;     // mass of the keys above the running select's prefix
   uint64_t kept;      // kept mass (after the top-p cut, or all candidates)
+  uint32_t n_cand;    // candidates after the top-k select (ties included)
+  int fast;           // 1: the fast path finishes this row
+  int n_gath;         // candidates the fast path has gathered so far
 };
 
 // order-preserving map of float32 to uint32 (larger float -> larger key);
@@ -95,6 +105,11 @@ struct SampWs {
   uint32_t* mini;  // [rows][G][256] lowest index per bin (last draw digit)
   uint64_t* best;  // [rows][G] (key << 32 | ~index) maxima
 };
+// fast path: the row's candidates as (key << 32 | ~index), in its mass histograms
+__device__ __forceinline__ uint64_t* fast_list(const SampWs& ws, int r, int G) {
+  return ws.mass + (size_t)r * G * SP_BINS;
+}
+__device__ __forceinline__ int fast_cap(int G) { return G * SP_BINS < SP_FAST_CAP ? G * SP_BINS : SP_FAST_CAP; }
 
 __device__ __forceinline__ void st_dev_u32(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -421,6 +436,9 @@ __global__ __launch_bounds__(SP_T) void k_sample_pass(int pass, const float* __r
       o.above = 0;
       if (kind <= 1) {
         o.lo_key = key;  // candidates: key >= the k-th largest key
+        const uint64_t n_cand = above + n_b;
+        o.n_cand = (uint32_t)(n_cand < 0xffffffffull ? n_cand : 0xffffffffull);
+        o.fast = n_cand <= (uint64_t)fast_cap(G) ? 1 : 0;
       } else if (kind == 2) {
         const uint64_t w = n_b ? m_b / n_b : 0;
         uint64_t keep = w ? (rem + w - 1) / w : n_b;
@@ -439,6 +457,172 @@ __global__ __launch_bounds__(SP_T) void k_sample_pass(int pass, const float* __r
         }
       }
     }
+  }
+}
+
+// ---- fast path, launch 1: chunk blockIdx.x of row blockIdx.y appends its
+// candidates (key >= lo_key) to the row's list.  Each thread takes 16
+// values per step (four 16-byte loads in flight when VEC); a wave with hits
+// reserves its slots with one atomic add.
+template <bool VEC>
+__global__ __launch_bounds__(SP_T) void k_sample_gather(const float* __restrict__ logits, int vocab, int64_t stride,
+                                                        int G, int chunk, SampWs ws) {
+  constexpr int E = 16;
+  const int r = blockIdx.y, g = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const SampRow s = ws.st[r];
+  if (s.mode != 1 || !s.fast) return;
+  const float* x = logits + (size_t)r * stride;
+  const int c0 = g * chunk, c1 = (c0 + chunk) < vocab ? (c0 + chunk) : vocab;
+  const float inv_t = s.inv_t;
+  const uint32_t lo = s.lo_key;
+  uint64_t* list = fast_list(ws, r, G);
+  const int cap = fast_cap(G);
+  // one step: value e of the thread is element idx(e); uniform trip count
+  for (int step = c0; step < c1; step += E * SP_T) {
+    float v[E];
+    int idx[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) idx[e] = VEC ? step + 4 * tid + 4 * SP_T * (e >> 2) + (e & 3) : step + tid + SP_T * e;
+    if (VEC && step + E * SP_T <= c1) {
+#pragma unroll
+      for (int u = 0; u < E / 4; ++u) {
+        const f32x4 q = *reinterpret_cast<const f32x4*>(x + idx[4 * u]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[4 * u + c] = q[c];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) v[e] = idx[e] < c1 ? x[idx[e]] : 0.f;
+    }
+    uint32_t key[E];
+    uint32_t hm = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      key[e] = skey(v[e] * inv_t, 0u);
+      hm |= (uint32_t)(idx[e] < c1 && key[e] >= lo) << e;
+    }
+    const int cnt = __popc(hm);
+    if (__ballot(cnt != 0) == 0ull) continue;
+    int incl = cnt;  // inclusive scan of the counts over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    int wbase = 0;
+    if (lane == 63) wbase = atomicAdd(&ws.st[r].n_gath, incl);
+    wbase = __shfl(wbase, 63, 64);
+    int pos = wbase + incl - cnt;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if ((hm >> e) & 1u) {
+        if (pos < cap) list[pos] = ((uint64_t)key[e] << 32) | (uint32_t)~(uint32_t)idx[e];
+        ++pos;
+      }
+  }
+}
+
+// ---- fast path, launch 2: one workgroup of SP_FT threads per row sorts its
+// candidates by (z descending, index ascending), takes the inclusive mass
+// sums, and makes the top-p cut and the draw with the passes' integer
+// arithmetic: the cut's group keeps ceil(rem / w) members, the draw lands on
+// member (rem - 1) / w of its group, w being the (equal) mass of one member.
+constexpr int SP_FT = SP_FAST_CAP;  // one candidate per thread
+__global__ __launch_bounds__(SP_FT) void k_sample_finish(int G, SampWs ws, int32_t* __restrict__ out) {
+  constexpr int N = SP_FAST_CAP;
+  __shared__ uint64_t e[N];
+  __shared__ uint64_t cum[N];
+  __shared__ uint64_t red[SP_FT / 64];
+  __shared__ int pos_c, pos_s, cnt_g;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const SampRow s = ws.st[r];
+  if (s.mode != 1 || !s.fast) return;
+  // a count that differs from the select's (cannot happen) leaves the row to the passes
+  const int n = s.n_gath;
+  if (n < 1 || n > fast_cap(G) || (uint32_t)n != s.n_cand) return;
+  int P = 1;  // sort the next power of two: entries n .. P-1 are 0 and sort last (no entry is 0)
+  while (P < n) P <<= 1;
+  e[tid] = tid < n ? fast_list(ws, r, G)[tid] : 0ull;
+  __syncthreads();
+  // bitonic sort, descending; thread tid owns the pair (tid, tid ^ j) when tid is its lower end
+  for (int k = 2; k <= P; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int ij = tid ^ j;
+      if (tid < P && ij > tid) {
+        const uint64_t a = e[tid], b = e[ij];
+        if (((tid & k) == 0) ? (a < b) : (a > b)) {
+          e[tid] = b;
+          e[ij] = a;
+        }
+      }
+      __syncthreads();
+    }
+  // inclusive sums of the fixed-point masses
+  uint64_t v = tid < n ? smass(skey_inv((uint32_t)(e[tid] >> 32)), s.zmax) : 0ull;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  if (lane == 63) red[wv] = v;
+  __syncthreads();
+  for (int w = 0; w < wv; ++w) v += red[w];
+  cum[tid] = v;
+  __syncthreads();
+  const uint64_t grand = cum[n - 1];
+  // the position where the inclusive sum first reaches `need`, its key's
+  // group (first position and size), or -1
+  auto cross = [&](uint64_t need) {
+    __syncthreads();  // the previous call's results have been read
+    if (tid == 0) {
+      pos_c = -1;
+      cnt_g = 0;
+    }
+    __syncthreads();
+    if (tid < n && cum[tid] >= need && (tid == 0 || cum[tid - 1] < need)) pos_c = tid;
+    __syncthreads();
+    const int c = pos_c;
+    if (c >= 0 && tid < n) {
+      const uint32_t kc = (uint32_t)(e[c] >> 32);
+      if ((uint32_t)(e[tid] >> 32) == kc) {
+        atomicAdd(&cnt_g, 1);
+        if (tid == 0 || (uint32_t)(e[tid - 1] >> 32) != kc) pos_s = tid;
+      }
+    }
+    __syncthreads();
+    return c;
+  };
+  uint64_t kept = grand;
+  if (s.topp) {
+    const double pz = (double)s.p * (double)grand;
+    uint64_t pp = (uint64_t)ceil(pz);
+    pp = pp < 1 ? 1 : (pp > grand ? grand : pp);
+    if (cross(pp) < 0) {  // masses vanished: keep the row's maximum (written by pass 0)
+      if (tid == 0) ws.st[r].mode = 0;
+      return;
+    }
+    const int sg = pos_s, ng = cnt_g;
+    const uint64_t above = sg > 0 ? cum[sg - 1] : 0ull;
+    const uint64_t w = cum[sg] - above;  // one member's mass
+    const uint64_t rem = pp - above;
+    uint64_t keep = w ? (rem + w - 1) / w : (uint64_t)ng;
+    keep = keep > (uint64_t)ng ? (uint64_t)ng : (keep < 1 ? 1 : keep);
+    kept = above + keep * w;
+  }
+  const uint64_t need = (uint64_t)floor((double)s.u * (double)kept) + 1;
+  if (cross(need) < 0) {
+    if (tid == 0) ws.st[r].mode = 0;
+    return;
+  }
+  if (tid == 0) {
+    const int sg = pos_s, ng = cnt_g;
+    const uint64_t above = sg > 0 ? cum[sg - 1] : 0ull;
+    const uint64_t w = cum[sg] - above;
+    const uint64_t rem = need - above;
+    uint64_t jj = w ? (rem - 1) / w : 0;
+    jj = jj >= (uint64_t)ng ? (ng ? (uint64_t)ng - 1 : 0) : jj;
+    out[r] = (int32_t)~(uint32_t)e[sg + (int)jj];
+    ws.st[r].mode = 0;
   }
 }
 
@@ -463,6 +647,14 @@ void launch_sample(const float* logits, int rows, int vocab, int64_t stride, con
                      top_k, top_p, uniform, ws);
   const bool vec = ((uintptr_t)logits & 15u) == 0 && (stride & 3) == 0;
   for (int pass = 0; pass < SP_PASSES; ++pass) {
+    if (pass == 4) {  // after the top-k select: the fast path for rows with few candidates
+      if (vec)
+        hipLaunchKernelGGL(k_sample_gather<true>, dim3(G, rows), dim3(SP_T), 0, s, logits, vocab, stride, G, chunk, ws);
+      else
+        hipLaunchKernelGGL(k_sample_gather<false>, dim3(G, rows), dim3(SP_T), 0, s, logits, vocab, stride, G, chunk,
+                           ws);
+      hipLaunchKernelGGL(k_sample_finish, dim3(rows), dim3(SP_FT), 0, s, G, ws, out);
+    }
     if (vec)
       hipLaunchKernelGGL(k_sample_pass<true>, dim3(G, rows), dim3(SP_T), 0, s, pass, logits, vocab, stride, G, chunk,
                          ws, out);

@@ -181,3 +181,35 @@ def test_sample_unaligned_rows(lib):
         x = rows[r, :vocab].astype(np.float64)
         want = O.sample(x, float(temps[r]), int(ks[r]), float(ps[r]), float(us[r]))
         assert got[r] == want or _allowed(x, float(temps[r]), int(ks[r]), float(ps[r]), float(us[r]), int(got[r]))
+
+
+def test_sample_candidate_sort_matches_passes(lib):
+    """Rows whose top-k leaves at most min(1024, 256 G) candidates (G the
+    chunks per row: 16 for a call of 32 rows, 1 from 512 rows on) are
+    finished by one workgroup that sorts them; the others by the radix
+    passes.  The same 512 rows with 257 <= k <= 1024 therefore take the
+    passes in one call of 512 rows and the sort in calls of 32 rows: the
+    tokens must be the same, bit for bit."""
+    B = lib
+    rng = np.random.default_rng(65)
+    n = 512
+    scale = rng.choice([0.64, 1.0, 3.0, 8.0], n)
+    rows = (rng.standard_normal((n, V)) * scale[:, None]).astype(np.float32)
+    rows[::5] = np.round(rows[::5] * 16) / 16        # ties, also inside the top-k and top-p cuts
+    temps = rng.choice([0.5, 1.0, 1.7], n).astype(np.float32)
+    ks = rng.integers(257, 1025, n).astype(np.int32)
+    ps = rng.choice([1.0, 0.99, 0.9, 0.6, 0.2], n).astype(np.float32)
+    us = rng.random(n).astype(np.float32)
+    passes = _run(B, rows, V, V, temps, ks, ps, us)
+    sort = np.concatenate([_run(B, rows[i:i + 32], V, V, temps[i:i + 32], ks[i:i + 32], ps[i:i + 32], us[i:i + 32],
+                                timed=i == 0) for i in range(0, n, 32)])
+    z = rows / temps[:, None]
+    kth = np.array([-np.partition(-z[r], ks[r] - 1)[ks[r] - 1] for r in range(n)])
+    n_cand = (z >= kth[:, None]).sum(axis=1)
+    log(f"[sample] {int((n_cand <= 1024).sum())}/{n} rows within the sort's 1024 candidates; "
+        f"{int((passes != sort).sum())} tokens differ")
+    np.testing.assert_array_equal(sort, passes)
+    for r in range(0, n, 16):
+        x = rows[r].astype(np.float64)
+        want = O.sample(x, float(temps[r]), int(ks[r]), float(ps[r]), float(us[r]))
+        assert sort[r] == want or _allowed(x, float(temps[r]), int(ks[r]), float(ps[r]), float(us[r]), int(sort[r]))
