@@ -23,7 +23,7 @@ QKV_ROWS, GATE_UP_ROWS = 4096, 6144
 
 Q3_OK, Q3_ERR_NULL, Q3_ERR_SHAPE, Q3_ERR_POSITION = 0, -1, -2, -3
 Q3_ERR_ALIGN, Q3_ERR_WORKSPACE, Q3_ERR_HIP, Q3_ERR_TOO_LARGE = -4, -5, -6, -7
-NOALLOC_MAX_BYTES = 40 << 20
+NOALLOC_MAX_BYTES = 21 << 20
 
 _vp = ctypes.c_void_p
 

@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libq3.so")
 
 HIP_SOURCES = ["elementwise.hip", "gemm_skinny.hip", "gemm_tiled.hip", "attn_prefill.hip", "attn_decode.hip",
-               "sample.hip"]
+               "sample.hip", "lm_head.hip"]
 HOST_SOURCES = ["api.cpp", "validate.cpp"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.

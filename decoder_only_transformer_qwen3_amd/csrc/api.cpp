@@ -28,7 +28,7 @@ constexpr int GEMV_MAX_ROWS = 8;
 struct Ws {
   float* resid;
   uint16_t *h, *qkv, *ao, *act, *fh;
-  float *part, *tpart, *apart, *logits, *ssq;
+  float *part, *tpart, *apart, *ssq;
   int* tick;  // 64 column-block tickets, then batch * 8 attention tickets
   int n_tick;
   void* amax;
@@ -46,7 +46,6 @@ Ws carve_rows(void* base, int32_t batch, int64_t rows, bool one_token) {
   w.part = reinterpret_cast<float*>(p + L.part);
   w.tpart = reinterpret_cast<float*>(p + L.tpart);
   w.apart = reinterpret_cast<float*>(p + L.apart);
-  w.logits = reinterpret_cast<float*>(p + L.logits);
   w.amax = p + L.amax;
   w.fh = reinterpret_cast<uint16_t*>(p + L.fh);
   w.ssq = reinterpret_cast<float*>(p + L.ssq);
@@ -242,7 +241,7 @@ void run_head(const q3_model* m, const Ws& ws, int B, int T, float* logits, int3
     a.X = X + (size_t)r0 * ldx;
     a.ldx = ldx;
     a.W = U(m->embed);
-    a.out = logits + (size_t)r0 * V;
+    a.out = logits ? logits + (size_t)r0 * V : nullptr;  // null: the caller wants no logits
     a.M = rows;
     a.N = V;
     a.K = C;
@@ -251,7 +250,7 @@ void run_head(const q3_model* m, const Ws& ws, int B, int T, float* logits, int3
     a.ssq = ssq + (size_t)r0 * ssq_ld;
     a.ssq_ld = ssq_ld;
     a.ssq_n = ssq_n;
-    launch_gemm_skinny(a, 1, EPI_LOGITS, s);
+    launch_lm_head(a, s);
   }
   launch_argmax_partials(ws.amax, B, n_part, next_ids, seq_lens, seq_mode, seq_val, in_ids, eos, s, packed);
 }
@@ -403,7 +402,7 @@ int q3_prefill(const q3_model* m, const q3_kv* kv, int32_t batch, int32_t prompt
     c.w_qkv_next = m->layer[(l + 1) % NL].w_qkv;  // after the last layer: the next step's first
     run_layer(c);
   }
-  run_head(m, wsp, batch, prompt_len, last_logits ? last_logits : wsp.logits, next_ids, seq_lens, 1, prompt_len, s);
+  run_head(m, wsp, batch, prompt_len, last_logits, next_ids, seq_lens, 1, prompt_len, s);
   return launch_status();
 }
 
@@ -451,7 +450,7 @@ int q3_prefill_packed(const q3_model* m, const q3_kv* kv, int32_t n_seqs, int32_
     c.w_qkv_next = m->layer[(l + 1) % NL].w_qkv;  // after the last layer: the next step's first
     run_layer(c);
   }
-  run_head(m, wsp, n_seqs, 0, last_logits ? last_logits : wsp.logits, next_ids, seq_lens, 3, 0, s, nullptr, -1,
+  run_head(m, wsp, n_seqs, 0, last_logits, next_ids, seq_lens, 3, 0, s, nullptr, -1,
            &c.sm);
   return launch_status();
 }
@@ -493,7 +492,7 @@ int q3_decode_step_eos(const q3_model* m, const q3_kv* kv, int32_t batch, const 
     c.w_qkv_next = m->layer[(l + 1) % NL].w_qkv;  // after the last layer: the next step's first
     run_layer(c);
   }
-  run_head(m, wsp, batch, 1, logits ? logits : wsp.logits, out_ids, seq_lens, 2, 0, s, in_ids, eos_id);
+  run_head(m, wsp, batch, 1, logits, out_ids, seq_lens, 2, 0, s, in_ids, eos_id);
   return launch_status();
 }
 

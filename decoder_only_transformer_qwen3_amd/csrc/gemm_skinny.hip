@@ -34,12 +34,6 @@
 
 namespace q3 {
 
-__device__ __forceinline__ bool am_better2(float a, int ia, float b, int ib) {
-  const bool an = a != a, bn = b != b;
-  if (an || bn) return an && (!bn || ia < ib);
-  return a > b || (a == b && ia < ib);
-}
-
 template <int NB, int RB, int EPI, int U, int WV>
 __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
   __shared__ float red[WV][RB][NB * 16][17];
@@ -184,30 +178,6 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
           *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + (size_t)m * ldo + n) = o;
         } else if constexpr (EPI == EPI_F32) {
           *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)m * ldo + n) = v;
-        } else if constexpr (EPI == EPI_LOGITS) {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)m * ldo + n) = v;
-          // this block's greedy candidate for row m: lowest index among equal maxima, NaN first
-          float bv = v[0];
-          int bi = n;
-#pragma unroll
-          for (int i = 1; i < 4; ++i)
-            if (am_better2(v[i], n + i, bv, bi)) {
-              bv = v[i];
-              bi = n + i;
-            }
-#pragma unroll
-          for (int o = 1; o <= 2; o <<= 1) {
-            const float ov = __shfl_xor(bv, o, 64);
-            const int oi = __shfl_xor(bi, o, 64);
-            if (am_better2(ov, oi, bv, bi)) {
-              bv = ov;
-              bi = oi;
-            }
-          }
-          if (ng == 0) {
-            float2* ap = reinterpret_cast<float2*>(a.amax_part) + (size_t)m * (N >> 4) + blk;
-            *ap = make_float2(bv, __int_as_float(bi));
-          }
         } else if constexpr (EPI == EPI_ADD_F32) {
           f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)m * ldo + n);
           v = *dst + v;
@@ -415,7 +385,8 @@ static void launch_rb(const SkinnyArgs& a, int n_split, hipStream_t s) {
 // activation rows of its K range once, so from 16 rows on (where that read
 // costs as much as the weights) more weight rows per workgroup pay off, as
 // long as enough workgroups remain to keep every CU streaming: the gate|up
-// projection (384 blocks) takes 2, the vocabulary projection (9496) takes 4.
+// projection (384 blocks) takes 2, a projection as wide as the vocabulary
+// (9496 blocks, through q3_linear) takes 4.
 static int rows_blocks(const SkinnyArgs& a, Epi epi) {
   if (a.M < 16) return 1;
   if (epi == EPI_SILU) return 2;
@@ -446,7 +417,6 @@ void launch_gemm_skinny(SkinnyArgs a, int n_split, Epi epi, hipStream_t s) {
   if (a.ldx == 0) a.ldx = a.K;
   a.kspan = a.K / n_split;
   switch (epi) {
-    case EPI_LOGITS: launch_epi<EPI_LOGITS>(a, n_split, s); break;
     case EPI_BF16: launch_epi<EPI_BF16>(a, n_split, s); break;
     case EPI_F32: launch_epi<EPI_F32>(a, n_split, s); break;
     case EPI_ADD_F32: launch_epi<EPI_ADD_F32>(a, n_split, s); break;
@@ -456,7 +426,7 @@ void launch_gemm_skinny(SkinnyArgs a, int n_split, Epi epi, hipStream_t s) {
 }
 
 void launch_gemm_skinny(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo, int n_split,
-                        Epi epi, hipStream_t s, void* amax_part) {
+                        Epi epi, hipStream_t s) {
   SkinnyArgs a{};
   a.X = X;
   a.W = W;
@@ -465,7 +435,6 @@ void launch_gemm_skinny(const uint16_t* X, const uint16_t* W, void* out, int M, 
   a.N = N;
   a.K = K;
   a.ldo = ldo;
-  a.amax_part = amax_part;
   launch_gemm_skinny(a, n_split, epi, s);
 }
 

@@ -14,7 +14,6 @@ enum Epi : int {
   EPI_ADD_F32 = 2,  // out f32 [M, ldo] += result (residual add)
   EPI_SILU = 3,     // W rows are [gate; up]; out bf16 [M, ldo] = silu(gate) * up
   EPI_PARTIAL = 4,  // out f32 [split][M][N] partial sums over a K range
-  EPI_LOGITS = 5,   // out f32 [M, ldo] and, per 16-column block, the block's (max, argmax) per row
 };
 
 // x[m] = E[ids[m]] widened to f32 (one row of 1024 per token); with a gain
@@ -61,7 +60,7 @@ struct SkinnyArgs {
   const uint16_t* W;  // weights [N, K]
   void* out;
   int M, N, K, ldo, ldx, kspan;
-  void* amax_part;    // EPI_LOGITS: per-16-column (max, argmax) of each row
+  void* amax_part;    // launch_lm_head: per-16-column (max, argmax) of each row
   // Optional input-norm scale: X holds bf16(gamma * r); output row m is
   // multiplied by 1 / sqrt(sum_{j<ssq_n} ssq[m * ssq_ld + j] / 1024 + eps).
   // ssq_n (also the layout of ssq_out below) is NSQ for up to 8 rows, else NSQ_BLK.
@@ -81,12 +80,18 @@ struct SkinnyArgs {
 };
 void launch_gemm_skinny(SkinnyArgs a, int n_split, Epi epi, hipStream_t s);
 
+// Tied lm_head over up to 64 rows: out [M][ldo] (skipped when out is null)
+// = (1 / rms) * X E^T for E = W [151936][1024], and amax_part [M][9496]
+// float2 = each 16-column block's (max, argmax) per row.  Uses X, ldx, W,
+// out, M, ldo, amax_part, ssq, ssq_ld, ssq_n of the arguments.
+void launch_lm_head(const SkinnyArgs& a, hipStream_t s);
+
 // resid[M][1024] += X[M][K] W[1024][K]^T for M <= 8, K in {1024, 2048, 3072};
 // with a gain also hg = bf16(gamma * r) and ssq_out [M][256].
 void launch_gemv_resid(const uint16_t* X, const uint16_t* W, int K, float* resid, int M, const uint16_t* gamma,
                        uint16_t* hg, float* ssq_out, hipStream_t s);
 void launch_gemm_skinny(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo,
-                        int n_split, Epi epi, hipStream_t s, void* amax_part = nullptr);
+                        int n_split, Epi epi, hipStream_t s);
 
 // Copy of the merged q|k|v rows and the q/k gains with the q and k rows of
 // every head (and the gains) permuted by P(j) = 2j (j < 64), 2(j-64)+1.

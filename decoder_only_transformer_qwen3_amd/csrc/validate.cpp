@@ -33,7 +33,6 @@ WsLayout ws_layout_rows(int32_t batch, int64_t rows, bool one_token) {
   L.part = take(M <= (size_t)SKINNY_MAX_ROWS ? (size_t)PART_MAX_SPLIT * M * Q3_HIDDEN * 4 : 0);
   L.tpart = take((size_t)tiled_part_bytes((int64_t)M));
   L.apart = take(n_tokens == 1 ? (size_t)batch * Q3_N_HEADS * DEC_SPLIT_MAX * (Q3_HEAD_DIM + 2) * 4 : 0);
-  L.logits = take((size_t)batch * Q3_VOCAB * 4);
   L.amax = take((size_t)batch * (Q3_VOCAB / 16) * 8);
   L.fh = take((size_t)batch * Q3_HIDDEN * 2);
   L.ssq = take(M * (Q3_HIDDEN / 4) * 4);

@@ -16,7 +16,7 @@ constexpr int SKINNY_MAX_ROWS = 64;  // row counts up to this use the skinny GEM
 constexpr int64_t MAX_TOKENS = 1 << 22;
 
 struct WsLayout {
-  size_t resid, h, qkv, ao, act, part, tpart, apart, logits, amax, fh, ssq, tick;
+  size_t resid, h, qkv, ao, act, part, tpart, apart, amax, fh, ssq, tick;
   size_t total;
 };
 

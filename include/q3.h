@@ -251,7 +251,7 @@ int q3_decode_step_eos(const q3_model *m, const q3_kv *kv, int32_t batch, const 
  * the scratch needs to start at zero (the step clears its own tickets).
  * Errors: those of q3_decode_step_eos, and Q3_ERR_TOO_LARGE when
  * q3_workspace_bytes(batch, 1) exceeds Q3_NOALLOC_MAX_BYTES (batch > 32). */
-#define Q3_NOALLOC_MAX_BYTES (40u << 20)
+#define Q3_NOALLOC_MAX_BYTES (21u << 20)
 int q3_decode_step_noalloc(const q3_model *m, const q3_kv *kv, int32_t batch, const int32_t *in_ids,
                            int32_t *seq_lens, int32_t max_len_hint, int32_t eos_id, float *logits,
                            int32_t *out_ids, void *stream);

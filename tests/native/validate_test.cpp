@@ -42,8 +42,8 @@ int main() {
   EXPECT_EQ(ws_layout(1, 0).total, 0);
   const WsLayout L1 = ws_layout(1, 16), L2 = ws_layout(32, 1), L3 = ws_layout(8, 4096);
   EXPECT_EQ(L1.total > 0, 1);
-  EXPECT_EQ(L1.apart, L1.logits);              // no decode partials for multi-token calls
-  EXPECT_EQ(L2.apart < L2.logits, 1);          // decode partials present for one-token calls
+  EXPECT_EQ(L1.apart, L1.amax);                // no decode partials for multi-token calls
+  EXPECT_EQ(L2.apart < L2.amax, 1);            // decode partials present for one-token calls
   EXPECT_EQ(L3.part, L3.apart);                // no skinny partials above 64 rows
   EXPECT_EQ(L1.resid % 256, 0); EXPECT_EQ(L1.h % 256, 0); EXPECT_EQ(L1.fh % 256, 0);
   EXPECT_EQ(L3.total >= (size_t)8 * 4096 * (1024 * 4 + 1024 * 2 + 4096 * 2 + 2048 * 2 + 3072 * 2), 1);
