@@ -12,8 +12,7 @@
 // dims (i, i+64) sit in lanes j and j^8 (a row rotate by 8).
 //
 // Grid (split, KV head g, sequence b); each workgroup reads its key range of
-// K and V once for both query heads 2g, 2g+1.  Its waves (8 when the
-// caches are far larger than the last-level cache, else 4) take 32-key
+// K and V once for both query heads 2g, 2g+1.  Its 4 waves take 32-key
 // tiles round-robin and each keeps its own online softmax, on
 // v_mfma_f32_16x16x32_bf16 (lane l: A row l%16, B column l%16, k-slot
 // (l/16, j); C column l%16, rows 4(l/16)+i):
@@ -145,7 +144,6 @@ static_assert(WARM_PER_XCD * WARM_LOADS >= WARM_UNITS, "every unit needs a load 
 __device__ __forceinline__ void warm_weights(const uint8_t* __restrict__ wo, const uint8_t* __restrict__ wgu,
                                              const uint8_t* __restrict__ wdown, const uint8_t* __restrict__ wqkv,
                                              int j) {
-  if (threadIdx.x >= 256) return;  // 8-wave workgroups: four waves cover a unit
   const int x = j & 7, r = j >> 3;  // XCD of this workgroup, its rank there
   const size_t t16 = (size_t)threadIdx.x * 16;
   u32x4 v[WARM_LOADS];
@@ -487,8 +485,8 @@ void launch_attn_decode(const uint16_t* qkv, const uint16_t* q_norm, const uint1
                         uint16_t* out, int B, int max_seq, const int32_t* pos_dev, int start, int n_split,
                         bool streaming, hipStream_t s, const void* warm_o, const void* warm_gate_up,
                         const void* warm_down, const void* warm_qkv) {
-  // streaming: caches far larger than the last-level cache, 8-wave workgroups
-  // with nontemporal loads; otherwise 4-wave workgroups with ordinary loads
+  // streaming: caches far larger than the last-level cache, nontemporal
+  // loads; otherwise ordinary loads (4-wave workgroups either way)
   // warming workgroups: whole z-slices of n_split * 8 after the B sequences
   // (so their linear ids keep j's residue modulo 8), 8 * WARM_PER_XCD or more
   const bool warm = warm_o && warm_gate_up && warm_down && warm_qkv;
@@ -502,8 +500,8 @@ void launch_attn_decode(const uint16_t* qkv, const uint16_t* q_norm, const uint1
                      static_cast<const uint8_t*>(warm_down), \
                      static_cast<const uint8_t*>(warm_qkv))
   if (streaming) {
-    if (n_split == 1) Q3_DEC_LAUNCH(true, 8, true);
-    else Q3_DEC_LAUNCH(true, 8, false);
+    if (n_split == 1) Q3_DEC_LAUNCH(true, 4, true);
+    else Q3_DEC_LAUNCH(true, 4, false);
   } else {
     if (n_split == 1) Q3_DEC_LAUNCH(false, 4, true);
     else Q3_DEC_LAUNCH(false, 4, false);

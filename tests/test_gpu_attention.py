@@ -221,7 +221,7 @@ def test_attention_decode_cached_split(lib, rope, batch, max_seq, positions):
 
 @pytest.mark.parametrize("max_seq,positions", [
     (256, (160, 37)),   # cached KV, one split, 4-wave workgroups
-    (4096, (4000,)),    # streaming KV, 8 splits, 8-wave workgroups
+    (4096, (4000,)),    # streaming KV, 8 splits
 ])
 def test_attention_decode_warm_matches_plain(lib, rope, max_seq, positions):
     """The entry point that also reads weights ahead into L2 (batch 1: the
