@@ -29,7 +29,7 @@ struct Ws {
   float* resid;
   uint16_t *h, *qkv, *ao, *act, *fh;
   float *part, *tpart, *apart, *ssq;
-  int* tick;  // 64 column-block tickets, then batch * 8 attention tickets
+  int* tick;  // 64 column-block tickets, batch * 8 attention tickets, the lm_head ticket
   int n_tick;
   void* amax;
 };
@@ -233,8 +233,18 @@ void run_head(const q3_model* m, const Ws& ws, int B, int T, float* logits, int3
     ssq = ws.ssq;
     ssq_ld = ssq_n;
   }
-  // logits plus each 16-row weight block's (max, argmax) per sequence
+  // logits (when asked for) and the greedy token of each sequence; the
+  // candidates of the lm_head's workgroups go to ws.amax, its ticket follows
+  // the attention tickets
   constexpr int n_part = V / 16;
+  HeadPick pick{};
+  pick.out_idx = next_ids;
+  pick.seq_lens = seq_lens;
+  pick.seq_mode = seq_mode;
+  pick.seq_val = seq_val;
+  pick.in_ids = in_ids;
+  pick.eos = eos;
+  pick.sm = packed ? *packed : SeqMap{nullptr, nullptr, 0, 1, 0, 0};
   for (int r0 = 0; r0 < B; r0 += q3v::SKINNY_MAX_ROWS) {
     const int rows = (B - r0) < q3v::SKINNY_MAX_ROWS ? (B - r0) : q3v::SKINNY_MAX_ROWS;
     SkinnyArgs a{};
@@ -250,9 +260,9 @@ void run_head(const q3_model* m, const Ws& ws, int B, int T, float* logits, int3
     a.ssq = ssq + (size_t)r0 * ssq_ld;
     a.ssq_ld = ssq_ld;
     a.ssq_n = ssq_n;
-    launch_lm_head(a, s);
+    pick.r0 = r0;
+    launch_lm_head(a, pick, ws.tick + q3v::head_ticket(B), s);
   }
-  launch_argmax_partials(ws.amax, B, n_part, next_ids, seq_lens, seq_mode, seq_val, in_ids, eos, s, packed);
 }
 
 inline int launch_status() { return hipGetLastError() == hipSuccess ? Q3_OK : Q3_ERR_HIP; }

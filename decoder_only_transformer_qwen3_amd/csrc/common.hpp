@@ -87,6 +87,18 @@ __device__ __forceinline__ float ld_dev(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+__device__ __forceinline__ void st_dev_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev_u32(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev_u64(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -152,6 +164,30 @@ __device__ __forceinline__ int sm_len(const SeqMap& sm, int s) {
 }
 __device__ __forceinline__ int sm_start(const SeqMap& sm, int s) {
   return sm.pos ? sm.pos[s] : (sm.off ? 0 : sm.start);
+}
+
+// Greedy choice ("手写Qwen3-0.6B推理" §推理) over (value, index) candidates.
+// Order: NaN above every number (first NaN wins), otherwise larger value,
+// ties to the lower index.
+__device__ __forceinline__ bool am_better(float a, int ia, float b, int ib) {
+  const bool an = a != a, bn = b != b;
+  if (an || bn) return an && (!bn || ia < ib);
+  return a > b || (a == b && ia < ib);
+}
+
+// The chosen token of row r: out_idx[r], and the row's sequence length.
+// seq_mode 2 with eos >= 0: a row whose input token in_ids[r] is eos has
+// finished; it keeps its length and emits eos again (in_ids may alias
+// out_idx: it is read first).
+// seq_mode 3 (packed prefill): seq_lens[r] = start + rows of sequence r.
+__device__ __forceinline__ void am_finish(int r, int bi, int32_t* out_idx, int32_t* seq_lens, int seq_mode,
+                                          int seq_val, const int32_t* in_ids = nullptr, int eos = -1,
+                                          const SeqMap* sm = nullptr) {
+  const bool fin = seq_mode == 2 && eos >= 0 && in_ids[r] == eos;
+  out_idx[r] = fin ? eos : bi;
+  if (seq_mode == 1) seq_lens[r] = seq_val;
+  if (seq_mode == 2 && !fin) seq_lens[r] += 1;
+  if (seq_mode == 3) seq_lens[r] = sm_start(*sm, r) + sm_len(*sm, r);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -307,14 +307,6 @@ void launch_kv_store(const uint16_t* qkv, const uint16_t* k_norm, const float* r
 
 // ---------------------------------------------------------------- argmax
 // Greedy choice over one row per block ("手写Qwen3-0.6B推理" §推理).
-// Order: NaN above every number (first NaN wins), otherwise larger value,
-// ties to the lower index.
-__device__ __forceinline__ bool am_better(float a, int ia, float b, int ib) {
-  const bool an = a != a, bn = b != b;
-  if (an || bn) return an && (!bn || ia < ib);
-  return a > b || (a == b && ia < ib);
-}
-
 __device__ __forceinline__ void am_wave_block_reduce(float& best, int& bi, float* sv, int* si) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -338,20 +330,6 @@ __device__ __forceinline__ void am_wave_block_reduce(float& best, int& bi, float
         bi = si[w];
       }
   }
-}
-
-// seq_mode 2 with eos >= 0: a row whose input token in_ids[r] is eos has
-// finished; it keeps its length and emits eos again (in_ids may alias
-// out_idx: it is read first).
-// seq_mode 3 (packed prefill): seq_lens[r] = start + rows of sequence r.
-__device__ __forceinline__ void am_finish(int r, int bi, int32_t* out_idx, int32_t* seq_lens, int seq_mode,
-                                          int seq_val, const int32_t* in_ids = nullptr, int eos = -1,
-                                          const SeqMap* sm = nullptr) {
-  const bool fin = seq_mode == 2 && eos >= 0 && in_ids[r] == eos;
-  out_idx[r] = fin ? eos : bi;
-  if (seq_mode == 1) seq_lens[r] = seq_val;
-  if (seq_mode == 2 && !fin) seq_lens[r] += 1;
-  if (seq_mode == 3) seq_lens[r] = sm_start(*sm, r) + sm_len(*sm, r);
 }
 
 // One block of 1024 threads per row; 16 B loads when the row is 16-byte
@@ -414,45 +392,6 @@ void launch_argmax(const float* logits, int rows, int vocab, int64_t row_stride,
                    int32_t* seq_lens, int seq_mode, int seq_val, hipStream_t s) {
   hipLaunchKernelGGL(k_argmax, dim3(rows), dim3(1024), 0, s, logits, vocab, row_stride, out_idx, seq_lens, seq_mode,
                      seq_val);
-}
-
-// Reduce the lm_head's per-block (value, index) candidates of one row.
-__global__ __launch_bounds__(1024) void k_argmax_partials(const float2* __restrict__ part, int n_part,
-                                                          int32_t* out_idx, int32_t* __restrict__ seq_lens,
-                                                          int seq_mode, int seq_val, const int32_t* in_ids,
-                                                          int eos, SeqMap sm) {
-  __shared__ float sv[16];
-  __shared__ int si[16];
-  const int r = blockIdx.x, tid = threadIdx.x;
-  const float2* row = part + (size_t)r * n_part;
-  float best = -INFINITY;
-  int bi = 0x7fffffff;
-  for (int base = 0; base < n_part; base += 1024 * 4) {
-    float2 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = base + u * 1024 + tid;
-      v[u] = i < n_part ? row[i] : make_float2(-INFINITY, __int_as_float(0x7fffffff));
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int idx = __float_as_int(v[u].y);
-      if (am_better(v[u].x, idx, best, bi)) {
-        best = v[u].x;
-        bi = idx;
-      }
-    }
-  }
-  am_wave_block_reduce(best, bi, sv, si);
-  if (tid == 0) am_finish(r, bi, out_idx, seq_lens, seq_mode, seq_val, in_ids, eos, &sm);
-}
-
-void launch_argmax_partials(const void* part, int rows, int n_part, int32_t* out_idx, int32_t* seq_lens,
-                            int seq_mode, int seq_val, const int32_t* in_ids, int eos, hipStream_t s,
-                            const SeqMap* sm) {
-  const SeqMap none{nullptr, nullptr, 0, 1, 0, 0};
-  hipLaunchKernelGGL(k_argmax_partials, dim3(rows), dim3(1024), 0, s, static_cast<const float2*>(part), n_part,
-                     out_idx, seq_lens, seq_mode, seq_val, in_ids, eos, sm ? *sm : none);
 }
 
 // ---------------------------------------------------------------------------

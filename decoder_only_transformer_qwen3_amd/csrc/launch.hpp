@@ -60,7 +60,7 @@ struct SkinnyArgs {
   const uint16_t* W;  // weights [N, K]
   void* out;
   int M, N, K, ldo, ldx, kspan;
-  void* amax_part;    // launch_lm_head: per-16-column (max, argmax) of each row
+  void* amax_part;    // launch_lm_head: its workgroups' (max, argmax) candidates
   // Optional input-norm scale: X holds bf16(gamma * r); output row m is
   // multiplied by 1 / sqrt(sum_{j<ssq_n} ssq[m * ssq_ld + j] / 1024 + eps).
   // ssq_n (also the layout of ssq_out below) is NSQ for up to 8 rows, else NSQ_BLK.
@@ -80,11 +80,26 @@ struct SkinnyArgs {
 };
 void launch_gemm_skinny(SkinnyArgs a, int n_split, Epi epi, hipStream_t s);
 
+// Greedy choice of the rows r0 .. r0 + M - 1 of a head call: out_idx[r],
+// and seq_lens[r] by seq_mode (1: = seq_val; 2: += 1, except that with
+// eos >= 0 a row whose input token in_ids[r] is eos has finished and emits
+// eos again with its length kept; 3: start + rows of sequence r of sm,
+// packed prefill).
+struct HeadPick {
+  int32_t* out_idx;
+  int32_t* seq_lens;
+  int seq_mode, seq_val;
+  const int32_t* in_ids;
+  int eos;
+  SeqMap sm;  // seq_mode 3 only
+  int r0;
+};
 // Tied lm_head over up to 64 rows: out [M][ldo] (skipped when out is null)
-// = (1 / rms) * X E^T for E = W [151936][1024], and amax_part [M][9496]
-// float2 = each 16-column block's (max, argmax) per row.  Uses X, ldx, W,
-// out, M, ldo, amax_part, ssq, ssq_ld, ssq_n of the arguments.
-void launch_lm_head(const SkinnyArgs& a, hipStream_t s);
+// = (1 / rms) * X E^T for E = W [151936][1024], and the greedy token of
+// each row (pick).  Uses X, ldx, W, out, M, ldo, ssq, ssq_ld, ssq_n of the
+// arguments; amax_part is scratch of at least (number of CUs) * M float2
+// and `ticket` one int that is zero on entry (and left zero).
+void launch_lm_head(const SkinnyArgs& a, const HeadPick& pick, int* ticket, hipStream_t s);
 
 // resid[M][1024] += X[M][K] W[1024][K]^T for M <= 8, K in {1024, 2048, 3072};
 // with a gain also hg = bf16(gamma * r) and ssq_out [M][256].
@@ -131,15 +146,6 @@ void launch_attn_decode(const uint16_t* qkv, const uint16_t* q_norm, const uint1
                         bool streaming, hipStream_t s, const void* warm_o = nullptr,
                         const void* warm_gate_up = nullptr, const void* warm_down = nullptr,
                         const void* warm_qkv = nullptr);
-
-// Final greedy choice from the lm_head's per-block (max, argmax) partials:
-// part is [rows][n_part] of (float value, int index).  seq_mode as below.
-// With seq_mode 2 and eos >= 0, rows whose input token in_ids[r] is eos
-// have finished: they emit eos and keep their length.
-// seq_mode 3: seq_lens[r] = start + rows of sequence r of *sm (packed prefill).
-void launch_argmax_partials(const void* part, int rows, int n_part, int32_t* out_idx, int32_t* seq_lens,
-                            int seq_mode, int seq_val, const int32_t* in_ids, int eos, hipStream_t s,
-                            const SeqMap* sm = nullptr);
 
 // Row argmax (lowest index on ties, first NaN wins).  seq_mode: 0 none,
 // 1 seq_lens[r] = seq_val, 2 seq_lens[r] += 1 (done after the argmax).

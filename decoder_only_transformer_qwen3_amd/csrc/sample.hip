@@ -111,19 +111,6 @@ __device__ __forceinline__ uint64_t* fast_list(const SampWs& ws, int r, int G) {
 }
 __device__ __forceinline__ int fast_cap(int G) { return G * SP_BINS < SP_FAST_CAP ? G * SP_BINS : SP_FAST_CAP; }
 
-__device__ __forceinline__ void st_dev_u32(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev_u64(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t ld_dev_u32(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld_dev_u64(const uint64_t* p) {
-  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // inclusive scan of one uint64 per thread over the 256 threads
 __device__ __forceinline__ uint64_t block_incl_scan_u64(uint64_t v, uint64_t* lds4) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;

@@ -61,7 +61,8 @@ inline int64_t tiled_part_bytes(int64_t rows) {
 }
 
 // Workgroup tickets in the workspace: 64 column blocks + 8 per sequence.
-inline int ticket_count(int32_t batch) { return 64 + 8 * batch; }
+inline int ticket_count(int32_t batch) { return 64 + 8 * batch + 1; }
+inline int head_ticket(int32_t batch) { return 64 + 8 * batch; }  // index of the lm_head's ticket
 
 // Decode attention over `batch` sequences of at most `ctx` keys: whether it
 // runs in its streaming configuration (caches far larger than the
