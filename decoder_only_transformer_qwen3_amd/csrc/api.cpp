@@ -151,7 +151,7 @@ inline void skinny_residual(const LayerCtx& c, const uint16_t* X, const void* W,
 }
 
 // One decoder layer ("手写Qwen3-0.6B推理" §Qwen3DecoderLayer).
-// Up to 64 rows (skinny path) the layer expects ws.h = bf16(gamma_in * r)
+// Up to 128 rows (skinny path) the layer expects ws.h = bf16(gamma_in * r)
 // and ws.ssq = the row sums of squares, and leaves the same for gamma_next;
 // above that the norms run as separate kernels around the tiled GEMMs.
 void run_layer(const LayerCtx& c) {
@@ -245,8 +245,8 @@ void run_head(const q3_model* m, const Ws& ws, int B, int T, float* logits, int3
   pick.in_ids = in_ids;
   pick.eos = eos;
   pick.sm = packed ? *packed : SeqMap{nullptr, nullptr, 0, 1, 0, 0};
-  for (int r0 = 0; r0 < B; r0 += q3v::SKINNY_MAX_ROWS) {
-    const int rows = (B - r0) < q3v::SKINNY_MAX_ROWS ? (B - r0) : q3v::SKINNY_MAX_ROWS;
+  for (int r0 = 0; r0 < B; r0 += q3v::LM_HEAD_MAX_ROWS) {
+    const int rows = (B - r0) < q3v::LM_HEAD_MAX_ROWS ? (B - r0) : q3v::LM_HEAD_MAX_ROWS;
     SkinnyArgs a{};
     a.X = X + (size_t)r0 * ldx;
     a.ldx = ldx;

@@ -204,12 +204,13 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
-// Sum over aligned groups of G = 4, 8 or 16 lanes (DPP only); every lane of
-// a group receives the total.  Every lane must be active.
+// Sum over aligned groups of G = 2, 4, 8 or 16 lanes (DPP only); every lane
+// of a group receives the total.  Every lane must be active.
 template <int G>
 __device__ __forceinline__ float group_sum_dpp(float v) {
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false));  // lane ^ 1
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false));  // lane ^ 2
+  if constexpr (G >= 4)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false));  // lane ^ 2
   if constexpr (G >= 8)
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false));  // half-row mirror
   if constexpr (G >= 16)

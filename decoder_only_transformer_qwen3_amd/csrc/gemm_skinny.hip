@@ -1,4 +1,4 @@
-// Skinny GEMM for decode-sized row counts (M <= 64 tokens):
+// Skinny GEMM for decode-sized row counts (M <= 128 tokens):
 //   out = X[M, K] * W[N, K]^T
 // Bandwidth-bound on the weights, so every weight byte is read exactly once
 // per call and streamed straight from HBM into MFMA operands (no LDS
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
   // norm statistics are loaded first so their latency hides behind the
   // weight stream: SG threads share a row, each reading NSQ / SG partials
   // (a.ssq_n is NSQ only for up to 8 rows, so SQV below covers both layouts)
-  constexpr int SG = NB == 1 ? 16 : (NB == 2 ? 8 : 4);
+  constexpr int SG = NB == 1 ? 16 : (NB == 2 ? 8 : (NB <= 4 ? 4 : 2));
   constexpr int SQV = NB == 1 ? NSQ / SG / 4 : NSQ_BLK / SG / 4;
   const int sqv = a.ssq_n / (SG * 4);
   const int sm = t / SG;
@@ -378,6 +378,15 @@ static void launch_rb(const SkinnyArgs& a, int n_split, hipStream_t s) {
       return;
     }
   }
+  // Above 64 rows each k-step loads NB activation chunks per lane: 8 waves
+  // spread the k-steps so that fewer rounds of loads run one after another
+  // (one row block: with two, 8 waves would spill).
+  if constexpr (NB > 4 && RB == 1) {
+    if (((a.kspan >> 5) % 16) == 0) {
+      launch_wv<NB, RB, EPI, 8>(a, gx, n_split, s);
+      return;
+    }
+  }
   launch_wv<NB, RB, EPI, 4>(a, gx, n_split, s);
 }
 
@@ -386,7 +395,7 @@ static void launch_rb(const SkinnyArgs& a, int n_split, hipStream_t s) {
 // costs as much as the weights) more weight rows per workgroup pay off, as
 // long as enough workgroups remain to keep every CU streaming: the gate|up
 // projection (384 blocks) takes 2, a projection as wide as the vocabulary
-// (9496 blocks, through q3_linear) takes 4.
+// (9496 blocks, through q3_linear) takes 4 (2 above 64 rows).
 static int rows_blocks(const SkinnyArgs& a, Epi epi) {
   if (a.M < 16) return 1;
   if (epi == EPI_SILU) return 2;
@@ -397,7 +406,7 @@ static int rows_blocks(const SkinnyArgs& a, Epi epi) {
 template <int NB, int EPI>
 static void launch_nb(const SkinnyArgs& a, int n_split, hipStream_t s) {
   switch (rows_blocks(a, static_cast<Epi>(EPI))) {
-    case 4: launch_rb<NB, 4, EPI>(a, n_split, s); break;
+    case 4: launch_rb<NB, (NB <= 4 ? 4 : 2), EPI>(a, n_split, s); break;  // (4 x 8 blocks would spill)
     case 2: launch_rb<NB, 2, EPI>(a, n_split, s); break;
     default: launch_rb<NB, 1, EPI>(a, n_split, s); break;
   }
@@ -409,7 +418,11 @@ static void launch_epi(const SkinnyArgs& a, int n_split, hipStream_t s) {
     case 1: launch_nb<1, EPI>(a, n_split, s); break;
     case 2: launch_nb<2, EPI>(a, n_split, s); break;
     case 3: launch_nb<3, EPI>(a, n_split, s); break;
-    default: launch_nb<4, EPI>(a, n_split, s); break;
+    case 4: launch_nb<4, EPI>(a, n_split, s); break;
+    case 5: launch_nb<5, EPI>(a, n_split, s); break;
+    case 6: launch_nb<6, EPI>(a, n_split, s); break;
+    case 7: launch_nb<7, EPI>(a, n_split, s); break;
+    default: launch_nb<8, EPI>(a, n_split, s); break;
   }
 }
 

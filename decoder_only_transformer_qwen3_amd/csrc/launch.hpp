@@ -53,7 +53,7 @@ void launch_kv_store(const uint16_t* qkv, const uint16_t* k_norm, const float* r
 void launch_gemm_tiled(const uint16_t* X, const uint16_t* W, void* out, int M, int N, int K, int ldo,
                        Epi epi, hipStream_t s, int n_split = 1, float* part = nullptr, bool reduce = true);
 
-// MFMA skinny GEMM for M <= 64 rows (weight streaming), split into n_split K ranges.
+// MFMA skinny GEMM for M <= 128 rows (weight streaming), split into n_split K ranges.
 // Requires N % 16 == 0 and (K / n_split) % 512 == 0; EPI_PARTIAL writes [n_split][M][N].
 struct SkinnyArgs {
   const uint16_t* X;  // activations, row m at X + m * ldx (ldx = 0 means K)

@@ -12,7 +12,8 @@ namespace q3v {
 
 constexpr int PART_MAX_SPLIT = 8;    // skinny-GEMM K splits held in the workspace
 constexpr int DEC_SPLIT_MAX = 64;    // decode-attention splits held in the workspace
-constexpr int SKINNY_MAX_ROWS = 64;  // row counts up to this use the skinny GEMM
+constexpr int SKINNY_MAX_ROWS = 128;  // row counts up to this use the skinny GEMM
+constexpr int LM_HEAD_MAX_ROWS = 64;   // rows per lm_head launch
 constexpr int64_t MAX_TOKENS = 1 << 22;
 
 struct WsLayout {

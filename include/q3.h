@@ -312,7 +312,7 @@ enum {
 };
 
 /* Helper: one projection y = x W^T on the same MFMA GEMM kernels the model
- * uses (skinny weight-streaming kernel for m <= 64 rows, LDS-tiled kernel
+ * uses (skinny weight-streaming kernel for m <= 128 rows, LDS-tiled kernel
  * above), e.g. the tied lm_head of "手写Qwen3-0.6B推理" §Qwen3Model or a
  * merged projection of "第 3 章" §3.3/§3.4.
  *   x    bf16 [m, k] row-major;  w  bf16 [n, k] row-major ([out, in]).

@@ -2,10 +2,10 @@
 against the float64 oracle, through the C ABI.
 
 Shapes cover the one-layer workload (1 x 16 tokens), the skinny/tiled GEMM
-boundary (64 / 65 rows), several tiles with a ragged tail, a multi-token
+boundary (128 / 129 rows), several tiles with a ragged tail, a multi-token
 chunk at an offset into a filled cache, decode-shaped calls (one token) at
 small, capacity-edge and full sizes (batch 32 over 2048 cached positions,
-batch 4 over 32768, 65 rows on the tiled GEMMs), the last position the
+batch 4 over 32768, 129 rows on the tiled GEMMs), the last position the
 rotary table holds (40959), and the 8 x 4096 prefill shape (one sequence
 checked against the oracle).
 """
@@ -88,8 +88,10 @@ def run_layer_case(lib, layer0, rope, batch, T, start, max_seq, check_seqs=None,
 
 @pytest.mark.parametrize("batch,T,start,max_seq", [
     (1, 16, 0, 16),       # one-layer workload: 1 x 16 tokens, positions 0..15
-    (1, 64, 0, 64),       # largest skinny-GEMM row count
-    (1, 65, 0, 80),       # smallest tiled-GEMM row count
+    (1, 64, 0, 64),       # 64 rows: four 16-row token blocks in the skinny GEMM
+    (1, 65, 0, 80),       # 65 rows: five token blocks, one of them ragged
+    (1, 128, 0, 128),     # largest skinny-GEMM row count (eight token blocks)
+    (1, 129, 0, 136),     # smallest tiled-GEMM row count
     (2, 100, 0, 128),     # several tiles + ragged tail on every axis
     (2, 77, 50, 160),     # multi-token chunk at an offset into a filled cache
     (3, 1, 700, 1024),    # decode-shaped, host start position
@@ -100,7 +102,8 @@ def run_layer_case(lib, layer0, rope, batch, T, start, max_seq, check_seqs=None,
     (5, 3, 13, 16),       # tiny chunk, several sequences, cache full afterwards
     (2, 11, 53, 72),      # unaligned chunk spanning three 8-position V blocks
     (1, 200, 0, 200),     # 128-position query tiles with a ragged last tile
-    (65, 1, 100, 128),    # 65 decode rows: the tiled GEMMs with one token per sequence
+    (65, 1, 100, 128),    # 65 decode rows: the skinny GEMMs over five token blocks
+    (129, 1, 100, 128),   # 129 decode rows: the tiled GEMMs with one token per sequence
     (97, 2, 10, 16),      # 194 rows over 97 sequences: two row tiles, K split
     (1, 1, 40959, 40960), # decode at the last position of the rotary table
     (1, 64, 40896, 40960),  # a prefill chunk ending at the position limit

@@ -1,7 +1,7 @@
 """GPU parity of the projection kernels (q3_linear) and of HIP-graph replay
 of the decode step.
 
-q3_linear runs the skinny weight-streaming GEMM for up to 64 rows and the
+q3_linear runs the skinny weight-streaming GEMM for up to 128 rows and the
 LDS-tiled GEMM above; both are checked against the plain float64 product
 x W^T on the layer's real projection shapes, with ragged row counts and
 every epilogue.
@@ -35,7 +35,7 @@ SHAPES = [  # (name, n, k)
 ]
 
 
-@pytest.mark.parametrize("m", [1, 7, 16, 33, 64, 65, 200, 2048, 2100])
+@pytest.mark.parametrize("m", [1, 7, 16, 33, 64, 65, 128, 129, 200, 2048, 2100])
 @pytest.mark.parametrize("name,n,k", SHAPES)
 def test_linear_all_epilogues(lib, m, name, n, k):
     B, dev = lib
