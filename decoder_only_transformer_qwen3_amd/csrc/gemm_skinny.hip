@@ -34,9 +34,13 @@
 
 namespace q3 {
 
-template <int NB, int RB, int EPI, int U, int WV>
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+constexpr int XL_ELEMS = 32768;  // activation tile capacity in LDS (bf16 elements, 64 KB)
+
+template <int NB, int RB, int EPI, int U, int WV, bool XL>
 __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
   __shared__ float red[WV][RB][NB * 16][17];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[XL ? XL_ELEMS : 8];
   __shared__ float rsc[NB * 16];
   __shared__ int last_ticket;
   const uint16_t* __restrict__ X = a.X;
@@ -98,28 +102,74 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
   auto kstep = [&](int s0, int u) {
     return (U % 2 == 0) ? (s0 - w) + 2 * ((u >> 1) * WV + w) + (u & 1) : s0 + WV * u;
   };
-  for (int s0 = w; s0 < nsteps; s0 += WV * U) {
+  if constexpr (XL) {
+    // The activation rows of this K range go to LDS once, with
+    // direct-to-LDS loads of 1 KB of one row per instruction (16-byte chunk
+    // c of row rr at slot c ^ (rr % 16), so that the 16 rows of an operand
+    // read hit 16 different bank groups); they are all in flight together
+    // with the first weight loads.
+    const int cpr = kspan >> 3, lcpr = 31 - __builtin_clz(cpr);  // 16-byte chunks per row
+    const size_t kg = (size_t)split * kspan;
     u32x4 wa[U][RB];
-    u32x4 bx[U][NB];
+    auto load_w = [&](int s0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        wa[u][rb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp[rb] + (size_t)kstep(s0, u) * 32));
+        for (int rb = 0; rb < RB; ++rb)
+          wa[u][rb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp[rb] + (size_t)kstep(s0, u) * 32));
+    };
+    load_w(w);
+    for (int base = w * 64; base < NB * 16 * cpr; base += 64 * WV) {
+      const int p = base + l, rr = p >> lcpr, c = (p & (cpr - 1)) ^ (rr & 15);
+      const int m = rr < M ? rr : M - 1;  // rows past M re-read row M - 1 (never stored)
+      __builtin_amdgcn_global_load_lds((const void*)(X + (size_t)m * a.ldx + kg + 8 * c), (lds_ptr_t)(xs + base * 8),
+                                       16, 0, 0);
+    }
+    vm_drain();
+    __syncthreads();
+    const uint16_t* xrow = xs + r * cpr * 8;
+    for (int s0 = w; s0 < nsteps; s0 += WV * U) {
+      if (s0 != w) load_w(s0);
+      u32x4 bx[U][NB];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) bx[u][nb] = *reinterpret_cast<const u32x4*>(xp[nb] + (size_t)kstep(s0, u) * 32);
-    __builtin_amdgcn_sched_barrier(0);  // every load of the step is in flight before the first MFMA waits
+        for (int nb = 0; nb < NB; ++nb)
+          bx[u][nb] = *reinterpret_cast<const u32x4*>(xrow + (nb * 16 * cpr + ((4 * kstep(s0, u) + qd) ^ r)) * 8);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          f32x4& c = (u & 1) ? acc2[rb][nb] : acc[rb][nb];
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u][rb]), as_bf16x8(bx[u][nb]), c, 0, 0, 0);
-        }
+          for (int nb = 0; nb < NB; ++nb) {
+            f32x4& c = (u & 1) ? acc2[rb][nb] : acc[rb][nb];
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u][rb]), as_bf16x8(bx[u][nb]), c, 0, 0, 0);
+          }
+    }
+  } else {
+    for (int s0 = w; s0 < nsteps; s0 += WV * U) {
+      u32x4 wa[U][RB];
+      u32x4 bx[U][NB];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          wa[u][rb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp[rb] + (size_t)kstep(s0, u) * 32));
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) bx[u][nb] = *reinterpret_cast<const u32x4*>(xp[nb] + (size_t)kstep(s0, u) * 32);
+      __builtin_amdgcn_sched_barrier(0);  // every load of the step is in flight before the first MFMA waits
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            f32x4& c = (u & 1) ? acc2[rb][nb] : acc[rb][nb];
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u][rb]), as_bf16x8(bx[u][nb]), c, 0, 0, 0);
+          }
+    }
   }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -341,9 +391,17 @@ void launch_gemv_resid(const uint16_t* X, const uint16_t* W, int K, float* resid
   else launch_gemv_mr<8>(X, W, K, resid, M, gamma, hg, ssq_out, s);
 }
 
+// XL: the activation tile of a workgroup's K range through LDS (2 to 4
+// token blocks whose tile fits XL_ELEMS); otherwise straight from memory.
 template <int NB, int RB, int EPI, int WV, int U>
 static void launch_k(const SkinnyArgs& a, int gx, int n_split, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm_skinny<NB, RB, EPI, U, WV>), dim3(gx, n_split), dim3(64 * WV), 0, s, a);
+  if constexpr (NB >= 2 && NB <= 4) {
+    if (NB * 16 * a.kspan <= XL_ELEMS) {
+      hipLaunchKernelGGL((k_gemm_skinny<NB, RB, EPI, U, WV, true>), dim3(gx, n_split), dim3(64 * WV), 0, s, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((k_gemm_skinny<NB, RB, EPI, U, WV, false>), dim3(gx, n_split), dim3(64 * WV), 0, s, a);
 }
 
 // Unroll U: as many 32-wide k-steps per wave and iteration as divide the
