@@ -391,38 +391,46 @@ void launch_gemv_resid(const uint16_t* X, const uint16_t* W, int K, float* resid
   else launch_gemv_mr<8>(X, W, K, resid, M, gamma, hg, ssq_out, s);
 }
 
-// XL: the activation tile of a workgroup's K range through LDS (2 to 4
-// token blocks whose tile fits XL_ELEMS); otherwise straight from memory.
-template <int NB, int RB, int EPI, int WV, int U>
+template <int NB, int RB, int EPI, int WV, int U, bool XL>
 static void launch_k(const SkinnyArgs& a, int gx, int n_split, hipStream_t s) {
-  if constexpr (NB >= 2 && NB <= 4) {
-    if (NB * 16 * a.kspan <= XL_ELEMS) {
-      hipLaunchKernelGGL((k_gemm_skinny<NB, RB, EPI, U, WV, true>), dim3(gx, n_split), dim3(64 * WV), 0, s, a);
-      return;
-    }
-  }
-  hipLaunchKernelGGL((k_gemm_skinny<NB, RB, EPI, U, WV, false>), dim3(gx, n_split), dim3(64 * WV), 0, s, a);
+  hipLaunchKernelGGL((k_gemm_skinny<NB, RB, EPI, U, WV, XL>), dim3(gx, n_split), dim3(64 * WV), 0, s, a);
 }
 
 // Unroll U: as many 32-wide k-steps per wave and iteration as divide the
-// workgroup's range, with at most 24 (RB > 1) or 36 (RB == 1, NB <= 2)
-// 16-byte loads per lane in flight.  Every caller keeps the K range a
-// multiple of 32 * WV (q3_linear: K % 512 == 0; the residual projections'
-// splits: 512-wide ranges), so the U = 1 kernel always fits.
+// workgroup's range, with at most LOADS 16-byte registers of loads per lane
+// in flight (PER_U per k-step: the weight rows and, straight from memory,
+// the activation rows; from LDS the activation operands live briefly).
+// Every caller keeps the K range a multiple of 32 * WV (q3_linear:
+// K % 512 == 0; the residual projections' splits: 512-wide ranges), so the
+// U = 1 kernel always fits.
+template <int NB, int RB, int EPI, int WV, bool XL>
+static void launch_u(const SkinnyArgs& a, int gx, int n_split, hipStream_t s) {
+  const int nsteps = a.kspan >> 5;  // 32-wide k-steps per workgroup
+  constexpr int PER_U = XL ? RB + (NB + 1) / 2 : RB + NB;
+  constexpr int LOADS = XL ? 32 : ((RB == 1 && NB <= 2) ? 36 : 24);
+  if (12 * PER_U <= LOADS && nsteps % (WV * 12) == 0)
+    launch_k<NB, RB, EPI, WV, (12 * PER_U <= LOADS ? 12 : 1), XL>(a, gx, n_split, s);
+  else if (8 * PER_U <= LOADS && nsteps % (WV * 8) == 0)
+    launch_k<NB, RB, EPI, WV, (8 * PER_U <= LOADS ? 8 : 1), XL>(a, gx, n_split, s);
+  else if (4 * PER_U <= LOADS && nsteps % (WV * 4) == 0)
+    launch_k<NB, RB, EPI, WV, (4 * PER_U <= LOADS ? 4 : 1), XL>(a, gx, n_split, s);
+  else if (nsteps % (WV * 2) == 0)
+    launch_k<NB, RB, EPI, WV, 2, XL>(a, gx, n_split, s);
+  else
+    launch_k<NB, RB, EPI, WV, 1, XL>(a, gx, n_split, s);
+}
+
+// XL: the activation tile of a workgroup's K range through LDS (2 to 4
+// token blocks whose tile fits XL_ELEMS); otherwise straight from memory.
 template <int NB, int RB, int EPI, int WV>
 static void launch_wv(const SkinnyArgs& a, int gx, int n_split, hipStream_t s) {
-  const int nsteps = a.kspan >> 5;  // 32-wide k-steps per workgroup
-  constexpr int LOADS = (RB == 1 && NB <= 2) ? 36 : 24;
-  if (12 * (RB + NB) <= LOADS && nsteps % (WV * 12) == 0)
-    launch_k<NB, RB, EPI, WV, (12 * (RB + NB) <= LOADS ? 12 : 1)>(a, gx, n_split, s);
-  else if (8 * (RB + NB) <= LOADS && nsteps % (WV * 8) == 0)
-    launch_k<NB, RB, EPI, WV, (8 * (RB + NB) <= LOADS ? 8 : 1)>(a, gx, n_split, s);
-  else if (4 * (RB + NB) <= LOADS && nsteps % (WV * 4) == 0)
-    launch_k<NB, RB, EPI, WV, (4 * (RB + NB) <= LOADS ? 4 : 1)>(a, gx, n_split, s);
-  else if (nsteps % (WV * 2) == 0)
-    launch_k<NB, RB, EPI, WV, 2>(a, gx, n_split, s);
-  else
-    launch_k<NB, RB, EPI, WV, 1>(a, gx, n_split, s);
+  if constexpr (NB >= 2 && NB <= 4) {
+    if (NB * 16 * a.kspan <= XL_ELEMS) {
+      launch_u<NB, RB, EPI, WV, true>(a, gx, n_split, s);
+      return;
+    }
+  }
+  launch_u<NB, RB, EPI, WV, false>(a, gx, n_split, s);
 }
 
 template <int NB, int RB, int EPI>
