@@ -37,10 +37,13 @@ namespace q3 {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 constexpr int XL_ELEMS = 32768;  // activation tile capacity in LDS (bf16 elements, 64 KB)
 
-template <int NB, int RB, int EPI, int U, int WV, bool XL>
+constexpr int WL_MAXK = 1024;    // longest K range whose weight tile goes through LDS
+
+template <int NB, int RB, int EPI, int U, int WV, bool XL, bool WL>
 __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
   __shared__ float red[WV][RB][NB * 16][17];
   __shared__ __attribute__((aligned(16))) uint16_t xs[XL ? XL_ELEMS : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t wsl[WL ? RB * 16 * WL_MAXK : 8];
   __shared__ float rsc[NB * 16];
   __shared__ int last_ticket;
   const uint16_t* __restrict__ X = a.X;
@@ -102,7 +105,53 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
   auto kstep = [&](int s0, int u) {
     return (U % 2 == 0) ? (s0 - w) + 2 * ((u >> 1) * WV + w) + (u & 1) : s0 + WV * u;
   };
-  if constexpr (XL) {
+  if constexpr (WL) {
+    // One token block: the weight rows of this K range go to LDS once, with
+    // direct-to-LDS loads of 1 KB of one row per instruction (16-byte chunk
+    // c of row rr at slot c ^ (rr % 16)), in flight together with the first
+    // activation loads; the MFMAs take their A operand from LDS.
+    const int cpr = kspan >> 3, lcpr = 31 - __builtin_clz(cpr);  // 16-byte chunks per row
+    const size_t kg = (size_t)split * kspan;
+    u32x4 bx[U][NB];
+    auto load_x = [&](int s0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) bx[u][nb] = *reinterpret_cast<const u32x4*>(xp[nb] + (size_t)kstep(s0, u) * 32);
+    };
+    for (int base = w * 64; base < RB * 16 * cpr; base += 64 * WV) {
+      const int p = base + l, rr = p >> lcpr, c = (p & (cpr - 1)) ^ (rr & 15);
+      const int blk = blockIdx.x * RB + (rr >> 4), rl = rr & 15;
+      int wrow;
+      if constexpr (EPI == EPI_SILU)
+        wrow = (rl < 8) ? blk * 8 + rl : (N >> 1) + blk * 8 + (rl - 8);
+      else
+        wrow = blk * 16 + rl;
+      __builtin_amdgcn_global_load_lds((const void*)(W + (size_t)wrow * K + kg + 8 * c), (lds_ptr_t)(wsl + base * 8),
+                                       16, 0, 0);
+    }
+    load_x(w);
+    vm_drain();
+    __syncthreads();
+    for (int s0 = w; s0 < nsteps; s0 += WV * U) {
+      if (s0 != w) load_x(s0);
+      u32x4 wa[U][RB];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          wa[u][rb] = *reinterpret_cast<const u32x4*>(wsl + ((rb * 16 + r) * cpr + ((4 * kstep(s0, u) + qd) ^ r)) * 8);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            f32x4& c = (u & 1) ? acc2[rb][nb] : acc[rb][nb];
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u][rb]), as_bf16x8(bx[u][nb]), c, 0, 0, 0);
+          }
+    }
+  } else if constexpr (XL) {
     // The activation rows of this K range go to LDS once, with
     // direct-to-LDS loads of 1 KB of one row per instruction (16-byte chunk
     // c of row rr at slot c ^ (rr % 16), so that the 16 rows of an operand
@@ -391,9 +440,9 @@ void launch_gemv_resid(const uint16_t* X, const uint16_t* W, int K, float* resid
   else launch_gemv_mr<8>(X, W, K, resid, M, gamma, hg, ssq_out, s);
 }
 
-template <int NB, int RB, int EPI, int WV, int U, bool XL>
+template <int NB, int RB, int EPI, int WV, int U, bool XL, bool WL>
 static void launch_k(const SkinnyArgs& a, int gx, int n_split, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm_skinny<NB, RB, EPI, U, WV, XL>), dim3(gx, n_split), dim3(64 * WV), 0, s, a);
+  hipLaunchKernelGGL((k_gemm_skinny<NB, RB, EPI, U, WV, XL, WL>), dim3(gx, n_split), dim3(64 * WV), 0, s, a);
 }
 
 // Unroll U: as many 32-wide k-steps per wave and iteration as divide the
@@ -403,21 +452,21 @@ static void launch_k(const SkinnyArgs& a, int gx, int n_split, hipStream_t s) {
 // Every caller keeps the K range a multiple of 32 * WV (q3_linear:
 // K % 512 == 0; the residual projections' splits: 512-wide ranges), so the
 // U = 1 kernel always fits.
-template <int NB, int RB, int EPI, int WV, bool XL>
+template <int NB, int RB, int EPI, int WV, bool XL, bool WL>
 static void launch_u(const SkinnyArgs& a, int gx, int n_split, hipStream_t s) {
   const int nsteps = a.kspan >> 5;  // 32-wide k-steps per workgroup
-  constexpr int PER_U = XL ? RB + (NB + 1) / 2 : RB + NB;
-  constexpr int LOADS = XL ? 32 : ((RB == 1 && NB <= 2) ? 36 : 24);
+  constexpr int PER_U = XL ? RB + (NB + 1) / 2 : (WL ? NB + (RB + 1) / 2 : RB + NB);
+  constexpr int LOADS = (XL || WL) ? 32 : ((RB == 1 && NB <= 2) ? 36 : 24);
   if (12 * PER_U <= LOADS && nsteps % (WV * 12) == 0)
-    launch_k<NB, RB, EPI, WV, (12 * PER_U <= LOADS ? 12 : 1), XL>(a, gx, n_split, s);
+    launch_k<NB, RB, EPI, WV, (12 * PER_U <= LOADS ? 12 : 1), XL, WL>(a, gx, n_split, s);
   else if (8 * PER_U <= LOADS && nsteps % (WV * 8) == 0)
-    launch_k<NB, RB, EPI, WV, (8 * PER_U <= LOADS ? 8 : 1), XL>(a, gx, n_split, s);
+    launch_k<NB, RB, EPI, WV, (8 * PER_U <= LOADS ? 8 : 1), XL, WL>(a, gx, n_split, s);
   else if (4 * PER_U <= LOADS && nsteps % (WV * 4) == 0)
-    launch_k<NB, RB, EPI, WV, (4 * PER_U <= LOADS ? 4 : 1), XL>(a, gx, n_split, s);
+    launch_k<NB, RB, EPI, WV, (4 * PER_U <= LOADS ? 4 : 1), XL, WL>(a, gx, n_split, s);
   else if (nsteps % (WV * 2) == 0)
-    launch_k<NB, RB, EPI, WV, 2, XL>(a, gx, n_split, s);
+    launch_k<NB, RB, EPI, WV, 2, XL, WL>(a, gx, n_split, s);
   else
-    launch_k<NB, RB, EPI, WV, 1, XL>(a, gx, n_split, s);
+    launch_k<NB, RB, EPI, WV, 1, XL, WL>(a, gx, n_split, s);
 }
 
 // XL: the activation tile of a workgroup's K range through LDS (2 to 4
@@ -426,11 +475,17 @@ template <int NB, int RB, int EPI, int WV>
 static void launch_wv(const SkinnyArgs& a, int gx, int n_split, hipStream_t s) {
   if constexpr (NB >= 2 && NB <= 4) {
     if (NB * 16 * a.kspan <= XL_ELEMS) {
-      launch_u<NB, RB, EPI, WV, true>(a, gx, n_split, s);
+      launch_u<NB, RB, EPI, WV, true, false>(a, gx, n_split, s);
       return;
     }
   }
-  launch_u<NB, RB, EPI, WV, false>(a, gx, n_split, s);
+  if constexpr (NB == 1 && RB <= 2) {
+    if (a.kspan <= WL_MAXK) {
+      launch_u<NB, RB, EPI, WV, false, true>(a, gx, n_split, s);
+      return;
+    }
+  }
+  launch_u<NB, RB, EPI, WV, false, false>(a, gx, n_split, s);
 }
 
 template <int NB, int RB, int EPI>
