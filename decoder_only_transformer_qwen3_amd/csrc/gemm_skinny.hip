@@ -105,86 +105,74 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
   auto kstep = [&](int s0, int u) {
     return (U % 2 == 0) ? (s0 - w) + 2 * ((u >> 1) * WV + w) + (u & 1) : s0 + WV * u;
   };
-  if constexpr (WL) {
-    // One token block: the weight rows of this K range go to LDS once, with
-    // direct-to-LDS loads of 1 KB of one row per instruction (16-byte chunk
-    // c of row rr at slot c ^ (rr % 16)), in flight together with the first
-    // activation loads; the MFMAs take their A operand from LDS.
-    const int cpr = kspan >> 3, lcpr = 31 - __builtin_clz(cpr);  // 16-byte chunks per row
-    const size_t kg = (size_t)split * kspan;
-    u32x4 bx[U][NB];
-    auto load_x = [&](int s0) {
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) bx[u][nb] = *reinterpret_cast<const u32x4*>(xp[nb] + (size_t)kstep(s0, u) * 32);
-    };
-    for (int base = w * 64; base < RB * 16 * cpr; base += 64 * WV) {
-      const int p = base + l, rr = p >> lcpr, c = (p & (cpr - 1)) ^ (rr & 15);
-      const int blk = blockIdx.x * RB + (rr >> 4), rl = rr & 15;
-      int wrow;
-      if constexpr (EPI == EPI_SILU)
-        wrow = (rl < 8) ? blk * 8 + rl : (N >> 1) + blk * 8 + (rl - 8);
-      else
-        wrow = blk * 16 + rl;
-      __builtin_amdgcn_global_load_lds((const void*)(W + (size_t)wrow * K + kg + 8 * c), (lds_ptr_t)(wsl + base * 8),
-                                       16, 0, 0);
-    }
-    load_x(w);
-    vm_drain();
-    __syncthreads();
-    for (int s0 = w; s0 < nsteps; s0 += WV * U) {
-      if (s0 != w) load_x(s0);
-      u32x4 wa[U][RB];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          wa[u][rb] = *reinterpret_cast<const u32x4*>(wsl + ((rb * 16 + r) * cpr + ((4 * kstep(s0, u) + qd) ^ r)) * 8);
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            f32x4& c = (u & 1) ? acc2[rb][nb] : acc[rb][nb];
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u][rb]), as_bf16x8(bx[u][nb]), c, 0, 0, 0);
-          }
-    }
-  } else if constexpr (XL) {
-    // The activation rows of this K range go to LDS once, with
+  if constexpr (XL || WL) {
+    // Operand tiles through LDS: the weight rows (WL) and / or the
+    // activation rows (XL) of this K range are copied to LDS once, with
     // direct-to-LDS loads of 1 KB of one row per instruction (16-byte chunk
     // c of row rr at slot c ^ (rr % 16), so that the 16 rows of an operand
-    // read hit 16 different bank groups); they are all in flight together
-    // with the first weight loads.
+    // read hit 16 different bank groups), all in flight together with the
+    // first register loads of the other operand; the MFMAs then read their
+    // staged operands from LDS.
     const int cpr = kspan >> 3, lcpr = 31 - __builtin_clz(cpr);  // 16-byte chunks per row
     const size_t kg = (size_t)split * kspan;
     u32x4 wa[U][RB];
-    auto load_w = [&](int s0) {
+    u32x4 bx[U][NB];
+    auto load_regs = [&](int s0) {
+      if constexpr (!WL) {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          wa[u][rb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp[rb] + (size_t)kstep(s0, u) * 32));
+          for (int rb = 0; rb < RB; ++rb)
+            wa[u][rb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp[rb] + (size_t)kstep(s0, u) * 32));
+      }
+      if constexpr (!XL) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            bx[u][nb] = *reinterpret_cast<const u32x4*>(xp[nb] + (size_t)kstep(s0, u) * 32);
+      }
     };
-    load_w(w);
-    for (int base = w * 64; base < NB * 16 * cpr; base += 64 * WV) {
-      const int p = base + l, rr = p >> lcpr, c = (p & (cpr - 1)) ^ (rr & 15);
-      const int m = rr < M ? rr : M - 1;  // rows past M re-read row M - 1 (never stored)
-      __builtin_amdgcn_global_load_lds((const void*)(X + (size_t)m * a.ldx + kg + 8 * c), (lds_ptr_t)(xs + base * 8),
-                                       16, 0, 0);
+    if constexpr (WL) {
+      for (int base = w * 64; base < RB * 16 * cpr; base += 64 * WV) {
+        const int p = base + l, rr = p >> lcpr, c = (p & (cpr - 1)) ^ (rr & 15);
+        const int blk = blockIdx.x * RB + (rr >> 4), rl = rr & 15;
+        int wrow;
+        if constexpr (EPI == EPI_SILU)
+          wrow = (rl < 8) ? blk * 8 + rl : (N >> 1) + blk * 8 + (rl - 8);
+        else
+          wrow = blk * 16 + rl;
+        __builtin_amdgcn_global_load_lds((const void*)(W + (size_t)wrow * K + kg + 8 * c),
+                                         (lds_ptr_t)(wsl + base * 8), 16, 0, 0);
+      }
+    }
+    load_regs(w);
+    if constexpr (XL) {
+      for (int base = w * 64; base < NB * 16 * cpr; base += 64 * WV) {
+        const int p = base + l, rr = p >> lcpr, c = (p & (cpr - 1)) ^ (rr & 15);
+        const int m = rr < M ? rr : M - 1;  // rows past M re-read row M - 1 (never stored)
+        __builtin_amdgcn_global_load_lds((const void*)(X + (size_t)m * a.ldx + kg + 8 * c),
+                                         (lds_ptr_t)(xs + base * 8), 16, 0, 0);
+      }
     }
     vm_drain();
     __syncthreads();
-    const uint16_t* xrow = xs + r * cpr * 8;
     for (int s0 = w; s0 < nsteps; s0 += WV * U) {
-      if (s0 != w) load_w(s0);
-      u32x4 bx[U][NB];
+      if (s0 != w) load_regs(s0);
+      if constexpr (WL) {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          bx[u][nb] = *reinterpret_cast<const u32x4*>(xrow + (nb * 16 * cpr + ((4 * kstep(s0, u) + qd) ^ r)) * 8);
+          for (int rb = 0; rb < RB; ++rb)
+            wa[u][rb] = *reinterpret_cast<const u32x4*>(wsl + ((rb * 16 + r) * cpr + ((4 * kstep(s0, u) + qd) ^ r)) * 8);
+      }
+      if constexpr (XL) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            bx[u][nb] = *reinterpret_cast<const u32x4*>(xs + ((nb * 16 + r) * cpr + ((4 * kstep(s0, u) + qd) ^ r)) * 8);
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -455,7 +443,7 @@ static void launch_k(const SkinnyArgs& a, int gx, int n_split, hipStream_t s) {
 template <int NB, int RB, int EPI, int WV, bool XL, bool WL>
 static void launch_u(const SkinnyArgs& a, int gx, int n_split, hipStream_t s) {
   const int nsteps = a.kspan >> 5;  // 32-wide k-steps per workgroup
-  constexpr int PER_U = XL ? RB + (NB + 1) / 2 : (WL ? NB + (RB + 1) / 2 : RB + NB);
+  constexpr int PER_U = (XL ? (NB + 1) / 2 : NB) + (WL ? (RB + 1) / 2 : RB);
   constexpr int LOADS = (XL || WL) ? 32 : ((RB == 1 && NB <= 2) ? 36 : 24);
   if (12 * PER_U <= LOADS && nsteps % (WV * 12) == 0)
     launch_k<NB, RB, EPI, WV, (12 * PER_U <= LOADS ? 12 : 1), XL, WL>(a, gx, n_split, s);
@@ -475,6 +463,12 @@ template <int NB, int RB, int EPI, int WV>
 static void launch_wv(const SkinnyArgs& a, int gx, int n_split, hipStream_t s) {
   if constexpr (NB >= 2 && NB <= 4) {
     if (NB * 16 * a.kspan <= XL_ELEMS) {
+      if constexpr (RB <= 2 && WV == 4 && RB * NB <= 4) {  // (both tiles and the reduction fit the LDS)
+        if (a.kspan <= WL_MAXK) {
+          launch_u<NB, RB, EPI, WV, true, true>(a, gx, n_split, s);
+          return;
+        }
+      }
       launch_u<NB, RB, EPI, WV, true, false>(a, gx, n_split, s);
       return;
     }
