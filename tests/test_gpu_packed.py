@@ -83,3 +83,21 @@ def test_packed_chunked_continuation(setup):
         check_greedy_step(rep, int(nxt[s]), logits[s], o_logits[0])
     log(f"[packed] chunked continuation: {rep}")
     assert rep.near_ties == 0, rep
+
+
+def test_packed_head_over_more_than_64_sequences(setup):
+    """70 short packed prompts: the head runs two lm_head launches (64 + 6
+    rows) that share one ticket; sequences on both sides of the split and
+    at its edges against the oracle, and every sequence's length."""
+    B, dev, dm, om = setup
+    lens = [2 + (i * 3) % 5 for i in range(70)]  # 2..6 tokens, 280 rows
+    seqs = [I.token_ids(300 + i, (1, t))[0] for i, t in enumerate(lens)]
+    kv = dev.DeviceKV(len(lens), 8)
+    logits, nxt, seq = _packed_call(B, dev, dm, kv, seqs)
+    np.testing.assert_array_equal(seq, lens)
+    rep = GreedyReport()
+    for s in (0, 1, 62, 63, 64, 65, 69):
+        o_logits, _, _, _ = O.prefill(om, seqs[s][None, :])
+        check_greedy_step(rep, int(nxt[s]), logits[s], o_logits[0])
+    log(f"[packed] 70 sequences: {rep}")
+    assert rep.near_ties == 0, rep
