@@ -113,7 +113,12 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
     // read hit 16 different bank groups), all in flight together with the
     // first register loads of the other operand; the MFMAs then read their
     // staged operands from LDS.
-    const int cpr = kspan >> 3, lcpr = 31 - __builtin_clz(cpr);  // 16-byte chunks per row
+    // Above 4 token blocks the activation tile goes through LDS in K chunks
+    // of XKC columns (the whole K range otherwise).
+    constexpr int XKC = (XL && NB > 4) ? XL_ELEMS / 128 : 0;
+    const int kc = XKC ? XKC : kspan;
+    const int cpr = kc >> 3, lcpr = 31 - __builtin_clz(cpr);  // 16-byte chunks per staged activation row
+    const int cpw = kspan >> 3, lcpw = 31 - __builtin_clz(cpw);  // ... per staged weight row
     const size_t kg = (size_t)split * kspan;
     u32x4 wa[U][RB];
     u32x4 bx[U][NB];
@@ -134,8 +139,8 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
       }
     };
     if constexpr (WL) {
-      for (int base = w * 64; base < RB * 16 * cpr; base += 64 * WV) {
-        const int p = base + l, rr = p >> lcpr, c = (p & (cpr - 1)) ^ (rr & 15);
+      for (int base = w * 64; base < RB * 16 * cpw; base += 64 * WV) {
+        const int p = base + l, rr = p >> lcpw, c = (p & (cpw - 1)) ^ (rr & 15);
         const int blk = blockIdx.x * RB + (rr >> 4), rl = rr & 15;
         int wrow;
         if constexpr (EPI == EPI_SILU)
@@ -146,42 +151,50 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_skinny(SkinnyArgs a) {
                                          (lds_ptr_t)(wsl + base * 8), 16, 0, 0);
       }
     }
-    load_regs(w);
-    if constexpr (XL) {
-      for (int base = w * 64; base < NB * 16 * cpr; base += 64 * WV) {
-        const int p = base + l, rr = p >> lcpr, c = (p & (cpr - 1)) ^ (rr & 15);
-        const int m = rr < M ? rr : M - 1;  // rows past M re-read row M - 1 (never stored)
-        __builtin_amdgcn_global_load_lds((const void*)(X + (size_t)m * a.ldx + kg + 8 * c),
-                                         (lds_ptr_t)(xs + base * 8), 16, 0, 0);
+    // one pass over the K range, or one per activation chunk: the first
+    // k-step's register loads, the chunk's activation rows into LDS, then
+    // the chunk's k-steps (kc / 32 of them, a multiple of WV * U)
+    for (int k0 = 0; k0 < kspan; k0 += kc) {
+      const int c0 = k0 >> 5;  // first k-step of the chunk
+      if (k0) __syncthreads();  // every wave is done with the previous chunk
+      load_regs(c0 + w);
+      if constexpr (XL) {
+        for (int base = w * 64; base < NB * 16 * cpr; base += 64 * WV) {
+          const int p = base + l, rr = p >> lcpr, c = (p & (cpr - 1)) ^ (rr & 15);
+          const int m = rr < M ? rr : M - 1;  // rows past M re-read row M - 1 (never stored)
+          __builtin_amdgcn_global_load_lds((const void*)(X + (size_t)m * a.ldx + kg + k0 + 8 * c),
+                                           (lds_ptr_t)(xs + base * 8), 16, 0, 0);
+        }
       }
-    }
-    vm_drain();
-    __syncthreads();
-    for (int s0 = w; s0 < nsteps; s0 += WV * U) {
-      if (s0 != w) load_regs(s0);
-      if constexpr (WL) {
+      vm_drain();
+      __syncthreads();
+      for (int s0 = c0 + w; s0 < c0 + (kc >> 5); s0 += WV * U) {
+        if (s0 != c0 + w) load_regs(s0);
+        if constexpr (WL) {
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              wa[u][rb] = *reinterpret_cast<const u32x4*>(wsl + ((rb * 16 + r) * cpw + ((4 * kstep(s0, u) + qd) ^ r)) * 8);
+        }
+        if constexpr (XL) {
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+              bx[u][nb] = *reinterpret_cast<const u32x4*>(
+                  xs + ((nb * 16 + r) * cpr + ((4 * (kstep(s0, u) - c0) + qd) ^ r)) * 8);
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
-            wa[u][rb] = *reinterpret_cast<const u32x4*>(wsl + ((rb * 16 + r) * cpr + ((4 * kstep(s0, u) + qd) ^ r)) * 8);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+              f32x4& c = (u & 1) ? acc2[rb][nb] : acc[rb][nb];
+              c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u][rb]), as_bf16x8(bx[u][nb]), c, 0, 0, 0);
+            }
       }
-      if constexpr (XL) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            bx[u][nb] = *reinterpret_cast<const u32x4*>(xs + ((nb * 16 + r) * cpr + ((4 * kstep(s0, u) + qd) ^ r)) * 8);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            f32x4& c = (u & 1) ? acc2[rb][nb] : acc[rb][nb];
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u][rb]), as_bf16x8(bx[u][nb]), c, 0, 0, 0);
-          }
     }
   } else {
     for (int s0 = w; s0 < nsteps; s0 += WV * U) {
@@ -442,7 +455,8 @@ static void launch_k(const SkinnyArgs& a, int gx, int n_split, hipStream_t s) {
 // U = 1 kernel always fits.
 template <int NB, int RB, int EPI, int WV, bool XL, bool WL>
 static void launch_u(const SkinnyArgs& a, int gx, int n_split, hipStream_t s) {
-  const int nsteps = a.kspan >> 5;  // 32-wide k-steps per workgroup
+  // 32-wide k-steps per workgroup, or per activation chunk (XL above 4 token blocks)
+  const int nsteps = (XL && NB > 4) ? XL_ELEMS / 128 / 32 : a.kspan >> 5;
   constexpr int PER_U = (XL ? (NB + 1) / 2 : NB) + (WL ? (RB + 1) / 2 : RB);
   constexpr int LOADS = (XL || WL) ? 32 : ((RB == 1 && NB <= 2) ? 36 : 24);
   if (12 * PER_U <= LOADS && nsteps % (WV * 12) == 0)
@@ -458,28 +472,33 @@ static void launch_u(const SkinnyArgs& a, int gx, int n_split, hipStream_t s) {
 }
 
 // XL: the activation tile of a workgroup's K range through LDS (2 to 4
-// token blocks whose tile fits XL_ELEMS); otherwise straight from memory.
+// token blocks whose tile fits XL_ELEMS; 5 to 8 blocks in chunks of 256
+// columns); otherwise straight from memory.
 template <int NB, int RB, int EPI, int WV>
 static void launch_wv(const SkinnyArgs& a, int gx, int n_split, hipStream_t s) {
-  if constexpr (NB >= 2 && NB <= 4) {
-    if (NB * 16 * a.kspan <= XL_ELEMS) {
-      if constexpr (RB <= 2 && WV == 4 && RB * NB <= 4) {  // (both tiles and the reduction fit the LDS)
-        if (a.kspan <= WL_MAXK) {
-          launch_u<NB, RB, EPI, WV, true, true>(a, gx, n_split, s);
-          return;
+  if constexpr (NB > 4) {
+    launch_u<NB, RB, EPI, WV, true, false>(a, gx, n_split, s);
+  } else {
+    if constexpr (NB >= 2) {
+      if (NB * 16 * a.kspan <= XL_ELEMS) {
+        if constexpr (RB <= 2 && WV == 4 && RB * NB <= 4) {  // (both tiles and the reduction fit the LDS)
+          if (a.kspan <= WL_MAXK) {
+            launch_u<NB, RB, EPI, WV, true, true>(a, gx, n_split, s);
+            return;
+          }
         }
+        launch_u<NB, RB, EPI, WV, true, false>(a, gx, n_split, s);
+        return;
       }
-      launch_u<NB, RB, EPI, WV, true, false>(a, gx, n_split, s);
-      return;
     }
-  }
-  if constexpr (NB == 1 && RB <= 2) {
-    if (a.kspan <= WL_MAXK) {
-      launch_u<NB, RB, EPI, WV, false, true>(a, gx, n_split, s);
-      return;
+    if constexpr (NB == 1 && RB <= 2) {
+      if (a.kspan <= WL_MAXK) {
+        launch_u<NB, RB, EPI, WV, false, true>(a, gx, n_split, s);
+        return;
+      }
     }
+    launch_u<NB, RB, EPI, WV, false, false>(a, gx, n_split, s);
   }
-  launch_u<NB, RB, EPI, WV, false, false>(a, gx, n_split, s);
 }
 
 template <int NB, int RB, int EPI>
